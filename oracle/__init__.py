@@ -1,0 +1,185 @@
+"""TEST INFRASTRUCTURE ONLY: Python binding of the fp64 CPU convolution oracle.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (``libconv`` and
+``direct_implicit_gemm_amd``) never does.
+
+The arithmetic lives in ``conv_oracle.c`` (plain C, fp64, OpenMP over output
+elements); this module only marshals numpy arrays.  Definition followed: the
+gather-form direct convolution of the page "PP-OCR on Vulkan compute shaders"
+(section 2.2), with ReLU fused after the bias (section 4.4), extended by one
+frame axis as in the Convolution3D layer of the page "SeedVR2 NCNN Vulkan"
+(section 3.2).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+SRC_PATH = os.path.join(_HERE, "conv_oracle.c")
+
+
+def build() -> str:
+    """Compile liboracle.so with gcc (fp64, OpenMP, no fast-math)."""
+    cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
+           "-shared", "-fPIC", "-Wall", "-Werror", "-o", LIB_PATH, SRC_PATH, "-lm"]
+    subprocess.run(cmd, check=True)
+    return LIB_PATH
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        lib = ctypes.CDLL(LIB_PATH)
+        dp = ctypes.POINTER(ctypes.c_double)
+        lp = ctypes.POINTER(ctypes.c_long)
+        lib.oracle_out_extent.argtypes = [ctypes.c_long] * 4
+        lib.oracle_out_extent.restype = ctypes.c_long
+        lib.oracle_threads.argtypes = [ctypes.c_int]
+        lib.oracle_threads.restype = ctypes.c_int
+        lib.oracle_conv.argtypes = [dp, dp, dp, dp, dp, lp, ctypes.c_int, ctypes.c_int]
+        lib.oracle_conv.restype = ctypes.c_int
+        lib.oracle_conv_points.argtypes = [dp, dp, dp, ctypes.POINTER(ctypes.c_int64),
+                                           ctypes.c_long, dp, dp, lp, ctypes.c_int,
+                                           ctypes.c_int]
+        lib.oracle_conv_points.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _dp(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def out_extent(n_in: int, k: int, pad: int, stride: int) -> int:
+    return int(_load().oracle_out_extent(n_in, k, pad, stride))
+
+
+def threads(requested: int = 0) -> int:
+    """OpenMP threads the oracle will use (after applying ``requested`` if > 0)."""
+    return int(_load().oracle_threads(requested))
+
+
+def _as5d(x: np.ndarray, w: np.ndarray):
+    """View 2-D (NCHW / OIHW) operands as 3-D with one frame and one time tap."""
+    if x.ndim == 4:
+        return x[:, :, None], w[:, :, None], 2
+    if x.ndim == 5:
+        return x, w, 3
+    raise ValueError("x must be NCHW or NCDHW")
+
+
+def _dims(x5, w5, stride, pad):
+    N, C, T, H, W = x5.shape
+    CO, C2, KT, KH, KW = w5.shape
+    if C2 != C:
+        raise ValueError("channel mismatch")
+    return np.array([N, C, T, H, W, CO, KT, KH, KW, pad[0], pad[1], pad[2],
+                     stride[0], stride[1], stride[2]], dtype=np.int64)
+
+
+def _norm3(v, nd) -> Tuple[int, int, int]:
+    if isinstance(v, int):
+        return (v, v, v)
+    v = tuple(int(t) for t in v)
+    if len(v) == 2:
+        return (0, v[0], v[1])
+    if len(v) == 3:
+        return v
+    raise ValueError(v)
+
+
+def _spatial(x5, w5, stride3, pad3, nd):
+    _, _, T, H, W = x5.shape
+    _, _, KT, KH, KW = w5.shape
+    o = (out_extent(T, KT, pad3[0], stride3[0]),
+         out_extent(H, KH, pad3[1], stride3[1]),
+         out_extent(W, KW, pad3[2], stride3[2]))
+    if min(o) < 0:
+        raise ValueError("bad geometry")
+    return o
+
+
+def conv(x: np.ndarray, w: np.ndarray, b: Optional[np.ndarray], stride=1, pad=0,
+         relu: bool = False, nthreads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+    """fp64 forward convolution.  Returns (y, S), both float64, shaped like y.
+
+    x: NCHW or NCDHW; w: OIHW or OIDHW; b: [C_out] or None.
+    stride / pad: an int, or one value per spatial axis ((h, w) or (t, h, w)).
+    For 2-D operands the time stride is 1 and the time pad is 0.
+    """
+    x5, w5, nd = _as5d(np.ascontiguousarray(x, np.float64), np.ascontiguousarray(w, np.float64))
+    s3 = _norm3(stride, nd)
+    p3 = _norm3(pad, nd)
+    if nd == 2:
+        s3, p3 = (1, s3[1], s3[2]), (0, p3[1], p3[2])
+    x5 = np.ascontiguousarray(x5)
+    w5 = np.ascontiguousarray(w5)
+    bb = None if b is None else np.ascontiguousarray(b, np.float64)
+    OT, OH, OW = _spatial(x5, w5, s3, p3, nd)
+    N, CO = x5.shape[0], w5.shape[0]
+    y = np.empty((N, CO, OT, OH, OW), np.float64)
+    s = np.empty_like(y)
+    dims = _dims(x5, w5, s3, p3)
+    rc = _load().oracle_conv(_dp(x5), _dp(w5), _dp(bb), _dp(y), _dp(s),
+                             dims.ctypes.data_as(ctypes.POINTER(ctypes.c_long)),
+                             int(bool(relu)), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_conv failed ({rc})")
+    if nd == 2:
+        y, s = y[:, :, 0], s[:, :, 0]
+    return y, s
+
+
+def conv_points(x: np.ndarray, w: np.ndarray, b: Optional[np.ndarray],
+                flat_idx: Sequence[int], stride=1, pad=0, relu: bool = False,
+                nthreads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+    """The outputs at flat indices of y (row-major over N, C_out, (OT,) OH, OW)."""
+    x5, w5, nd = _as5d(np.ascontiguousarray(x, np.float64), np.ascontiguousarray(w, np.float64))
+    s3 = _norm3(stride, nd)
+    p3 = _norm3(pad, nd)
+    if nd == 2:
+        s3, p3 = (1, s3[1], s3[2]), (0, p3[1], p3[2])
+    x5 = np.ascontiguousarray(x5)
+    w5 = np.ascontiguousarray(w5)
+    bb = None if b is None else np.ascontiguousarray(b, np.float64)
+    idx = np.ascontiguousarray(np.asarray(flat_idx, dtype=np.int64))
+    y = np.empty(idx.shape[0], np.float64)
+    s = np.empty_like(y)
+    dims = _dims(x5, w5, s3, p3)
+    rc = _load().oracle_conv_points(_dp(x5), _dp(w5), _dp(bb),
+                                    idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                    idx.shape[0], _dp(y), _dp(s),
+                                    dims.ctypes.data_as(ctypes.POINTER(ctypes.c_long)),
+                                    int(bool(relu)), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle_conv_points failed ({rc})")
+    return y, s
+
+
+def output_shape(x_shape, w_shape, stride=1, pad=0):
+    """Shape of y for the given operand shapes (the oracle's own extents)."""
+    nd = len(x_shape) - 2
+    s3 = _norm3(stride, nd)
+    p3 = _norm3(pad, nd)
+    if nd == 2:
+        o = (out_extent(x_shape[2], w_shape[2], p3[1], s3[1]),
+             out_extent(x_shape[3], w_shape[3], p3[2], s3[2]))
+    else:
+        o = (out_extent(x_shape[2], w_shape[2], p3[0], s3[0]),
+             out_extent(x_shape[3], w_shape[3], p3[1], s3[1]),
+             out_extent(x_shape[4], w_shape[4], p3[2], s3[2]))
+    return (x_shape[0], w_shape[0]) + o
