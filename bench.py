@@ -1,0 +1,270 @@
+"""Forward-convolution benchmark on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+A step is one pass of the workload's convolution layers over one batch of
+synthetic input, chained on the GPU (layer k reads layer k-1's output), with
+every layer through libconv.  The default workload is the fp32 OCR-detection
+stack (N=1, 3x640x640; conv3x3/s2 3->32 +ReLU, conv3x3 32->32 +ReLU,
+conv1x1 32->64 +ReLU, conv3x3/s2 64->64 +ReLU).
+
+Printed: ONE JSON line.  ``value`` is the step's effective TFLOP/s
+(2*N*C_out*out_spatial*C_in*taps summed over layers, divided by the time of a
+step); per-layer figures (µs, TFLOP/s, GB/s, binding roofline and fraction)
+are in ``layers``; ``roofline`` describes the layer whose kernel takes the most
+time; ``cpu_baseline`` is the fp64 oracle timed on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+# MI355X published peaks
+PEAK_HBM_GBS = 8000.0
+PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6, "bf16": 2516.6}   # dense MFMA
+METRIC = "conv fwd effective TFLOP/s + HBM GB/s per layer, % of binding MI355X roofline"
+
+WORKLOAD_TEXT = {
+    "conv1": "single conv2d fp32 N=1 3x32x32 -> 8, 3x3 s1 p1, bias",
+    "ocr_stack": ("OCR-detection fp32 stack N=1 3x640x640: conv3x3 s2 p1 3->32 +ReLU, "
+                  "conv3x3 s1 p1 32->32 +ReLU, conv1x1 32->64 +ReLU, conv3x3 s2 p1 64->64 +ReLU"),
+    "textrec_f16": ("text-recognition f16 N=16: conv3x3 64->128 on 24x160 +ReLU; "
+                    "conv1x1 128->256 on 12x80"),
+    "unet_bf16": "diffusion-UNet bf16 N=2: conv3x3 640->640 on 64x64; conv3x3 1280->1280 on 32x32",
+    "vae3d_f16": ("video-VAE f16 conv3d N=1 T=5: 3x3x3 128->128 on 256x480; "
+                  "3x3x3 512->512 on 64x120 +ReLU"),
+}
+
+
+def out_shape(layer: W.Layer, lib):
+    o = [lib.libconv_out_size(layer.T, layer.KT, layer.pad[0], layer.stride[0]),
+         lib.libconv_out_size(layer.H, layer.KH, layer.pad[1], layer.stride[1]),
+         lib.libconv_out_size(layer.W, layer.KW, layer.pad[2], layer.stride[2])]
+    return o
+
+
+def layer_work(layer: W.Layer, lib):
+    ot, oh, ow = out_shape(layer, lib)
+    out_spatial = ot * oh * ow
+    flops = 2 * layer.N * layer.C_out * out_spatial * layer.C_in * layer.taps
+    e = W.DTYPE_BYTES[layer.dtype]
+    nbytes = e * (int(np.prod(layer.x_shape)) + int(np.prod(layer.w_shape)) + layer.C_out
+                  + layer.N * layer.C_out * out_spatial)
+    return flops, nbytes
+
+
+def roofline_of(layer, flops, nbytes, seconds):
+    t_mfma = flops / (PEAK_TFLOPS[layer.dtype] * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    bound = "mfma" if t_mfma >= t_hbm else "hbm"
+    tflops = flops / seconds / 1e12
+    gbs = nbytes / seconds / 1e9
+    frac = (tflops / PEAK_TFLOPS[layer.dtype]) if bound == "mfma" else (gbs / PEAK_HBM_GBS)
+    return bound, tflops, gbs, frac
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for f in ("direct.hip", "igemm.hip", "device_common.h"):
+        with open(os.path.join(ROOT, "direct_implicit_gemm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(tile_name: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    e = d.get(workload, {}).get(tile_name)
+    if not e or e.get("source_sha") != kernel_source_sha():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(layers, inputs, budget_s: float):
+    """The oracle (as it stands) on the same step, repeated to ~budget_s."""
+    import oracle
+    threads = oracle.threads(len(os.sched_getaffinity(0)))
+    total_flops = 0
+    runs = 0
+    t0 = time.perf_counter()
+    while True:
+        x = inputs[0][0].f64()
+        for layer, (_, w, b) in zip(layers, inputs):
+            st, pd = (layer.stride[1:], layer.pad[1:]) if layer.dims == 2 else (layer.stride, layer.pad)
+            y, _ = oracle.conv(x, w.f64(), b.f64(), st, pd, relu=layer.act == "relu")
+            x = W.Tensor.quantise(y, layer.dtype).f64()
+        runs += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    return el / runs, threads, runs
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="ocr_stack", choices=sorted(W.WORKLOADS))
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import direct_implicit_gemm_amd as L
+
+    lib = L.load()
+    if L.libconv_device_supported(0) != 0:
+        print("cuda:0 is not a gfx950 device", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    _, layers = W.WORKLOADS[args.workload]
+    # Inputs: the workload's seeded tensors; the stack is chained, so only the
+    # first layer's x is used when layers feed each other.
+    inputs = [W.make_inputs(l) for l in layers]
+    chained = args.workload in ("ocr_stack",)
+    xs, ws, bs = [], [], []
+    for (x, w, b) in inputs:
+        xs.append(x.torch(dev))
+        ws.append(w.torch(dev))
+        bs.append(b.torch(dev))
+    outs = []
+    for i, l in enumerate(layers):
+        ot, oh, ow = out_shape(l, lib)
+        shape = (l.N, l.C_out, oh, ow) if l.dims == 2 else (l.N, l.C_out, ot, oh, ow)
+        outs.append(torch.empty(shape, dtype=xs[i].dtype, device=dev))
+
+    def sp(l):
+        return (l.stride[1:], l.pad[1:]) if l.dims == 2 else (l.stride, l.pad)
+
+    def step(events=None):
+        for i, l in enumerate(layers):
+            x_in = outs[i - 1] if (chained and i > 0) else xs[i]
+            s, p = sp(l)
+            if events is not None:
+                events[i][0].record()
+            L.conv_nd(x_in, ws[i], bs[i], s, p, l.act, out=outs[i])
+            if events is not None:
+                events[i][1].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in layers] for _ in range(K)]
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record()
+    for k in range(K):
+        step(ev[k])
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / K
+
+    per_layer = []
+    step_flops = 0
+    for i, l in enumerate(layers):
+        times = [ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(K)]
+        us = 1000.0 * float(np.mean(times))
+        flops, nbytes = layer_work(l, lib)
+        step_flops += flops
+        bound, tflops, gbs, frac = roofline_of(l, flops, nbytes, us * 1e-6)
+        st_, algo, tile, grid = L.libconv_query_algo(
+            l.N, l.C_in, l.T, l.H, l.W, l.C_out, l.KT, l.KH, l.KW, *l.pad, *l.stride,
+            W.DTYPE_CODE[l.dtype], W.ACT_CODE[l.act], L.ALGO_AUTO)
+        per_layer.append({
+            "layer": l.name, "kernel": L.libconv_tile_name(tile), "grid": grid,
+            "us_mean": round(us, 3), "us_min": round(1000.0 * float(np.min(times)), 3),
+            "us_median": round(1000.0 * float(np.median(times)), 3),
+            "gflop": round(flops / 1e9, 4), "mbytes": round(nbytes / 1e6, 3),
+            "tflops": round(tflops, 3), "gbs": round(gbs, 1),
+            "bound": bound, "frac": round(frac, 4),
+        })
+
+    dom = max(range(len(layers)), key=lambda i: per_layer[i]["us_mean"])
+    dl = per_layer[dom]
+    flops, nbytes = layer_work(layers[dom], lib)
+    if dl["bound"] == "mfma":
+        roof = {"bound": "mfma", "achieved": dl["tflops"], "peak": PEAK_TFLOPS[layers[dom].dtype],
+                "unit": "TFLOP/s", "frac": dl["frac"]}
+    else:
+        roof = {"bound": "hbm", "achieved": dl["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": dl["frac"]}
+    traffic = measured_traffic(dl["kernel"], args.workload)
+    roof["traffic"] = traffic
+    roof["layer"] = dl["layer"]
+    roof["kernel"] = dl["kernel"]
+    roof["algorithmic"] = flops if dl["bound"] == "mfma" else nbytes
+
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu:
+        sec, threads, runs = cpu_baseline(layers, inputs, args.cpu_budget) if chained else (None, None, None)
+        if sec is None:  # unchained workloads: each layer on its own input
+            import oracle
+            threads = oracle.threads(len(os.sched_getaffinity(0)))
+            t0 = time.perf_counter()
+            for l, (x, w, b) in zip(layers, inputs):
+                s, p = sp(l)
+                oracle.conv(x.f64(), w.f64(), b.f64(), s, p, relu=l.act == "relu")
+            sec, runs = time.perf_counter() - t0, 1
+        cpu = {"value": round(step_flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"the whole step ({len(layers)} layers, fp64, incl. the |x*w| sum), "
+                         f"{runs} run(s), {sec:.3f} s per step",
+               "cpu": platform.processor() or platform.machine()}
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 4),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": layers[0].dtype,
+        "data": "synthetic (seeded; shapes and value distributions of the workload)",
+        "config": {"workload": args.workload, "description": WORKLOAD_TEXT[args.workload],
+                   "chained": chained, "wall_s_timed": round(wall, 4)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "layers": per_layer,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,219 @@
+"""Python binding of libconv, the gfx950 forward-convolution library.
+
+Argument marshalling only: every convolution runs in the HIP kernels of
+``libconv.so`` (built from ``csrc/`` by ``python -m direct_implicit_gemm_amd.build``).
+There is no fallback: if the library is missing, importing the raw entry
+points raises.  PyTorch supplies device memory and the current stream.
+
+Raw entry points (same names and argument order as ``include/libconv.h``)
+take integer device addresses and return the status code.  The tensor-level
+helpers ``conv2d`` / ``conv3d`` allocate the output and raise ``LibconvError``
+on a non-zero status.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Sequence, Tuple, Union
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libconv.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "libconv.h")
+
+F32, F16, BF16 = 0, 1, 2
+ACT_NONE, ACT_RELU = 0, 1
+ALGO_AUTO, ALGO_DIRECT, ALGO_IGEMM = 0, 1, 2
+
+STATUS = {
+    0: "OK", 1: "ERR_NULL_POINTER", 2: "ERR_BAD_SHAPE", 3: "ERR_BAD_DTYPE",
+    4: "ERR_BAD_ACTIVATION", 5: "ERR_ALIAS", 6: "ERR_UNSUPPORTED", 7: "ERR_NO_DEVICE",
+    8: "ERR_LAUNCH", 9: "ERR_BAD_ALGO", 10: "ERR_TOO_LARGE",
+}
+_ALGOS = {"auto": ALGO_AUTO, "direct": ALGO_DIRECT, "igemm": ALGO_IGEMM}
+_ACTS = {"none": ACT_NONE, "relu": ACT_RELU}
+
+
+class LibconvError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({status_string(status)})")
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libconv.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m direct_implicit_gemm_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    I, P, LL = ctypes.c_int, ctypes.c_void_p, ctypes.c_longlong
+    lib.conv2d_forward.argtypes = [P, P, P, P] + [I] * 13 + [P]
+    lib.conv2d_forward.restype = I
+    lib.conv3d_forward.argtypes = [P, P, P, P] + [I] * 17 + [P]
+    lib.conv3d_forward.restype = I
+    lib.libconv_forward_algo.argtypes = [P, P, P, P] + [I] * 18 + [P]
+    lib.libconv_forward_algo.restype = I
+    lib.libconv_query_algo.argtypes = [I] * 18 + [ctypes.POINTER(I), ctypes.POINTER(I),
+                                                  ctypes.POINTER(LL)]
+    lib.libconv_query_algo.restype = I
+    lib.libconv_tile_name.argtypes = [I]
+    lib.libconv_tile_name.restype = ctypes.c_char_p
+    lib.libconv_out_size.argtypes = [I, I, I, I]
+    lib.libconv_out_size.restype = I
+    lib.libconv_status_string.argtypes = [I]
+    lib.libconv_status_string.restype = ctypes.c_char_p
+    lib.libconv_device_supported.argtypes = [I]
+    lib.libconv_device_supported.restype = I
+    lib.libconv_version.argtypes = []
+    lib.libconv_version.restype = I
+    _lib = lib
+    return lib
+
+
+def header_functions() -> list:
+    """Names of the functions declared in include/libconv.h."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:libconv_status|int|const char\*)\s+(\w+)\s*\(", text, flags=re.M)
+
+
+# ------------------------------------------------------------ raw entry points
+def conv2d_forward(x, w, bias, y, N, C_in, H, W, C_out, KH, KW, pad_h, pad_w,
+                   stride_h, stride_w, dtype, act, stream) -> int:
+    return load().conv2d_forward(x, w, bias, y, N, C_in, H, W, C_out, KH, KW, pad_h, pad_w,
+                                 stride_h, stride_w, dtype, act, stream)
+
+
+def conv3d_forward(x, w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW, pad_t, pad_h, pad_w,
+                   stride_t, stride_h, stride_w, dtype, act, stream) -> int:
+    return load().conv3d_forward(x, w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW,
+                                 pad_t, pad_h, pad_w, stride_t, stride_h, stride_w,
+                                 dtype, act, stream)
+
+
+def libconv_forward_algo(x, w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW, pad_t, pad_h,
+                         pad_w, stride_t, stride_h, stride_w, dtype, act, algo, stream) -> int:
+    return load().libconv_forward_algo(x, w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW,
+                                       pad_t, pad_h, pad_w, stride_t, stride_h, stride_w,
+                                       dtype, act, algo, stream)
+
+
+def libconv_query_algo(N, C_in, T, H, W, C_out, KT, KH, KW, pad_t, pad_h, pad_w,
+                       stride_t, stride_h, stride_w, dtype, act, algo) -> Tuple[int, int, int, int]:
+    """Returns (status, algo, tile_id, grid)."""
+    a, t, g = ctypes.c_int(-1), ctypes.c_int(-1), ctypes.c_longlong(-1)
+    st = load().libconv_query_algo(N, C_in, T, H, W, C_out, KT, KH, KW, pad_t, pad_h, pad_w,
+                                   stride_t, stride_h, stride_w, dtype, act, algo,
+                                   ctypes.byref(a), ctypes.byref(t), ctypes.byref(g))
+    return st, a.value, t.value, g.value
+
+
+def libconv_tile_name(tile_id: int) -> str:
+    return load().libconv_tile_name(tile_id).decode()
+
+
+def libconv_out_size(n_in: int, k: int, pad: int, stride: int) -> int:
+    return load().libconv_out_size(n_in, k, pad, stride)
+
+
+def libconv_status_string(status: int) -> str:
+    return load().libconv_status_string(status).decode()
+
+
+status_string = libconv_status_string
+
+
+def libconv_device_supported(device: int) -> int:
+    return load().libconv_device_supported(device)
+
+
+def libconv_version() -> int:
+    return load().libconv_version()
+
+
+# ------------------------------------------------------- tensor-level helpers
+def _triple(v, nd: int) -> Tuple[int, ...]:
+    if isinstance(v, int):
+        return (v,) * nd
+    v = tuple(int(t) for t in v)
+    if len(v) != nd:
+        raise ValueError(f"expected {nd} values, got {v}")
+    return v
+
+
+def _dtype_code(t) -> int:
+    import torch
+    m = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def conv_nd(x, w, b=None, stride: Union[int, Sequence[int]] = 1,
+            padding: Union[int, Sequence[int]] = 0, act: str = "none", algo: str = "auto",
+            out=None, stream=None):
+    """Convolution of CUDA (HIP) tensors through libconv; 2-D or 3-D by x.ndim."""
+    import torch
+    nd = x.dim() - 2
+    if nd not in (2, 3) or w.dim() != x.dim():
+        raise ValueError("x must be NCHW or NCDHW and w OIHW or OIDHW")
+    for t in (x, w) + ((b,) if b is not None else ()):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != x.dtype:
+            raise ValueError("x, w, b must be contiguous device tensors of one dtype")
+    s = _triple(stride, nd)
+    p = _triple(padding, nd)
+    dt = _dtype_code(x)
+    if nd == 2:
+        N, C, H, W = x.shape
+        T, KT, st, pt = 1, 1, 1, 0
+        K, _, KH, KW = w.shape
+        sh, sw = s
+        ph, pw = p
+    else:
+        N, C, T, H, W = x.shape
+        K, _, KT, KH, KW = w.shape
+        st, sh, sw = s
+        pt, ph, pw = p
+    if w.shape[1] != C:
+        raise ValueError("channel mismatch")
+    lib = load()
+    ot = lib.libconv_out_size(T, KT, pt, st)
+    oh = lib.libconv_out_size(H, KH, ph, sh)
+    ow = lib.libconv_out_size(W, KW, pw, sw)
+    if min(ot, oh, ow) < 1:
+        raise LibconvError(2, "conv")
+    shape = (N, K, oh, ow) if nd == 2 else (N, K, ot, oh, ow)
+    y = torch.empty(shape, dtype=x.dtype, device=x.device) if out is None else out
+    if tuple(y.shape) != shape or not y.is_contiguous() or y.dtype != x.dtype:
+        raise ValueError("bad output tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    st_ = lib.libconv_forward_algo(_ptr(x), _ptr(w), _ptr(b), _ptr(y), N, C, T, H, W, K, KT, KH,
+                                   KW, pt, ph, pw, st, sh, sw, dt, _ACTS[act], _ALGOS[algo],
+                                   stream)
+    if st_ != 0:
+        raise LibconvError(st_, "libconv_forward_algo")
+    return y
+
+
+def conv2d(x, w, b=None, stride=1, padding=0, act="none", algo="auto", out=None, stream=None):
+    if x.dim() != 4:
+        raise ValueError("conv2d takes NCHW")
+    return conv_nd(x, w, b, stride, padding, act, algo, out, stream)
+
+
+def conv3d(x, w, b=None, stride=1, padding=0, act="none", algo="auto", out=None, stream=None):
+    if x.dim() != 5:
+        raise ValueError("conv3d takes NCDHW")
+    return conv_nd(x, w, b, stride, padding, act, algo, out, stream)

@@ -1,0 +1,65 @@
+"""Build libconv.so (HIP, gfx950) in-tree.
+
+    python -m direct_implicit_gemm_amd.build
+
+Compiles each source with hipcc for gfx950 only, in parallel, and links the
+shared library next to this file.  Every build recompiles.
+"""
+from __future__ import annotations
+
+import concurrent.futures
+import os
+import subprocess
+import sys
+import tempfile
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_PATH = os.path.join(HERE, "libconv.so")
+SOURCES = ["api.cpp", "direct.hip", "igemm.hip"]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-Wall",
+    "-Werror",
+    "-Wno-unused-function",
+    # no packed-fp32 instructions in device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", INCLUDE,
+    "-I", CSRC,
+]
+
+
+def _compile(src: str, obj: str) -> None:
+    cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    err = "\n".join(l for l in r.stderr.splitlines()
+                    if "packed-fp32-ops' is not a recognized feature" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{err}")
+    if err.strip():
+        sys.stderr.write(err + "\n")
+
+
+def build(verbose: bool = True) -> str:
+    with tempfile.TemporaryDirectory(prefix="libconv_build_") as tmp:
+        objs = [os.path.join(tmp, s.rsplit(".", 1)[0] + ".o") for s in SOURCES]
+        with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+            list(ex.map(_compile, SOURCES, objs))
+        out_tmp = LIB_PATH + ".tmp"
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", out_tmp, *objs]
+        subprocess.run(cmd, check=True, capture_output=True, text=True)
+        os.replace(out_tmp, LIB_PATH)
+    if verbose:
+        print(f"built {LIB_PATH}")
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    build()

@@ -1,0 +1,272 @@
+// api.cpp -- the exported C ABI of libconv: argument validation, output
+// extents, the shape-driven dispatcher and the launch.
+//
+// Error conventions follow the fault-tolerant backend bring-up of the page
+// "OpenCL-101 issue 52" (githubissues.com/ysh329/OpenCL-101/52): nothing here
+// aborts; every failure is a status the caller can inspect, and whether the
+// device is usable is a query (libconv_device_supported).  Unsupported shapes
+// are reported, never silently sent elsewhere (the page "SeedVR2 NCNN
+// Vulkan", section 3.6, on a Convolution3D that fell back to the CPU).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <initializer_list>
+#include <mutex>
+
+#include "internal.h"
+#include "libconv.h"
+
+namespace libconv {
+namespace {
+
+constexpr long long kMaxBytes = 0x7fffffffLL;  // byte offsets are 32-bit signed in the kernels
+
+// a * b, saturated well below overflow (every factor here is a non-negative int)
+long long mul_sat(long long a, long long b) {
+  constexpr long long kCap = 1LL << 62;
+  if (a == 0 || b == 0) return 0;
+  if (a > kCap / b) return kCap;
+  return a * b;
+}
+
+long long product(std::initializer_list<long long> v) {
+  long long r = 1;
+  for (long long f : v) r = mul_sat(r, f);
+  return r;
+}
+
+long long out_extent(long long in, long long k, long long pad, long long stride) {
+  if (in < 1 || k < 1 || pad < 0 || stride < 1) return -1;
+  const long long span = in + 2 * pad - k;
+  if (span < 0) return -1;
+  return span / stride + 1;
+}
+
+bool overlaps(const void* a, long long abytes, const void* b, long long bbytes) {
+  if (!a || !b || abytes <= 0 || bbytes <= 0) return false;
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+// Checks everything that can be checked without a GPU and fills the output
+// extents.  Pointers are only checked when `with_pointers` is set.
+libconv_status validate(Problem& p, int algo, bool with_pointers) {
+  if (p.dtype != LIBCONV_F32 && p.dtype != LIBCONV_F16 && p.dtype != LIBCONV_BF16)
+    return LIBCONV_ERR_BAD_DTYPE;
+  if (p.act != LIBCONV_ACT_NONE && p.act != LIBCONV_ACT_RELU) return LIBCONV_ERR_BAD_ACTIVATION;
+  if (algo != LIBCONV_ALGO_AUTO && algo != LIBCONV_ALGO_DIRECT && algo != LIBCONV_ALGO_IGEMM)
+    return LIBCONV_ERR_BAD_ALGO;
+  if (p.N < 0 || p.C < 1 || p.T < 1 || p.H < 1 || p.W < 1 || p.K < 1 || p.KT < 1 || p.KH < 1 ||
+      p.KW < 1)
+    return LIBCONV_ERR_BAD_SHAPE;
+  const long long ot = out_extent(p.T, p.KT, p.pt, p.st);
+  const long long oh = out_extent(p.H, p.KH, p.ph, p.sh);
+  const long long ow = out_extent(p.W, p.KW, p.pw, p.sw);
+  if (ot < 1 || oh < 1 || ow < 1) return LIBCONV_ERR_BAD_SHAPE;
+  if (ot > 0x7fffffff || oh > 0x7fffffff || ow > 0x7fffffff) return LIBCONV_ERR_TOO_LARGE;
+  p.OT = (int)ot;
+  p.OH = (int)oh;
+  p.OW = (int)ow;
+  const long long eb = dtype_bytes(p.dtype);
+  const long long xb = product({p.N, p.C, p.T, p.H, p.W, eb});
+  const long long wb = product({p.K, p.C, p.KT, p.KH, p.KW, eb});
+  const long long yb = product({p.N, p.K, ot, oh, ow, eb});
+  if (xb > kMaxBytes || wb > kMaxBytes || yb > kMaxBytes) return LIBCONV_ERR_TOO_LARGE;
+  if (with_pointers) {
+    if (!p.x || !p.w || !p.y) return LIBCONV_ERR_NULL_POINTER;
+    if (yb > 0 && (overlaps(p.y, yb, p.x, xb) || overlaps(p.y, yb, p.w, wb) ||
+                   overlaps(p.y, yb, p.b, (long long)p.K * eb)))
+      return LIBCONV_ERR_ALIAS;
+  }
+  return LIBCONV_OK;
+}
+
+// Per-device "is this a gfx950" cache, filled once per process.
+constexpr int kMaxDevices = 64;
+std::once_flag g_dev_once;
+int g_dev_count = 0;
+bool g_dev_ok[kMaxDevices];
+
+void init_devices() {
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n < 0) n = 0;
+  if (n > kMaxDevices) n = kMaxDevices;
+  for (int d = 0; d < n; ++d) {
+    hipDeviceProp_t prop;
+    g_dev_ok[d] = hipGetDeviceProperties(&prop, d) == hipSuccess &&
+                  std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  }
+  g_dev_count = n;
+  (void)hipGetLastError();  // a host without GPUs leaves an error behind: clear it
+}
+
+bool device_ok(int d) {
+  std::call_once(g_dev_once, init_devices);
+  return d >= 0 && d < g_dev_count && g_dev_ok[d];
+}
+
+// The dispatcher.  The vector-ALU direct kernel takes layers whose
+// reduction per output (C_in * taps) is too short to fill an MFMA k-step
+// pipeline -- stems with 3 input channels, thin pointwise layers -- and any
+// geometry the MFMA family has no tile for; everything else is an implicit
+// GEMM on the matrix cores.
+constexpr long long kMinMfmaReduction = 64;
+
+libconv_status plan_for(const Problem& p, int algo, Plan* plan) {
+  const long long red = (long long)p.C * p.KT * p.KH * p.KW;
+  Plan ig, dr;
+  const bool has_ig = igemm_plan(p, &ig);
+  const bool has_dr = direct_plan(p, &dr);
+  if (algo == LIBCONV_ALGO_IGEMM) {
+    if (!has_ig) return LIBCONV_ERR_UNSUPPORTED;
+    *plan = ig;
+    return LIBCONV_OK;
+  }
+  if (algo == LIBCONV_ALGO_DIRECT) {
+    if (!has_dr) return LIBCONV_ERR_UNSUPPORTED;
+    *plan = dr;
+    return LIBCONV_OK;
+  }
+  if (has_ig && red >= kMinMfmaReduction) {
+    *plan = ig;
+    return LIBCONV_OK;
+  }
+  if (has_dr) {
+    *plan = dr;
+    return LIBCONV_OK;
+  }
+  if (has_ig) {
+    *plan = ig;
+    return LIBCONV_OK;
+  }
+  return LIBCONV_ERR_UNSUPPORTED;
+}
+
+libconv_status run(Problem& p, int algo) {
+  libconv_status st = validate(p, algo, true);
+  if (st != LIBCONV_OK) return st;
+  if (p.N == 0) return LIBCONV_OK;  // empty batch: nothing to compute
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || !device_ok(dev)) {
+    (void)hipGetLastError();
+    return LIBCONV_ERR_NO_DEVICE;
+  }
+  Plan plan;
+  st = plan_for(p, algo, &plan);
+  if (st != LIBCONV_OK) return st;
+  if (std::getenv("LIBCONV_LOG")) {
+    const char* name = plan.algo == LIBCONV_ALGO_DIRECT ? direct_tile_name(plan.tile)
+                                                        : igemm_tile_name(plan.tile);
+    std::fprintf(stderr, "libconv: %s grid=%lld (N=%d C=%d T=%d H=%d W=%d K=%d k=%dx%dx%d)\n",
+                 name ? name : "?", plan.grid, p.N, p.C, p.T, p.H, p.W, p.K, p.KT, p.KH, p.KW);
+  }
+  return plan.algo == LIBCONV_ALGO_DIRECT ? direct_launch(p, plan) : igemm_launch(p, plan);
+}
+
+Problem make_problem(const void* x, const void* w, const void* bias, void* y, int N, int C_in,
+                     int T, int H, int W, int C_out, int KT, int KH, int KW, int pad_t, int pad_h,
+                     int pad_w, int stride_t, int stride_h, int stride_w, int dtype, int act,
+                     void* stream) {
+  Problem p;
+  std::memset(&p, 0, sizeof(p));
+  p.N = N; p.C = C_in; p.T = T; p.H = H; p.W = W;
+  p.K = C_out; p.KT = KT; p.KH = KH; p.KW = KW;
+  p.pt = pad_t; p.ph = pad_h; p.pw = pad_w;
+  p.st = stride_t; p.sh = stride_h; p.sw = stride_w;
+  p.dtype = dtype; p.act = act;
+  p.x = x; p.w = w; p.b = bias; p.y = y;
+  p.stream = reinterpret_cast<hipStream_t>(stream);
+  return p;
+}
+
+}  // namespace
+}  // namespace libconv
+
+using namespace libconv;
+
+extern "C" {
+
+libconv_status conv2d_forward(const void* x, const void* w, const void* bias, void* y, int N,
+                              int C_in, int H, int W, int C_out, int KH, int KW, int pad_h,
+                              int pad_w, int stride_h, int stride_w, int dtype, int act,
+                              void* stream) {
+  Problem p = make_problem(x, w, bias, y, N, C_in, 1, H, W, C_out, 1, KH, KW, 0, pad_h, pad_w, 1,
+                           stride_h, stride_w, dtype, act, stream);
+  return run(p, LIBCONV_ALGO_AUTO);
+}
+
+libconv_status conv3d_forward(const void* x, const void* w, const void* bias, void* y, int N,
+                              int C_in, int T, int H, int W, int C_out, int KT, int KH, int KW,
+                              int pad_t, int pad_h, int pad_w, int stride_t, int stride_h,
+                              int stride_w, int dtype, int act, void* stream) {
+  Problem p = make_problem(x, w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW, pad_t, pad_h, pad_w,
+                           stride_t, stride_h, stride_w, dtype, act, stream);
+  return run(p, LIBCONV_ALGO_AUTO);
+}
+
+libconv_status libconv_forward_algo(const void* x, const void* w, const void* bias, void* y, int N,
+                                    int C_in, int T, int H, int W, int C_out, int KT, int KH,
+                                    int KW, int pad_t, int pad_h, int pad_w, int stride_t,
+                                    int stride_h, int stride_w, int dtype, int act, int algo,
+                                    void* stream) {
+  Problem p = make_problem(x, w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW, pad_t, pad_h, pad_w,
+                           stride_t, stride_h, stride_w, dtype, act, stream);
+  return run(p, algo);
+}
+
+libconv_status libconv_query_algo(int N, int C_in, int T, int H, int W, int C_out, int KT, int KH,
+                                  int KW, int pad_t, int pad_h, int pad_w, int stride_t,
+                                  int stride_h, int stride_w, int dtype, int act, int algo,
+                                  int* algo_out, int* tile_out, long long* grid_out) {
+  if (!algo_out || !tile_out || !grid_out) return LIBCONV_ERR_NULL_POINTER;
+  Problem p = make_problem(nullptr, nullptr, nullptr, nullptr, N, C_in, T, H, W, C_out, KT, KH, KW,
+                           pad_t, pad_h, pad_w, stride_t, stride_h, stride_w, dtype, act, nullptr);
+  libconv_status st = validate(p, algo, false);
+  if (st != LIBCONV_OK) return st;
+  Plan plan;
+  st = plan_for(p, algo, &plan);
+  if (st != LIBCONV_OK) return st;
+  *algo_out = plan.algo;
+  *tile_out = plan.tile;
+  *grid_out = p.N == 0 ? 0 : plan.grid;
+  return LIBCONV_OK;
+}
+
+const char* libconv_tile_name(int tile_id) {
+  const char* n = direct_tile_name(tile_id);
+  if (!n) n = igemm_tile_name(tile_id);
+  return n ? n : "?";
+}
+
+int libconv_out_size(int in, int k, int pad, int stride) {
+  const long long o = out_extent(in, k, pad, stride);
+  return (o < 1 || o > 0x7fffffff) ? -1 : (int)o;
+}
+
+const char* libconv_status_string(int status) {
+  switch (status) {
+    case LIBCONV_OK: return "ok";
+    case LIBCONV_ERR_NULL_POINTER: return "null pointer";
+    case LIBCONV_ERR_BAD_SHAPE: return "bad shape";
+    case LIBCONV_ERR_BAD_DTYPE: return "bad dtype";
+    case LIBCONV_ERR_BAD_ACTIVATION: return "bad activation";
+    case LIBCONV_ERR_ALIAS: return "output overlaps an input";
+    case LIBCONV_ERR_UNSUPPORTED: return "unsupported shape for the requested algorithm";
+    case LIBCONV_ERR_NO_DEVICE: return "no gfx950 device";
+    case LIBCONV_ERR_LAUNCH: return "kernel launch failed";
+    case LIBCONV_ERR_BAD_ALGO: return "bad algorithm";
+    case LIBCONV_ERR_TOO_LARGE: return "tensor too large";
+    default: return "unknown status";
+  }
+}
+
+libconv_status libconv_device_supported(int device) {
+  return device_ok(device) ? LIBCONV_OK : LIBCONV_ERR_NO_DEVICE;
+}
+
+int libconv_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,524 @@
+// igemm.hip -- implicit-GEMM convolution on the gfx950 matrix cores (MFMA).
+//
+// The convolution of the page "PP-OCR on Vulkan compute shaders" (section
+// 2.2; the frame axis as in the Convolution3D layer of "SeedVR2 NCNN Vulkan",
+// section 3.2) is, for wide layers, a dense contraction:
+//     Y[co][px] = sum_k Wm[co][k] * Xcol[k][px],   k = (ci, kt, kh, kw)
+// with Xcol the zero-padded input window of each output pixel (im2col).  The
+// im2col matrix is never materialised in memory: each workgroup stages the
+// input halo of its pixel tile in LDS and the MFMA operands are read from it
+// at per-tap offsets.
+//
+// Workgroup tile: BM output channels x (TH x TW) output pixels of one output
+// plane (n, ot); four waves in a WM x WN grid, each owning (BM/WM) x (BN/WN)
+// outputs as 32x32 MFMA blocks held in fp32 accumulators.
+//
+// K loop: stages of CK = CG * SE input channels (SE = 8 for 16-bit types,
+// 4 for fp32: one 16-byte "slot"), all taps at once.  Per stage:
+//   * weights  W[co][ci][taps] (contiguous per co) are read with 16-byte
+//     loads and transposed into LDS as Wl[slot][co][SE], slot = tap*CG + g;
+//   * the input halo (KT frames x HR rows x HC cols) is read row-contiguously
+//     and written channel-innermost as Xl[g][kt][hr][hc][SE]; taps outside
+//     the input are zero (this is the padding);
+//   * the stage's slots are consumed in pairs by one MFMA k-step (32x32x16
+//     f16/bf16: lanes 0-31 carry slot 2p, lanes 32-63 slot 2p+1) or by four
+//     (32x32x2 f32, one element of each slot per step).  Both operands of a
+//     slot are single 16-byte LDS reads.
+// LDS holds two stages; the global loads of stage s+1 are in flight while
+// stage s is multiplied.
+//
+// Epilogue (shared with the direct kernel): fp32 accumulator + bias ->
+// optional ReLU -> one round-to-nearest-even conversion -> store, with the
+// 32 lanes of a half-wave writing 32 consecutive output pixels of one
+// channel.  Every output element has exactly one writer.
+#include "device_common.h"
+#include "internal.h"
+
+namespace libconv {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <int DT> struct Mma;
+
+template <> struct Mma<DT_F16> {
+  static constexpr int SE = 8;  // elements per 16-byte slot
+  __device__ static __forceinline__ void step(const u32x4_t& a, const u32x4_t& b, float16_t& c) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a),
+                                               __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
+  }
+};
+
+template <> struct Mma<DT_BF16> {
+  static constexpr int SE = 8;
+  __device__ static __forceinline__ void step(const u32x4_t& a, const u32x4_t& b, float16_t& c) {
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+};
+
+template <> struct Mma<DT_F32> {
+  static constexpr int SE = 4;
+  __device__ static __forceinline__ void step(const u32x4_t& a, const u32x4_t& b, float16_t& c) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      c = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, a[k]),
+                                               __builtin_bit_cast(float, b[k]), c, 0, 0, 0);
+  }
+};
+
+struct IgemmArgs {
+  const void* x;
+  const void* w;
+  const void* b;
+  void* y;
+  int N, C, T, H, W, K;
+  int OT, OH, OW;
+  int pt, ph, pw;
+  int st;             // time stride (the spatial strides are template parameters)
+  int relu;
+  int stages;         // ceil(C / CK)
+  int co_tiles, row_tiles, col_tiles;
+  uint32_t x_bytes, w_bytes, b_bytes, y_bytes;
+};
+
+template <int DT_, int KT_, int KH_, int KW_, int SH_, int SW_, int BM_, int TH_, int TW_,
+          int WM_, int WN_, int CG_>
+struct Cfg {
+  static constexpr int DT = DT_, KT = KT_, KH = KH_, KW = KW_, SH = SH_, SW = SW_;
+  static constexpr int BM = BM_, TH = TH_, TW = TW_, WM = WM_, WN = WN_, CG = CG_;
+  static constexpr int EB = Elem<DT>::bytes;
+  static constexpr int SE = Mma<DT>::SE;
+  static constexpr int CK = CG * SE;
+  static constexpr int TS = KT * KH * KW;
+  static constexpr int NSLOT = TS * CG;
+  static constexpr int NPAIR = (NSLOT + 1) / 2;
+  static constexpr int BN = TH * TW;
+  static constexpr int HR = (TH - 1) * SH + KH;
+  static constexpr int HC = (TW - 1) * SW + KW;
+  static constexpr int XPLANE = KT * HR * HC;      // halo pixels per channel group
+  static constexpr int WBYTES = NSLOT * BM * 16;
+  static constexpr int XBYTES = CG * XPLANE * 16;
+  static constexpr int BUF = WBYTES + XBYTES;
+  static constexpr int LDS = 2 * BUF;
+  static constexpr int WTM = BM / WM, WTN = BN / WN;
+  static constexpr int FA = WTM / 32, FB = WTN / 32;
+  static constexpr int BPR = TW / 32;              // 32-pixel blocks per tile row
+  // weight staging: QN 16-byte vectors per output channel per stage
+  static constexpr int QN = CG * TS;
+  static constexpr int WROWS = kThreads / QN;      // channels loaded per pass
+  static constexpr int WPASS = (BM + WROWS - 1) / WROWS;
+  // input staging: one unit = one halo pixel of one channel group
+  static constexpr int XUNITS = CG * XPLANE;
+  static constexpr int XPASS = (XUNITS + kThreads - 1) / kThreads;
+
+  static_assert(WM * WN == 4, "four waves");
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
+  static_assert(TW % 32 == 0, "tile rows are whole 32-pixel blocks");
+  static_assert(QN <= kThreads, "weight stage too wide");
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+// Global -> registers for one stage.
+template <class G>
+struct StageRegs {
+  u32x4_t wv[G::WPASS];
+  u32x4_t xv[G::XPASS];
+};
+
+template <class G>
+__global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
+  using E = Elem<G::DT>;
+  constexpr int EB = G::EB;
+  constexpr int SE = G::SE;
+  __shared__ __attribute__((aligned(16))) unsigned char lds[G::LDS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int il = lane & 31;   // row (A) / column (B) inside a 32x32 block
+  const int hf = lane >> 5;   // which slot of the pair this lane carries
+
+  // ---- tile coordinates; XCD-aware order: the hardware deals workgroups to
+  // the 8 XCDs round-robin, so consecutive logical tiles (same output-channel
+  // tile, neighbouring pixel tiles) are gathered onto one XCD and its L2.
+  const int G_ = gridDim.x;
+  int bid = blockIdx.x;
+  if ((G_ & 7) == 0) bid = (bid & 7) * (G_ >> 3) + (bid >> 3);
+  const int ctile = bid % a.col_tiles;
+  bid /= a.col_tiles;
+  const int rtile = bid % a.row_tiles;
+  bid /= a.row_tiles;
+  const int ot = bid % a.OT;
+  bid /= a.OT;
+  const int n = bid % a.N;
+  const int cot = bid / a.N;
+  const int co0 = cot * G::BM;
+  const int oh0 = rtile * G::TH;
+  const int ow0 = ctile * G::TW;
+  const int ih0 = oh0 * G::SH - a.ph;
+  const int iw0 = ow0 * G::SW - a.pw;
+  const int it0 = ot * a.st - a.pt;
+
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.w, a.w_bytes);
+  constexpr int kOob = 0x7ffffff0;  // byte offset beyond any tensor: reads 0
+
+  // ---- per-thread weight staging geometry (fixed across stages)
+  const int wq = tid % G::QN;            // which 16-byte vector of a channel's block
+  const int wrow = tid / G::QN;          // first channel (within the tile) of this thread
+  const bool wactive = wrow < G::WROWS;
+  int wdst[SE];                          // LDS byte offset of element j, channel 0
+  int wci[SE];                           // channel (within the stage) of element j
+#pragma unroll
+  for (int j = 0; j < SE; ++j) {
+    const int e = wq * SE + j;           // element within the [CK][TS] block
+    const int ci = e / G::TS;
+    const int tap = e - ci * G::TS;
+    const int slot = tap * G::CG + ci / SE;
+    wdst[j] = slot * G::BM * 16 + (ci % SE) * EB;
+    wci[j] = ci;
+  }
+  const int cstride = a.C * G::TS;       // elements between output channels in w
+  const int plane = a.T * a.H * a.W;     // elements between input channels in x
+
+  auto load_stage = [&](int s, StageRegs<G>& r) {
+    const int ci0 = s * G::CK;
+    // weights: vector wq of channels co0 + wrow + pass * WROWS
+#pragma unroll
+    for (int i = 0; i < G::WPASS; ++i) {
+      const int col = wrow + i * G::WROWS;
+      const int co = co0 + col;
+      int off = kOob;
+      if (wactive && col < G::BM && co < a.K) off = (co * cstride + ci0 * G::TS + wq * SE) * EB;
+      r.wv[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 0));
+    }
+    // input halo: unit u = ((g * KT + kt) * HR + hr) * HC + hc
+#pragma unroll
+    for (int i = 0; i < G::XPASS; ++i) {
+      const int u = tid + i * kThreads;
+      int v = u;
+      const int hc = v % G::HC;
+      v /= G::HC;
+      const int hr = v % G::HR;
+      v /= G::HR;
+      const int kt = v % G::KT;
+      const int g = v / G::KT;
+      const int ih = ih0 + hr, iw = iw0 + hc, it = it0 + kt;
+      const bool ok = u < G::XUNITS && (unsigned)ih < (unsigned)a.H &&
+                      (unsigned)iw < (unsigned)a.W && (unsigned)it < (unsigned)a.T;
+      const int cbase = ci0 + g * SE;
+      const int base = (((n * a.C + cbase) * a.T + it) * a.H + ih) * a.W + iw;
+      uint32_t e[SE];
+#pragma unroll
+      for (int j = 0; j < SE; ++j) {
+        const int off = (ok && cbase + j < a.C) ? (base + j * plane) * EB : kOob;
+        e[j] = E::load_bits(xr, off);
+      }
+      if constexpr (SE == 8) {
+        r.xv[i] = u32x4_t{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
+                          e[6] | (e[7] << 16)};
+      } else {
+        r.xv[i] = u32x4_t{e[0], e[1], e[2], e[3]};
+      }
+    }
+  };
+
+  auto store_stage = [&](int s, const StageRegs<G>& r, unsigned char* buf) {
+    const int ci0 = s * G::CK;
+    // weights: transpose [ci][tap] -> [slot][co][ci % SE]
+#pragma unroll
+    for (int i = 0; i < G::WPASS; ++i) {
+      const int col = wrow + i * G::WROWS;
+      if (wactive && col < G::BM) {
+#pragma unroll
+        for (int j = 0; j < SE; ++j) {
+          const bool cok = ci0 + wci[j] < a.C;
+          unsigned char* dst = buf + wdst[j] + col * 16;
+          if constexpr (SE == 8) {
+            const uint32_t word = r.wv[i][j >> 1];
+            const uint16_t h = (uint16_t)((j & 1) ? (word >> 16) : (word & 0xffffu));
+            *reinterpret_cast<uint16_t*>(dst) = cok ? h : (uint16_t)0;
+          } else {
+            *reinterpret_cast<uint32_t*>(dst) = cok ? r.wv[i][j] : 0u;
+          }
+        }
+      }
+    }
+    // input halo
+    unsigned char* xbuf = buf + G::WBYTES;
+#pragma unroll
+    for (int i = 0; i < G::XPASS; ++i) {
+      const int u = tid + i * kThreads;
+      if (u < G::XUNITS) *reinterpret_cast<u32x4_t*>(xbuf + u * 16) = r.xv[i];
+    }
+  };
+
+  // ---- MFMA operand addressing
+  const int wm = wave % G::WM;
+  const int wn = wave / G::WM;
+  const int co_w0 = wm * G::WTM;
+  const int blk0 = wn * G::FB;                       // first 32-pixel block of this wave
+  const int prow0 = blk0 / G::BPR, pcol0 = (blk0 % G::BPR) * 32;
+  // A: Wl[slot][co][16 B]; lanes of half hf read slot 2p + hf.
+  const int a_lane = ((hf * G::BM) + co_w0 + il) * 16;
+  // B: Xl[g][kt][hr][hc][16 B] at the lane's pixel.
+  const int b_lane = ((prow0 * G::SH) * G::HC + (pcol0 + il) * G::SW) * 16;
+
+  float16_t acc[G::FA][G::FB];
+#pragma unroll
+  for (int i = 0; i < G::FA; ++i)
+#pragma unroll
+    for (int j = 0; j < G::FB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // byte offset of slot s inside the halo area (pixel (0,0) of the tile)
+  auto xslot = [](int s) constexpr -> int {
+    const int tap = s / G::CG, g = s % G::CG;
+    const int kt = tap / (G::KH * G::KW);
+    const int kh = (tap / G::KW) % G::KH;
+    const int kw = tap % G::KW;
+    return (((g * G::KT + kt) * G::HR + kh) * G::HC + kw) * 16;
+  };
+  // byte offset of block j of this wave relative to its first block
+  auto xblock = [&](int j) -> int {
+    const int b = blk0 + j;
+    const int r = b / G::BPR, c = (b % G::BPR) * 32;
+    return ((r - prow0) * G::SH * G::HC + (c - pcol0) * G::SW) * 16;
+  };
+
+  auto compute = [&](const unsigned char* buf) {
+    const unsigned char* wl = buf;
+    const unsigned char* xl = buf + G::WBYTES;
+    u32x4_t fa[2][G::FA], fb[2][G::FB];
+    auto load_frags = [&](int p, int k) {
+      const int s0 = 2 * p;
+      const int s1 = (2 * p + 1 < G::NSLOT) ? 2 * p + 1 : 2 * p;
+      const int xo = hf ? xslot(s1) : xslot(s0);
+#pragma unroll
+      for (int i = 0; i < G::FA; ++i)
+        fa[k][i] = *reinterpret_cast<const u32x4_t*>(wl + a_lane + (s0 * G::BM + i * 32) * 16);
+#pragma unroll
+      for (int j = 0; j < G::FB; ++j)
+        fb[k][j] = *reinterpret_cast<const u32x4_t*>(xl + b_lane + xo + xblock(j));
+      if (2 * p + 1 >= G::NSLOT && hf) {
+        // odd slot count: the second half of the last pair carries nothing
+#pragma unroll
+        for (int i = 0; i < G::FA; ++i) fa[k][i] = u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int j = 0; j < G::FB; ++j) fb[k][j] = u32x4_t{0u, 0u, 0u, 0u};
+      }
+    };
+    load_frags(0, 0);
+#pragma unroll
+    for (int p = 0; p < G::NPAIR; ++p) {
+      if (p + 1 < G::NPAIR) load_frags(p + 1, (p + 1) & 1);
+#pragma unroll
+      for (int i = 0; i < G::FA; ++i)
+#pragma unroll
+        for (int j = 0; j < G::FB; ++j) Mma<G::DT>::step(fa[p & 1][i], fb[p & 1][j], acc[i][j]);
+    }
+  };
+
+  // ---- main loop: two LDS stages, next stage's global loads in flight
+  StageRegs<G> regs;
+  load_stage(0, regs);
+  store_stage(0, regs, lds);
+  __syncthreads();
+  for (int s = 0; s < a.stages; ++s) {
+    unsigned char* cur = lds + (s & 1) * G::BUF;
+    unsigned char* nxt = lds + ((s + 1) & 1) * G::BUF;
+    const bool more = s + 1 < a.stages;
+    if (more) load_stage(s + 1, regs);
+    compute(cur);
+    if (more) store_stage(s + 1, regs, nxt);
+    __syncthreads();
+  }
+
+  // ---- epilogue
+  const __amdgpu_buffer_rsrc_t yr = make_rsrc(a.y, a.y_bytes);
+  const __amdgpu_buffer_rsrc_t br = make_rsrc(a.b, a.b_bytes);
+  const int ohw = a.OH * a.OW;
+#pragma unroll
+  for (int i = 0; i < G::FA; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int co = co0 + co_w0 + i * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+      if (co >= a.K) continue;
+      const float bias = a.b ? E::load(br, co * EB) : 0.0f;
+      const int cbase = ((n * a.K + co) * a.OT + ot) * ohw;
+#pragma unroll
+      for (int j = 0; j < G::FB; ++j) {
+        const int b = blk0 + j;
+        const int oh = oh0 + b / G::BPR;
+        const int ow = ow0 + (b % G::BPR) * 32 + il;
+        if (oh < a.OH && ow < a.OW)
+          E::store(epilogue(acc[i][j][r], bias, a.relu), yr, (cbase + oh * a.OW + ow) * EB);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ tiles
+using LaunchFn = hipError_t (*)(const IgemmArgs&, unsigned, hipStream_t);
+
+template <class G>
+hipError_t launch_cfg(const IgemmArgs& a, unsigned grid, hipStream_t s) {
+  hipLaunchKernelGGL(igemm_kernel<G>, dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+struct TileDesc {
+  int id;
+  int wide;       // 0: fp32 operands, 1: 16-bit operands
+  int KT, KH, KW, SH, SW;
+  int flat;       // 1: 1x1 stride-1 pad-0 layer viewed as one long row per plane
+  int BM, TH, TW, CG;
+  int lds;
+  const char* name;
+  LaunchFn fn[3];  // by libconv_dtype
+};
+
+// Launcher of a tile for one storage dtype, or null when the tile's operand
+// width does not match the dtype.
+template <int DT, int WIDE, int KT, int KH, int KW, int SH, int SW, int BM, int TH, int TW,
+          int WM, int WN, int CG>
+constexpr LaunchFn launcher() {
+  if constexpr ((DT == DT_F32) == (WIDE == 0))
+    return &launch_cfg<Cfg<DT, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG>>;
+  else
+    return nullptr;
+}
+
+#define LIBCONV_TILE(ID, WIDE, KT, KH, KW, SH, SW, FLAT, BM, TH, TW, WM, WN, CG, NAME)     \
+  {ID, WIDE, KT, KH, KW, SH, SW, FLAT, BM, TH, TW, CG,                                      \
+   Cfg<WIDE ? DT_F16 : DT_F32, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG>::LDS, NAME,      \
+   {launcher<DT_F32, WIDE, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG>(),                   \
+    launcher<DT_F16, WIDE, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG>(),                   \
+    launcher<DT_BF16, WIDE, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG>()}}
+
+const TileDesc kTiles[] = {
+    // 16-bit operands, 3x3 stride 1
+    LIBCONV_TILE(200, 1, 1, 3, 3, 1, 1, 0, 128, 8, 32, 2, 2, 2, "igemm16_k3s1_m128_n8x32"),
+    LIBCONV_TILE(201, 1, 1, 3, 3, 1, 1, 0, 128, 4, 32, 2, 2, 2, "igemm16_k3s1_m128_n4x32"),
+    LIBCONV_TILE(202, 1, 1, 3, 3, 1, 1, 0, 128, 2, 64, 2, 2, 2, "igemm16_k3s1_m128_n2x64"),
+    LIBCONV_TILE(203, 1, 1, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, "igemm16_k3s1_m64_n8x32"),
+    // 16-bit operands, 3x3 stride 2
+    LIBCONV_TILE(210, 1, 1, 3, 3, 2, 2, 0, 64, 4, 32, 2, 2, 2, "igemm16_k3s2_m64_n4x32"),
+    // 16-bit operands, 1x1 stride 1 pad 0 (flattened planes)
+    LIBCONV_TILE(220, 1, 1, 1, 1, 1, 1, 1, 128, 1, 256, 2, 2, 8, "igemm16_k1_m128_n256"),
+    LIBCONV_TILE(221, 1, 1, 1, 1, 1, 1, 1, 128, 1, 128, 2, 2, 8, "igemm16_k1_m128_n128"),
+    // 16-bit operands, 3x3x3 stride 1
+    LIBCONV_TILE(230, 1, 3, 3, 3, 1, 1, 0, 128, 8, 32, 2, 2, 1, "igemm16_k333s1_m128_n8x32"),
+    LIBCONV_TILE(231, 1, 3, 3, 3, 1, 1, 0, 128, 4, 32, 2, 2, 1, "igemm16_k333s1_m128_n4x32"),
+    // fp32 operands
+    LIBCONV_TILE(240, 0, 1, 3, 3, 1, 1, 0, 32, 8, 32, 1, 4, 4, "igemm32_k3s1_m32_n8x32"),
+    LIBCONV_TILE(241, 0, 1, 3, 3, 1, 1, 0, 64, 4, 32, 2, 2, 4, "igemm32_k3s1_m64_n4x32"),
+    LIBCONV_TILE(242, 0, 1, 3, 3, 2, 2, 0, 64, 2, 32, 2, 2, 4, "igemm32_k3s2_m64_n2x32"),
+    LIBCONV_TILE(243, 0, 1, 1, 1, 1, 1, 1, 64, 1, 128, 2, 2, 8, "igemm32_k1_m64_n128"),
+};
+
+#undef LIBCONV_TILE
+
+const TileDesc* find_tile(int id) {
+  for (const auto& t : kTiles)
+    if (t.id == id) return &t;
+  return nullptr;
+}
+
+bool is_flat(const Problem& p) {
+  return p.KT == 1 && p.KH == 1 && p.KW == 1 && p.st == 1 && p.sh == 1 && p.sw == 1 &&
+         p.pt == 0 && p.ph == 0 && p.pw == 0;
+}
+
+bool tile_fits(const TileDesc& t, const Problem& p) {
+  const int wide = p.dtype == LIBCONV_F32 ? 0 : 1;
+  if (t.wide != wide) return false;
+  const int se = wide ? 8 : 4;
+  if (p.C % se != 0) return false;  // 16-byte weight vectors must not straddle channels
+  if (t.flat) return is_flat(p);
+  return p.KT == t.KT && p.KH == t.KH && p.KW == t.KW && p.sh == t.SH && p.sw == t.SW &&
+         (t.KT > 1 || (p.st == 1 && p.pt == 0));
+}
+
+struct TileCounts {
+  long long co, rows, cols, total;
+};
+
+TileCounts counts(const TileDesc& t, const Problem& p) {
+  TileCounts c;
+  c.co = (p.K + t.BM - 1) / t.BM;
+  if (t.flat) {
+    c.rows = 1;
+    c.cols = ((long long)p.OH * p.OW + t.TW - 1) / t.TW;
+  } else {
+    c.rows = (p.OH + t.TH - 1) / t.TH;
+    c.cols = (p.OW + t.TW - 1) / t.TW;
+  }
+  c.total = c.co * p.N * p.OT * c.rows * c.cols;
+  return c;
+}
+
+}  // namespace
+
+const char* igemm_tile_name(int id) {
+  const TileDesc* t = find_tile(id);
+  return t ? t->name : nullptr;
+}
+
+bool igemm_plan(const Problem& p, Plan* plan) {
+  // Among the tiles that fit, minimise the critical path on 256 compute
+  // units: rounds of workgroups times the (padded) work of one tile.
+  const TileDesc* best = nullptr;
+  double best_cost = 0.0;
+  long long best_total = 0;
+  for (const auto& t : kTiles) {
+    if (!tile_fits(t, p)) continue;
+    const TileCounts c = counts(t, p);
+    const double rounds = (double)((c.total + 255) / 256);
+    const double cost = rounds * (double)t.BM * t.TH * t.TW;
+    if (!best || cost < best_cost * 0.999 ||
+        (cost <= best_cost * 1.001 && (long long)t.BM * t.TH * t.TW > (long long)best->BM * best->TH * best->TW)) {
+      best = &t;
+      best_cost = cost;
+      best_total = c.total;
+    }
+  }
+  if (!best) return false;
+  plan->algo = LIBCONV_ALGO_IGEMM;
+  plan->tile = best->id;
+  plan->grid = best_total;
+  return true;
+}
+
+libconv_status igemm_launch(const Problem& p, const Plan& plan) {
+  const TileDesc* t = find_tile(plan.tile);
+  if (!t || !tile_fits(*t, p)) return LIBCONV_ERR_UNSUPPORTED;
+  const LaunchFn fn = t->fn[p.dtype];
+  if (!fn) return LIBCONV_ERR_UNSUPPORTED;
+  const TileCounts c = counts(*t, p);
+  if (c.total > 0x7fffffffLL) return LIBCONV_ERR_UNSUPPORTED;
+  IgemmArgs a;
+  a.x = p.x; a.w = p.w; a.b = p.b; a.y = p.y;
+  a.N = p.N; a.C = p.C; a.T = p.T; a.K = p.K; a.OT = p.OT;
+  if (t->flat) {  // a 1x1 layer: each plane is one row of H*W pixels
+    a.H = 1; a.W = p.H * p.W; a.OH = 1; a.OW = p.OH * p.OW;
+  } else {
+    a.H = p.H; a.W = p.W; a.OH = p.OH; a.OW = p.OW;
+  }
+  a.pt = p.pt; a.ph = p.ph; a.pw = p.pw; a.st = p.st;
+  a.relu = p.act == LIBCONV_ACT_RELU;
+  const int ck = t->CG * (t->wide ? 8 : 4);
+  a.stages = (p.C + ck - 1) / ck;
+  a.co_tiles = (int)c.co; a.row_tiles = (int)c.rows; a.col_tiles = (int)c.cols;
+  const int eb = dtype_bytes(p.dtype);
+  a.x_bytes = (uint32_t)((long long)p.N * p.C * p.T * p.H * p.W * eb);
+  a.w_bytes = (uint32_t)((long long)p.K * p.C * p.KT * p.KH * p.KW * eb);
+  a.b_bytes = p.b ? (uint32_t)(p.K * eb) : 0u;
+  a.y_bytes = (uint32_t)((long long)p.N * p.K * p.OT * p.OH * p.OW * eb);
+  const hipError_t e = fn(a, (unsigned)c.total, p.stream);
+  return e == hipSuccess ? LIBCONV_OK : LIBCONV_ERR_LAUNCH;
+}
+
+}  // namespace libconv

@@ -1,0 +1,50 @@
+// internal.h -- types shared by the host side of libconv (validation,
+// dispatch) and the two kernel families.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+#include "libconv.h"
+
+namespace libconv {
+
+// One convolution call, normalised to the 3-D form (2-D: T = KT = 1,
+// pt = 0, st = 1).  K is C_out.  Output extents are filled by validation.
+struct Problem {
+  int N, C, T, H, W;
+  int K, KT, KH, KW;
+  int pt, ph, pw;
+  int st, sh, sw;
+  int OT, OH, OW;
+  int dtype;  // libconv_dtype
+  int act;    // libconv_act
+  const void* x;
+  const void* w;
+  const void* b;  // may be null
+  void* y;
+  hipStream_t stream;
+};
+
+// What the dispatcher decided.
+struct Plan {
+  int algo;         // LIBCONV_ALGO_DIRECT or LIBCONV_ALGO_IGEMM
+  int tile;         // tile configuration id (see tile_name)
+  long long grid;   // workgroups
+};
+
+inline int dtype_bytes(int dt) { return dt == LIBCONV_F32 ? 4 : 2; }
+
+// Direct (vector ALU) family: every shape is supported.
+bool direct_plan(const Problem& p, Plan* plan);
+libconv_status direct_launch(const Problem& p, const Plan& plan);
+
+// Implicit-GEMM (MFMA) family: a fixed set of geometries; returns false
+// when the shape is not one of them.
+bool igemm_plan(const Problem& p, Plan* plan);
+libconv_status igemm_launch(const Problem& p, const Plan& plan);
+
+const char* direct_tile_name(int id);
+const char* igemm_tile_name(int id);
+
+}  // namespace libconv

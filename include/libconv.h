@@ -1,0 +1,171 @@
+/*
+ * libconv.h -- forward 2-D / 3-D convolution on AMD Instinct MI355X (gfx950).
+ *
+ * Plain C ABI: no C++ types, no HIP headers needed by callers.
+ *
+ * What every convolution entry point computes (the definition):
+ *   y[n][co][o] = act( b[co] + sum_{ci < C_in} sum_{k in taps} xz[n][ci][o*s - p + k] * w[co][ci][k] )
+ * where o, k, s, p are per-axis (h, w) or (t, h, w) indices, xz is x inside the
+ * input and 0 outside (zero padding), there is no kernel flip, and act is the
+ * identity or ReLU (max(v, 0)), applied after the bias.  This is the
+ * gather-form direct convolution of the page "PP-OCR on Vulkan compute
+ * shaders" (lpnh.cn/news/2745477), section 2.2 (output coordinate -> input
+ * coordinate, out-of-range taps skipped, bias added per output channel),
+ * with the ReLU fused into the write-back as in section 4.4 of that page, and
+ * with one more spatial axis (frames) for the Convolution3D layer of the page
+ * "SeedVR2 NCNN Vulkan" (Tencent/ncnn discussion 7001), section 3.2.
+ *
+ * Output extent per axis: out = floor((in + 2*pad - k) / stride) + 1; a
+ * geometry whose window does not fit (in + 2*pad < k) is rejected.
+ *
+ * Conventions shared by every entry point:
+ *   Ownership   x, w, bias and y are DEVICE pointers owned by the caller, in
+ *               dense row-major layout (x NCHW / NCDHW, w OIHW / OIDHW,
+ *               y NCHW / NCDHW), aligned at least to their element size.
+ *               libconv keeps no pointer after the call returns, allocates
+ *               nothing, copies nothing between host and device and never
+ *               synchronises the host.
+ *   Stream      work is enqueued on `stream` (a hipStream_t; NULL means the
+ *               null stream) and the call returns as soon as it is enqueued.
+ *               Inputs must stay valid until the stream reaches the kernel.
+ *               The call makes no allocation and no host sync, so it may be
+ *               recorded into a HIP graph.
+ *   Dtypes      x, w, bias and y share one storage dtype (libconv_dtype).
+ *               Products and sums are formed in fp32 (fp16/bf16 products are
+ *               exact in fp32) and y is rounded once, to nearest even.
+ *   Errors      argument errors are returned before anything is enqueued;
+ *               a failed launch returns LIBCONV_ERR_LAUNCH.  Nothing aborts or
+ *               prints.  A shape no kernel supports returns
+ *               LIBCONV_ERR_UNSUPPORTED; there is no silent fallback to
+ *               another device or to the host.
+ *   Limits      every tensor must hold fewer than 2^31 elements; all sizes
+ *               must be >= 1 except N, which may be 0 (nothing is enqueued).
+ *   Threads     calls from several host threads are safe; the only shared
+ *               state is a per-device property cache filled once.
+ */
+#ifndef LIBCONV_H
+#define LIBCONV_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LIBCONV_F32 = 0,   /* IEEE binary32 */
+  LIBCONV_F16 = 1,   /* IEEE binary16 */
+  LIBCONV_BF16 = 2   /* bfloat16 (upper half of binary32) */
+} libconv_dtype;
+
+typedef enum {
+  LIBCONV_ACT_NONE = 0,
+  LIBCONV_ACT_RELU = 1
+} libconv_act;
+
+/* Kernel families the dispatcher chooses between. */
+typedef enum {
+  LIBCONV_ALGO_AUTO = 0,    /* shape-driven choice (the default) */
+  LIBCONV_ALGO_DIRECT = 1,  /* LDS halo-tiled direct kernel on the vector ALUs */
+  LIBCONV_ALGO_IGEMM = 2    /* implicit GEMM on the matrix cores (MFMA) */
+} libconv_algo;
+
+typedef enum {
+  LIBCONV_OK = 0,
+  LIBCONV_ERR_NULL_POINTER = 1,   /* x, w or y is NULL */
+  LIBCONV_ERR_BAD_SHAPE = 2,      /* a size < 1 (N < 0), stride < 1, pad < 0,
+                                     channel mismatch, or the window does not fit */
+  LIBCONV_ERR_BAD_DTYPE = 3,      /* dtype is not a libconv_dtype */
+  LIBCONV_ERR_BAD_ACTIVATION = 4, /* act is not a libconv_act */
+  LIBCONV_ERR_ALIAS = 5,          /* y overlaps x, w or bias */
+  LIBCONV_ERR_UNSUPPORTED = 6,    /* the requested algorithm cannot run this shape */
+  LIBCONV_ERR_NO_DEVICE = 7,      /* no HIP device, or the current device is not gfx950 */
+  LIBCONV_ERR_LAUNCH = 8,         /* the kernel launch failed */
+  LIBCONV_ERR_BAD_ALGO = 9,       /* algo is not a libconv_algo */
+  LIBCONV_ERR_TOO_LARGE = 10      /* a tensor holds 2^31 or more elements */
+} libconv_status;
+
+/*
+ * 2-D convolution.
+ *   x    [N][C_in][H][W]          device, read only
+ *   w    [C_out][C_in][KH][KW]    device, read only
+ *   bias [C_out] or NULL          device, read only; NULL means no bias
+ *   y    [N][C_out][OH][OW]       device, written (every element exactly once)
+ *   pad_*    zero padding added on both sides of the axis (>= 0)
+ *   stride_* step of the window (>= 1)
+ *   dtype    libconv_dtype of x, w, bias and y
+ *   act      libconv_act applied after the bias
+ *   stream   hipStream_t or NULL
+ * Definition: page "PP-OCR on Vulkan compute shaders", section 2.2 (batch
+ * added as an outer loop; per-axis pad and stride).
+ */
+libconv_status conv2d_forward(const void* x, const void* w, const void* bias, void* y,
+                              int N, int C_in, int H, int W, int C_out, int KH, int KW,
+                              int pad_h, int pad_w, int stride_h, int stride_w,
+                              int dtype, int act, void* stream);
+
+/*
+ * 3-D convolution over frames.
+ *   x    [N][C_in][T][H][W]          y [N][C_out][OT][OH][OW]
+ *   w    [C_out][C_in][KT][KH][KW]   bias [C_out] or NULL
+ * Other arguments as for conv2d_forward.
+ * Definition: the Convolution3D layer of the page "SeedVR2 NCNN Vulkan",
+ * section 3.2: the 2-D rule with the frame axis added (zero padding in time
+ * as in space).
+ */
+libconv_status conv3d_forward(const void* x, const void* w, const void* bias, void* y,
+                              int N, int C_in, int T, int H, int W,
+                              int C_out, int KT, int KH, int KW,
+                              int pad_t, int pad_h, int pad_w,
+                              int stride_t, int stride_h, int stride_w,
+                              int dtype, int act, void* stream);
+
+/*
+ * 3-D convolution with an explicit kernel family (libconv_algo).  With
+ * LIBCONV_ALGO_AUTO this is conv3d_forward.  A 2-D convolution is the case
+ * T = KT = 1, pad_t = 0, stride_t = 1.  Returns LIBCONV_ERR_UNSUPPORTED if
+ * the requested family cannot run the shape.  Meant for tests and for the
+ * evidence behind the dispatcher's choice.
+ */
+libconv_status libconv_forward_algo(const void* x, const void* w, const void* bias, void* y,
+                                    int N, int C_in, int T, int H, int W,
+                                    int C_out, int KT, int KH, int KW,
+                                    int pad_t, int pad_h, int pad_w,
+                                    int stride_t, int stride_h, int stride_w,
+                                    int dtype, int act, int algo, void* stream);
+
+/*
+ * Which kernel the dispatcher would launch for this shape, without launching.
+ * Arguments as for libconv_forward_algo (algo may force a family).  On
+ * LIBCONV_OK: *algo_out is LIBCONV_ALGO_DIRECT or LIBCONV_ALGO_IGEMM,
+ * *tile_out the tile configuration id (see libconv_tile_name) and
+ * *grid_out the number of workgroups.  Pure host arithmetic: works without a
+ * GPU.  Output pointers may not be NULL.
+ */
+libconv_status libconv_query_algo(int N, int C_in, int T, int H, int W,
+                                  int C_out, int KT, int KH, int KW,
+                                  int pad_t, int pad_h, int pad_w,
+                                  int stride_t, int stride_h, int stride_w,
+                                  int dtype, int act, int algo,
+                                  int* algo_out, int* tile_out, long long* grid_out);
+
+/* Human-readable name of a tile configuration id; "?" if unknown. */
+const char* libconv_tile_name(int tile_id);
+
+/* floor((in + 2*pad - k) / stride) + 1, or -1 if an argument is out of range
+ * (in < 1, k < 1, pad < 0, stride < 1) or the window does not fit. */
+int libconv_out_size(int in, int k, int pad, int stride);
+
+/* Static description of a status code; never NULL. */
+const char* libconv_status_string(int status);
+
+/* LIBCONV_OK if `device` exists and is a gfx950 GPU, else LIBCONV_ERR_NO_DEVICE.
+ * Never aborts; safe on a host without any GPU. */
+libconv_status libconv_device_supported(int device);
+
+/* Library version as 10000*major + 100*minor + patch. */
+int libconv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBCONV_H */

@@ -1,0 +1,122 @@
+"""Host-side checks of the libconv C ABI that need no GPU: the library loads
+and exports every function its header declares, the output-extent rule, the
+status strings, argument validation (which returns before any launch), and
+the dispatcher's choices."""
+import itertools
+
+import pytest
+
+import direct_implicit_gemm_amd as L
+import oracle
+import workloads as W
+
+
+def test_library_loads_and_exports_header_symbols():
+    lib = L.load()
+    names = L.header_functions()
+    assert {"conv2d_forward", "conv3d_forward", "libconv_forward_algo", "libconv_query_algo",
+            "libconv_out_size", "libconv_status_string", "libconv_device_supported",
+            "libconv_tile_name", "libconv_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_out_size_matches_oracle_extent():
+    """The library's closed form against the oracle's walked count."""
+    for n_in, k, p, s in itertools.product(range(1, 14), range(1, 8), range(0, 4), range(1, 5)):
+        want = oracle.out_extent(n_in, k, p, s)
+        got = L.libconv_out_size(n_in, k, p, s)
+        assert got == (want if want >= 1 else -1), (n_in, k, p, s)
+    for args in [(0, 3, 1, 1), (5, 0, 1, 1), (5, 3, -1, 1), (5, 3, 1, 0)]:
+        assert L.libconv_out_size(*args) == -1
+
+
+def test_status_strings():
+    for code in range(11):
+        assert L.libconv_status_string(code)
+    assert L.libconv_status_string(12345) == "unknown status"
+
+
+# A valid 2-D argument set (pointers are fake, non-null, non-overlapping:
+# validation never dereferences them and returns before any launch).
+X, Wp, B, Y = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+GOOD2 = dict(N=1, C_in=4, H=8, W=8, C_out=8, KH=3, KW=3, pad_h=1, pad_w=1, stride_h=1,
+             stride_w=1, dtype=L.F32, act=L.ACT_NONE)
+
+
+def call2(x=X, w=Wp, b=B, y=Y, **kw):
+    a = dict(GOOD2)
+    a.update(kw)
+    return L.conv2d_forward(x, w, b, y, a["N"], a["C_in"], a["H"], a["W"], a["C_out"], a["KH"],
+                            a["KW"], a["pad_h"], a["pad_w"], a["stride_h"], a["stride_w"],
+                            a["dtype"], a["act"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(x=None), 1), (dict(w=None), 1), (dict(y=None), 1),
+    (dict(C_in=0), 2), (dict(H=0), 2), (dict(C_out=0), 2), (dict(KH=0), 2), (dict(N=-1), 2),
+    (dict(stride_h=0), 2), (dict(pad_w=-1), 2), (dict(H=2, KH=5, pad_h=0), 2),
+    (dict(dtype=7), 3), (dict(dtype=-1), 3), (dict(act=2), 4), (dict(act=-3), 4),
+    (dict(y=X + 16), 5), (dict(y=Wp - 64), 5), (dict(b=Y + 4), 5),
+    (dict(H=70000, W=70000), 10),
+])
+def test_validation_errors(kw, code):
+    assert call2(**kw) == code
+
+
+def test_bad_algo():
+    st = L.libconv_forward_algo(X, Wp, B, Y, 1, 4, 1, 8, 8, 8, 1, 3, 3, 0, 1, 1, 1, 1, 1,
+                                L.F32, 0, 3, None)
+    assert st == 9
+
+
+def test_null_bias_is_allowed_and_empty_batch_is_a_no_op():
+    # N = 0 returns OK without touching the device (works with no GPU)
+    assert call2(b=None, N=0) == 0
+
+
+def test_no_device_is_reported():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert call2() == 7
+    assert L.libconv_device_supported(0) == 7
+
+
+def test_query_algo_validation():
+    st, *_ = L.libconv_query_algo(1, 4, 1, 8, 8, 8, 1, 3, 3, 0, 1, 1, 1, 1, 1, 5, 0, 0)
+    assert st == 3
+
+
+EXPECTED_ALGO = {  # the dispatcher's choice per workload layer
+    "c1": L.ALGO_DIRECT, "c2_L1": L.ALGO_DIRECT, "c2_L2": L.ALGO_IGEMM,
+    "c2_L3": L.ALGO_DIRECT, "c2_L4": L.ALGO_IGEMM, "c3_A": L.ALGO_IGEMM,
+    "c3_B": L.ALGO_IGEMM, "c4_A": L.ALGO_IGEMM, "c4_B": L.ALGO_IGEMM,
+    "c5_A": L.ALGO_IGEMM, "c5_B": L.ALGO_IGEMM,
+}
+
+
+@pytest.mark.parametrize("name", sorted(W.ALL_LAYERS))
+def test_dispatch_choice(name):
+    l = W.ALL_LAYERS[name]
+    st, algo, tile, grid = L.libconv_query_algo(
+        l.N, l.C_in, l.T, l.H, l.W, l.C_out, l.KT, l.KH, l.KW, *l.pad, *l.stride,
+        W.DTYPE_CODE[l.dtype], W.ACT_CODE[l.act], L.ALGO_AUTO)
+    assert st == 0
+    assert algo == EXPECTED_ALGO[name]
+    assert L.libconv_tile_name(tile) != "?"
+    assert grid >= 1
+
+
+def test_forced_algorithms():
+    # 3x3 stride-1 fp32 with C_in = 32: both families can run it
+    args = (1, 32, 1, 20, 20, 32, 1, 3, 3, 0, 1, 1, 1, 1, 1, L.F32, 0)
+    assert L.libconv_query_algo(*args, L.ALGO_DIRECT)[1] == L.ALGO_DIRECT
+    assert L.libconv_query_algo(*args, L.ALGO_IGEMM)[1] == L.ALGO_IGEMM
+    # 5x5: the MFMA family has no tile -> UNSUPPORTED when forced, direct otherwise
+    args5 = (1, 32, 1, 20, 20, 32, 1, 5, 5, 0, 2, 2, 1, 1, 1, L.F16, 0)
+    assert L.libconv_query_algo(*args5, L.ALGO_IGEMM)[0] == 6
+    assert L.libconv_query_algo(*args5, L.ALGO_AUTO)[1] == L.ALGO_DIRECT
+    # fp16 with C_in not a multiple of 8: direct
+    args7 = (1, 12, 1, 20, 20, 32, 1, 3, 3, 0, 1, 1, 1, 1, 1, L.F16, 0)
+    assert L.libconv_query_algo(*args7, L.ALGO_AUTO)[1] == L.ALGO_DIRECT
