@@ -39,11 +39,15 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// One MFMA k-step over a pair of 16-byte slots.  KSUB is the number of
+// instructions a slot pair takes; step(.., k) issues sub-step k.
 template <int DT> struct Mma;
 
 template <> struct Mma<DT_F16> {
   static constexpr int SE = 8;  // elements per 16-byte slot
-  __device__ static __forceinline__ void step(const u32x4_t& a, const u32x4_t& b, float16_t& c) {
+  static constexpr int KSUB = 1;
+  __device__ static __forceinline__ void step(const u32x4_t& a, const u32x4_t& b, float16_t& c,
+                                              int) {
     c = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, a),
                                                __builtin_bit_cast(half8_t, b), c, 0, 0, 0);
   }
@@ -51,19 +55,26 @@ template <> struct Mma<DT_F16> {
 
 template <> struct Mma<DT_BF16> {
   static constexpr int SE = 8;
-  __device__ static __forceinline__ void step(const u32x4_t& a, const u32x4_t& b, float16_t& c) {
+  static constexpr int KSUB = 1;
+  __device__ static __forceinline__ void step(const u32x4_t& a, const u32x4_t& b, float16_t& c,
+                                              int) {
     c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
   }
 };
 
+// fp32: 32x32x2, lanes 0-31 give K index 0 (slot 2p), lanes 32-63 K index 1
+// (slot 2p+1); sub-step k multiplies element k of both slots.  The fragment
+// is reinterpreted as a whole float4 before indexing: bit-casting a single
+// vector element has been seen to compile to element 0 for every k.
 template <> struct Mma<DT_F32> {
   static constexpr int SE = 4;
-  __device__ static __forceinline__ void step(const u32x4_t& a, const u32x4_t& b, float16_t& c) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      c = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(float, a[k]),
-                                               __builtin_bit_cast(float, b[k]), c, 0, 0, 0);
+  static constexpr int KSUB = 4;
+  __device__ static __forceinline__ void step(const u32x4_t& a, const u32x4_t& b, float16_t& c,
+                                              int k) {
+    const float4_t af = __builtin_bit_cast(float4_t, a);
+    const float4_t bf = __builtin_bit_cast(float4_t, b);
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(af[k], bf[k], c, 0, 0, 0);
   }
 };
 
@@ -315,9 +326,12 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
     for (int p = 0; p < G::NPAIR; ++p) {
       if (p + 1 < G::NPAIR) load_frags(p + 1, (p + 1) & 1);
 #pragma unroll
-      for (int i = 0; i < G::FA; ++i)
+      for (int k = 0; k < Mma<G::DT>::KSUB; ++k)
 #pragma unroll
-        for (int j = 0; j < G::FB; ++j) Mma<G::DT>::step(fa[p & 1][i], fb[p & 1][j], acc[i][j]);
+        for (int i = 0; i < G::FA; ++i)
+#pragma unroll
+          for (int j = 0; j < G::FB; ++j)
+            Mma<G::DT>::step(fa[p & 1][i], fb[p & 1][j], acc[i][j], k);
     }
   };
 
