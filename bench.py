@@ -125,6 +125,9 @@ def main():
     ap.add_argument("--workload", default="ocr_stack", choices=sorted(W.WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the workload, copy MIB MiB device-to-device --steps times "
+                         "(a plain copy of known size, to scale HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -141,6 +144,21 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4,
+                          "copies": args.steps,
+                          "GBps_read_plus_write": round(2 * n * 4 * args.steps / el / 1e9, 1)}))
+        return
 
     _, layers = W.WORKLOADS[args.workload]
     # Inputs: the workload's seeded tensors; the stack is chained, so only the
