@@ -28,7 +28,7 @@ ALGO_AUTO, ALGO_DIRECT, ALGO_IGEMM = 0, 1, 2
 STATUS = {
     0: "OK", 1: "ERR_NULL_POINTER", 2: "ERR_BAD_SHAPE", 3: "ERR_BAD_DTYPE",
     4: "ERR_BAD_ACTIVATION", 5: "ERR_ALIAS", 6: "ERR_UNSUPPORTED", 7: "ERR_NO_DEVICE",
-    8: "ERR_LAUNCH", 9: "ERR_BAD_ALGO", 10: "ERR_TOO_LARGE",
+    8: "ERR_LAUNCH", 9: "ERR_BAD_ALGO", 10: "ERR_TOO_LARGE", 11: "ERR_OUT_OF_MEMORY",
 }
 _ALGOS = {"auto": ALGO_AUTO, "direct": ALGO_DIRECT, "igemm": ALGO_IGEMM}
 _ACTS = {"none": ACT_NONE, "relu": ACT_RELU}
@@ -72,6 +72,12 @@ def load() -> ctypes.CDLL:
     lib.libconv_device_supported.restype = I
     lib.libconv_version.argtypes = []
     lib.libconv_version.restype = I
+    lib.libconv_packed_weight_bytes.argtypes = [I] * 6
+    lib.libconv_packed_weight_bytes.restype = LL
+    lib.libconv_pack_weights.argtypes = [P, P, LL] + [I] * 6 + [P]
+    lib.libconv_pack_weights.restype = I
+    lib.libconv_forward_packed.argtypes = [P, P, P, P] + [I] * 17 + [P]
+    lib.libconv_forward_packed.restype = I
     _lib = lib
     return lib
 
@@ -81,7 +87,8 @@ def header_functions() -> list:
     with open(HEADER_PATH) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return re.findall(r"^\s*(?:libconv_status|int|const char\*)\s+(\w+)\s*\(", text, flags=re.M)
+    return re.findall(r"^\s*(?:libconv_status|int|long long|const char\*)\s+(\w+)\s*\(", text,
+                      flags=re.M)
 
 
 # ------------------------------------------------------------ raw entry points
@@ -103,6 +110,22 @@ def libconv_forward_algo(x, w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW, pad
     return load().libconv_forward_algo(x, w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW,
                                        pad_t, pad_h, pad_w, stride_t, stride_h, stride_w,
                                        dtype, act, algo, stream)
+
+
+def libconv_packed_weight_bytes(C_in, C_out, KT, KH, KW, dtype) -> int:
+    return load().libconv_packed_weight_bytes(C_in, C_out, KT, KH, KW, dtype)
+
+
+def libconv_pack_weights(w, packed, packed_bytes, C_in, C_out, KT, KH, KW, dtype, stream) -> int:
+    return load().libconv_pack_weights(w, packed, packed_bytes, C_in, C_out, KT, KH, KW, dtype,
+                                       stream)
+
+
+def libconv_forward_packed(x, packed_w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW, pad_t,
+                           pad_h, pad_w, stride_t, stride_h, stride_w, dtype, act, stream) -> int:
+    return load().libconv_forward_packed(x, packed_w, bias, y, N, C_in, T, H, W, C_out, KT, KH,
+                                         KW, pad_t, pad_h, pad_w, stride_t, stride_h, stride_w,
+                                         dtype, act, stream)
 
 
 def libconv_query_algo(N, C_in, T, H, W, C_out, KT, KH, KW, pad_t, pad_h, pad_w,
@@ -204,6 +227,75 @@ def conv_nd(x, w, b=None, stride: Union[int, Sequence[int]] = 1,
                                    stream)
     if st_ != 0:
         raise LibconvError(st_, "libconv_forward_algo")
+    return y
+
+
+class PackedWeights:
+    """Weights in the packed layout, with the shape they were packed from."""
+
+    def __init__(self, data, w_shape, dtype):
+        self.data = data          # uint8 device tensor
+        self.w_shape = tuple(w_shape)
+        self.dtype = dtype
+
+
+def pack_weights(w, stream=None) -> PackedWeights:
+    """Pack OIHW / OIDHW weights (device tensor) for libconv_forward_packed."""
+    import torch
+    if not w.is_cuda or not w.is_contiguous():
+        raise ValueError("w must be a contiguous device tensor")
+    K, C = w.shape[:2]
+    ks = tuple(w.shape[2:])
+    KT, KH, KW = (1,) + ks if len(ks) == 2 else ks
+    dt = _dtype_code(w)
+    nbytes = load().libconv_packed_weight_bytes(C, K, KT, KH, KW, dt)
+    if nbytes < 0:
+        raise LibconvError(6, "libconv_packed_weight_bytes")
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=w.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(w.device).cuda_stream
+    st = load().libconv_pack_weights(w.data_ptr(), buf.data_ptr(), nbytes, C, K, KT, KH, KW, dt,
+                                     stream)
+    if st != 0:
+        raise LibconvError(st, "libconv_pack_weights")
+    return PackedWeights(buf, w.shape, w.dtype)
+
+
+def conv_nd_packed(x, pw: PackedWeights, b=None, stride=1, padding=0, act="none", out=None,
+                   stream=None):
+    """Convolution with weights packed by pack_weights (never allocates in libconv)."""
+    import torch
+    nd = x.dim() - 2
+    if pw.dtype != x.dtype or len(pw.w_shape) != x.dim():
+        raise ValueError("packed weights do not match x")
+    s = _triple(stride, nd)
+    p = _triple(padding, nd)
+    if nd == 2:
+        N, C, H, W = x.shape
+        T, KT, st, pt = 1, 1, 1, 0
+        K, _, KH, KW = pw.w_shape
+        sh, sw = s
+        ph, pw_ = p
+    else:
+        N, C, T, H, W = x.shape
+        K, _, KT, KH, KW = pw.w_shape
+        st, sh, sw = s
+        pt, ph, pw_ = p
+    lib = load()
+    ot = lib.libconv_out_size(T, KT, pt, st)
+    oh = lib.libconv_out_size(H, KH, ph, sh)
+    ow = lib.libconv_out_size(W, KW, pw_, sw)
+    if min(ot, oh, ow) < 1:
+        raise LibconvError(2, "conv")
+    shape = (N, K, oh, ow) if nd == 2 else (N, K, ot, oh, ow)
+    y = torch.empty(shape, dtype=x.dtype, device=x.device) if out is None else out
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    st_ = lib.libconv_forward_packed(x.data_ptr(), pw.data.data_ptr(), _ptr(b), y.data_ptr(), N, C,
+                                     T, H, W, K, KT, KH, KW, pt, ph, pw_, st, sh, sw,
+                                     _dtype_code(x), _ACTS[act], stream)
+    if st_ != 0:
+        raise LibconvError(st_, "libconv_forward_packed")
     return y
 
 

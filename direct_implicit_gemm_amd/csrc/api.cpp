@@ -75,10 +75,12 @@ libconv_status validate(Problem& p, int algo, bool with_pointers) {
   const long long wb = product({p.K, p.C, p.KT, p.KH, p.KW, eb});
   const long long yb = product({p.N, p.K, ot, oh, ow, eb});
   if (xb > kMaxBytes || wb > kMaxBytes || yb > kMaxBytes) return LIBCONV_ERR_TOO_LARGE;
+  const long long pb = packed_weight_bytes(p.C, p.K, p.KT, p.KH, p.KW, p.dtype);
+  if (pb > kMaxBytes) return LIBCONV_ERR_TOO_LARGE;
   if (with_pointers) {
-    if (!p.x || !p.w || !p.y) return LIBCONV_ERR_NULL_POINTER;
+    if (!p.x || !(p.w || p.wp) || !p.y) return LIBCONV_ERR_NULL_POINTER;
     if (yb > 0 && (overlaps(p.y, yb, p.x, xb) || overlaps(p.y, yb, p.w, wb) ||
-                   overlaps(p.y, yb, p.b, (long long)p.K * eb)))
+                   overlaps(p.y, yb, p.wp, pb) || overlaps(p.y, yb, p.b, (long long)p.K * eb)))
       return LIBCONV_ERR_ALIAS;
   }
   return LIBCONV_OK;
@@ -115,8 +117,22 @@ bool device_ok(int d) {
 // GEMM on the matrix cores.
 constexpr long long kMinMfmaReduction = 64;
 
-libconv_status plan_for(const Problem& p, int algo, Plan* plan) {
+libconv_status plan_for(const Problem& p, int algo, Plan* plan, bool packed_only = false) {
   const long long red = (long long)p.C * p.KT * p.KH * p.KW;
+  // Evidence hook: LIBCONV_FORCE_TILE=<id> runs that MFMA tile when it fits
+  // the shape (tile ids: libconv_tile_name); ignored otherwise.
+  if (const char* ft = std::getenv("LIBCONV_FORCE_TILE")) {
+    Plan forced;
+    if (igemm_plan_tile(p, std::atoi(ft), &forced) && algo != LIBCONV_ALGO_DIRECT &&
+        (!packed_only || igemm_tile_packed(forced.tile))) {
+      *plan = forced;
+      return LIBCONV_OK;
+    }
+  }
+  if (packed_only) {  // only packed weights exist: MFMA tiles that read them
+    if (algo == LIBCONV_ALGO_DIRECT || !igemm_plan_packed(p, plan)) return LIBCONV_ERR_UNSUPPORTED;
+    return LIBCONV_OK;
+  }
   Plan ig, dr;
   const bool has_ig = igemm_plan(p, &ig);
   const bool has_dr = direct_plan(p, &dr);
@@ -155,7 +171,7 @@ libconv_status run(Problem& p, int algo) {
     return LIBCONV_ERR_NO_DEVICE;
   }
   Plan plan;
-  st = plan_for(p, algo, &plan);
+  st = plan_for(p, algo, &plan, p.w == nullptr);
   if (st != LIBCONV_OK) return st;
   if (std::getenv("LIBCONV_LOG")) {
     const char* name = plan.algo == LIBCONV_ALGO_DIRECT ? direct_tile_name(plan.tile)
@@ -163,7 +179,24 @@ libconv_status run(Problem& p, int algo) {
     std::fprintf(stderr, "libconv: %s grid=%lld (N=%d C=%d T=%d H=%d W=%d K=%d k=%dx%dx%d)\n",
                  name ? name : "?", plan.grid, p.N, p.C, p.T, p.H, p.W, p.K, p.KT, p.KH, p.KW);
   }
-  return plan.algo == LIBCONV_ALGO_DIRECT ? direct_launch(p, plan) : igemm_launch(p, plan);
+  if (plan.algo == LIBCONV_ALGO_DIRECT) return direct_launch(p, plan);
+  if (!igemm_tile_packed(plan.tile) || p.wp) return igemm_launch(p, plan);
+  // The tile reads packed weights but the caller passed OIHW weights: pack
+  // them into a stream-ordered temporary on the call's stream (no device-wide
+  // synchronisation; recordable in a HIP graph), run, and release it.
+  const long long pb = packed_weight_bytes(p.C, p.K, p.KT, p.KH, p.KW, p.dtype);
+  void* tmp = nullptr;
+  if (hipMallocAsync(&tmp, (size_t)pb, p.stream) != hipSuccess || !tmp) {
+    (void)hipGetLastError();
+    return LIBCONV_ERR_OUT_OF_MEMORY;
+  }
+  st = pack_launch(p.w, tmp, p.C, p.K, p.KT, p.KH, p.KW, p.dtype, p.stream);
+  if (st == LIBCONV_OK) {
+    p.wp = tmp;
+    st = igemm_launch(p, plan);
+  }
+  if (hipFreeAsync(tmp, p.stream) != hipSuccess && st == LIBCONV_OK) st = LIBCONV_ERR_LAUNCH;
+  return st;
 }
 
 Problem make_problem(const void* x, const void* w, const void* bias, void* y, int N, int C_in,
@@ -217,6 +250,47 @@ libconv_status libconv_forward_algo(const void* x, const void* w, const void* bi
   return run(p, algo);
 }
 
+long long libconv_packed_weight_bytes(int C_in, int C_out, int KT, int KH, int KW, int dtype) {
+  if (C_in < 1 || C_out < 1 || KT < 1 || KH < 1 || KW < 1) return -1;
+  if (dtype != LIBCONV_F32 && dtype != LIBCONV_F16 && dtype != LIBCONV_BF16) return -1;
+  if (!pack_supported(KT, KH, KW, dtype)) return -1;
+  const long long b = packed_weight_bytes(C_in, C_out, KT, KH, KW, dtype);
+  return b > 0x7fffffffLL ? -1 : b;
+}
+
+libconv_status libconv_pack_weights(const void* w, void* packed, long long packed_bytes, int C_in,
+                                    int C_out, int KT, int KH, int KW, int dtype, void* stream) {
+  if (dtype != LIBCONV_F32 && dtype != LIBCONV_F16 && dtype != LIBCONV_BF16)
+    return LIBCONV_ERR_BAD_DTYPE;
+  if (C_in < 1 || C_out < 1 || KT < 1 || KH < 1 || KW < 1) return LIBCONV_ERR_BAD_SHAPE;
+  if (!w || !packed) return LIBCONV_ERR_NULL_POINTER;
+  if (!pack_supported(KT, KH, KW, dtype)) return LIBCONV_ERR_UNSUPPORTED;
+  const long long need = packed_weight_bytes(C_in, C_out, KT, KH, KW, dtype);
+  const long long wb = (long long)C_out * C_in * KT * KH * KW * dtype_bytes(dtype);
+  if (need > 0x7fffffffLL || wb > 0x7fffffffLL) return LIBCONV_ERR_TOO_LARGE;
+  if (packed_bytes < need) return LIBCONV_ERR_BAD_SHAPE;
+  if (overlaps(packed, need, w, wb)) return LIBCONV_ERR_ALIAS;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || !device_ok(dev)) {
+    (void)hipGetLastError();
+    return LIBCONV_ERR_NO_DEVICE;
+  }
+  return pack_launch(w, packed, C_in, C_out, KT, KH, KW, dtype,
+                     reinterpret_cast<hipStream_t>(stream));
+}
+
+libconv_status libconv_forward_packed(const void* x, const void* packed_w, const void* bias,
+                                      void* y, int N, int C_in, int T, int H, int W, int C_out,
+                                      int KT, int KH, int KW, int pad_t, int pad_h, int pad_w,
+                                      int stride_t, int stride_h, int stride_w, int dtype,
+                                      int act, void* stream) {
+  Problem p = make_problem(x, nullptr, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW, pad_t, pad_h,
+                           pad_w, stride_t, stride_h, stride_w, dtype, act, stream);
+  p.wp = packed_w;
+  if (!packed_w && x && y) return LIBCONV_ERR_NULL_POINTER;
+  return run(p, LIBCONV_ALGO_IGEMM);
+}
+
 libconv_status libconv_query_algo(int N, int C_in, int T, int H, int W, int C_out, int KT, int KH,
                                   int KW, int pad_t, int pad_h, int pad_w, int stride_t,
                                   int stride_h, int stride_w, int dtype, int act, int algo,
@@ -259,6 +333,7 @@ const char* libconv_status_string(int status) {
     case LIBCONV_ERR_LAUNCH: return "kernel launch failed";
     case LIBCONV_ERR_BAD_ALGO: return "bad algorithm";
     case LIBCONV_ERR_TOO_LARGE: return "tensor too large";
+    case LIBCONV_ERR_OUT_OF_MEMORY: return "out of device memory for packed weights";
     default: return "unknown status";
   }
 }

@@ -15,8 +15,16 @@
 //
 // K loop: stages of CK = CG * SE input channels (SE = 8 for 16-bit types,
 // 4 for fp32: one 16-byte "slot"), all taps at once.  Per stage:
-//   * weights  W[co][ci][taps] (contiguous per co) are read with 16-byte
-//     loads and transposed into LDS as Wl[slot][co][SE], slot = tap*CG + g;
+//   * weights land in LDS as Wl[slot][co][SE], slot = tap*CG + g (the SE
+//     channels of group g at one tap, for each output channel).  Two ways:
+//       - from OIHW weights: each thread reads one channel's TS contiguous
+//         16-byte vectors and transposes them in registers (16-byte LDS
+//         stores, lanes on consecutive channels);
+//       - from packed weights ([C/SE][taps][C_out padded][SE], made by the
+//         pack kernel below -- the per-layer weight packing of the
+//         Convolution3D work in "SeedVR2 NCNN Vulkan", section 3.2): a stage
+//         is NSLOT contiguous runs that are copied straight into LDS with
+//         direct-to-LDS loads (no registers, no arithmetic);
 //   * the input halo (KT frames x HR rows x HC cols) is read row-contiguously
 //     and written channel-innermost as Xl[g][kt][hr][hc][SE]; taps outside
 //     the input are zero (this is the padding);
@@ -38,6 +46,7 @@ namespace libconv {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kPackAlign = 128;  // output channels of packed weights are padded to this
 
 // One MFMA k-step over a pair of 16-byte slots.  KSUB is the number of
 // instructions a slot pair takes; step(.., k) issues sub-step k.
@@ -80,7 +89,7 @@ template <> struct Mma<DT_F32> {
 
 struct IgemmArgs {
   const void* x;
-  const void* w;
+  const void* w;      // OIHW weights, or packed weights when the tile is packed
   const void* b;
   void* y;
   int N, C, T, H, W, K;
@@ -89,15 +98,17 @@ struct IgemmArgs {
   int st;             // time stride (the spatial strides are template parameters)
   int relu;
   int stages;         // ceil(C / CK)
+  int kp;             // packed weights: output-channel stride (C_out rounded up)
   int co_tiles, row_tiles, col_tiles;
   uint32_t x_bytes, w_bytes, b_bytes, y_bytes;
 };
 
 template <int DT_, int KT_, int KH_, int KW_, int SH_, int SW_, int BM_, int TH_, int TW_,
-          int WM_, int WN_, int CG_>
+          int WM_, int WN_, int CG_, int PK_>
 struct Cfg {
   static constexpr int DT = DT_, KT = KT_, KH = KH_, KW = KW_, SH = SH_, SW = SW_;
   static constexpr int BM = BM_, TH = TH_, TW = TW_, WM = WM_, WN = WN_, CG = CG_;
+  static constexpr bool PK = PK_ != 0;
   static constexpr int EB = Elem<DT>::bytes;
   static constexpr int SE = Mma<DT>::SE;
   static constexpr int CK = CG * SE;
@@ -115,10 +126,13 @@ struct Cfg {
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int FA = WTM / 32, FB = WTN / 32;
   static constexpr int BPR = TW / 32;              // 32-pixel blocks per tile row
-  // weight staging: QN 16-byte vectors per output channel per stage
-  static constexpr int QN = CG * TS;
-  static constexpr int WROWS = kThreads / QN;      // channels loaded per pass
-  static constexpr int WPASS = (BM + WROWS - 1) / WROWS;
+  // weight staging from OIHW: one unit = one output channel x one group of
+  // SE input channels = TS contiguous 16-byte vectors; unit u = g * BM + channel
+  static constexpr int WUNITS = PK ? 0 : BM * CG;
+  static constexpr int WPASS = PK ? 0 : (WUNITS + kThreads - 1) / kThreads;
+  // weight staging from packed weights: NSLOT runs of BM 16-byte vectors,
+  // moved as 1 KB chunks (one wave, one instruction each)
+  static constexpr int WCHUNKS = NSLOT * BM / 64;
   // input staging: one unit = one halo pixel of one channel group
   static constexpr int XUNITS = CG * XPLANE;
   static constexpr int XPASS = (XUNITS + kThreads - 1) / kThreads;
@@ -126,16 +140,55 @@ struct Cfg {
   static_assert(WM * WN == 4, "four waves");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
   static_assert(TW % 32 == 0, "tile rows are whole 32-pixel blocks");
-  static_assert(QN <= kThreads, "weight stage too wide");
+  static_assert(BM % 64 == 0 || !PK, "packed tiles move whole 64-channel chunks");
+  static_assert(BM <= kPackAlign, "packed channel padding covers one tile");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-// Global -> registers for one stage.
+// Global -> registers for one stage (weights only when they are transposed
+// here; packed weights go straight to LDS).
 template <class G>
 struct StageRegs {
-  u32x4_t wv[G::WPASS];
+  u32x4_t wv[G::WPASS > 0 ? G::WPASS : 1][G::TS];
   u32x4_t xv[G::XPASS];
 };
+
+// Slot vector of tap t from a unit's TS vectors: the unit holds
+// w[co][c0 .. c0+SE)[0 .. TS) with the tap index fastest; the slot wants the
+// SE channels of one tap.  All indices are compile-time, so this is register
+// selection (fp32) or one byte permute per output word (16-bit).
+template <int SE, int TS, int t>
+__device__ __forceinline__ u32x4_t transpose_slot(const u32x4_t (&v)[TS]) {
+  u32x4_t o;
+  if constexpr (SE == 4) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int e = m * TS + t;
+      o[m] = v[e / 4][e % 4];
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int e0 = (2 * m) * TS + t, e1 = (2 * m + 1) * TS + t;
+      const uint32_t d0 = v[e0 / 8][(e0 % 8) / 2];
+      const uint32_t d1 = v[e1 / 8][(e1 % 8) / 2];
+      const uint32_t lo = (e0 & 1) ? (d0 >> 16) : (d0 & 0xffffu);
+      const uint32_t hi = (e1 & 1) ? (d1 & 0xffff0000u) : (d1 << 16);
+      o[m] = lo | hi;
+    }
+  }
+  return o;
+}
+
+// LDS stores of the TS slot vectors of one unit (t = 0 .. TS-1).
+template <int SE, int TS, int t>
+__device__ __forceinline__ void store_slots(unsigned char* base, int slot_stride,
+                                            const u32x4_t (&v)[TS]) {
+  if constexpr (t < TS) {
+    *reinterpret_cast<u32x4_t*>(base + t * slot_stride) = transpose_slot<SE, TS, t>(v);
+    store_slots<SE, TS, t + 1>(base, slot_stride, v);
+  }
+}
 
 template <class G>
 __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
@@ -175,34 +228,43 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.w, a.w_bytes);
   constexpr int kOob = 0x7ffffff0;  // byte offset beyond any tensor: reads 0
 
-  // ---- per-thread weight staging geometry (fixed across stages)
-  const int wq = tid % G::QN;            // which 16-byte vector of a channel's block
-  const int wrow = tid / G::QN;          // first channel (within the tile) of this thread
-  const bool wactive = wrow < G::WROWS;
-  int wdst[SE];                          // LDS byte offset of element j, channel 0
-  int wci[SE];                           // channel (within the stage) of element j
-#pragma unroll
-  for (int j = 0; j < SE; ++j) {
-    const int e = wq * SE + j;           // element within the [CK][TS] block
-    const int ci = e / G::TS;
-    const int tap = e - ci * G::TS;
-    const int slot = tap * G::CG + ci / SE;
-    wdst[j] = slot * G::BM * 16 + (ci % SE) * EB;
-    wci[j] = ci;
-  }
   const int cstride = a.C * G::TS;       // elements between output channels in w
   const int plane = a.T * a.H * a.W;     // elements between input channels in x
 
+  // Packed weights of stage s straight into LDS buffer `buf`: chunk c covers
+  // 64 channels of one slot; a wave moves one chunk per instruction, lane l
+  // landing at chunk base + 16 l.
+  auto dma_weights = [&](int s, unsigned char* buf) {
+    if constexpr (G::PK) {
+      for (int c = wave; c < G::WCHUNKS; c += kThreads / 64) {
+        const int slot = c / (G::BM / 64), part = c % (G::BM / 64);
+        const int t = slot / G::CG, g = slot % G::CG;
+        const int gabs = s * G::CG + g;
+        const int src = ((gabs * G::TS + t) * a.kp + co0 + part * 64 + lane) * 16;
+        unsigned char* dst = buf + (slot * G::BM + part * 64) * 16;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            wr, (__attribute__((address_space(3))) void*)dst, 16, src, 0, 0, 0);
+      }
+    }
+  };
+
   auto load_stage = [&](int s, StageRegs<G>& r) {
     const int ci0 = s * G::CK;
-    // weights: vector wq of channels co0 + wrow + pass * WROWS
+    // weights from OIHW: unit u = g * BM + col -> TS vectors of
+    // w[co0 + col][ci0 + g*SE ..][..] (C is a multiple of SE, so a group is
+    // wholly inside or outside C)
 #pragma unroll
     for (int i = 0; i < G::WPASS; ++i) {
-      const int col = wrow + i * G::WROWS;
+      const int u = tid + i * kThreads;
+      const int g = u / G::BM, col = u % G::BM;
       const int co = co0 + col;
-      int off = kOob;
-      if (wactive && col < G::BM && co < a.K) off = (co * cstride + ci0 * G::TS + wq * SE) * EB;
-      r.wv[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wr, off, 0, 0));
+      const int cg = ci0 + g * SE;
+      const bool ok = u < G::WUNITS && co < a.K && cg < a.C;
+      const int base = (co * cstride + cg * G::TS) * EB;
+#pragma unroll
+      for (int k = 0; k < G::TS; ++k)
+        r.wv[i][k] = __builtin_bit_cast(
+            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wr, ok ? base + k * 16 : kOob, 0, 0));
     }
     // input halo: unit u = ((g * KT + kt) * HR + hr) * HC + hc
 #pragma unroll
@@ -216,16 +278,14 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
       const int kt = v % G::KT;
       const int g = v / G::KT;
       const int ih = ih0 + hr, iw = iw0 + hc, it = it0 + kt;
+      const int cbase = ci0 + g * SE;
       const bool ok = u < G::XUNITS && (unsigned)ih < (unsigned)a.H &&
                       (unsigned)iw < (unsigned)a.W && (unsigned)it < (unsigned)a.T;
-      const int cbase = ci0 + g * SE;
       const int base = (((n * a.C + cbase) * a.T + it) * a.H + ih) * a.W + iw;
       uint32_t e[SE];
 #pragma unroll
-      for (int j = 0; j < SE; ++j) {
-        const int off = (ok && cbase + j < a.C) ? (base + j * plane) * EB : kOob;
-        e[j] = E::load_bits(xr, off);
-      }
+      for (int j = 0; j < SE; ++j)
+        e[j] = E::load_bits(xr, (ok && cbase + j < a.C) ? (base + j * plane) * EB : kOob);
       if constexpr (SE == 8) {
         r.xv[i] = u32x4_t{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
                           e[6] | (e[7] << 16)};
@@ -235,26 +295,16 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
     }
   };
 
-  auto store_stage = [&](int s, const StageRegs<G>& r, unsigned char* buf) {
-    const int ci0 = s * G::CK;
-    // weights: transpose [ci][tap] -> [slot][co][ci % SE]
+  auto store_stage = [&](const StageRegs<G>& r, unsigned char* buf) {
+    // weights from OIHW: [ci][tap] per unit -> Wl[slot = tap * CG + g][co][SE];
+    // lanes of a wave hold consecutive channels, so each 16-byte store is
+    // conflict-free
 #pragma unroll
     for (int i = 0; i < G::WPASS; ++i) {
-      const int col = wrow + i * G::WROWS;
-      if (wactive && col < G::BM) {
-#pragma unroll
-        for (int j = 0; j < SE; ++j) {
-          const bool cok = ci0 + wci[j] < a.C;
-          unsigned char* dst = buf + wdst[j] + col * 16;
-          if constexpr (SE == 8) {
-            const uint32_t word = r.wv[i][j >> 1];
-            const uint16_t h = (uint16_t)((j & 1) ? (word >> 16) : (word & 0xffffu));
-            *reinterpret_cast<uint16_t*>(dst) = cok ? h : (uint16_t)0;
-          } else {
-            *reinterpret_cast<uint32_t*>(dst) = cok ? r.wv[i][j] : 0u;
-          }
-        }
-      }
+      const int u = tid + i * kThreads;
+      if (u < G::WUNITS)
+        store_slots<SE, G::TS, 0>(buf + ((u / G::BM) * G::BM + u % G::BM) * 16,
+                                  G::CG * G::BM * 16, r.wv[i]);
     }
     // input halo
     unsigned char* xbuf = buf + G::WBYTES;
@@ -337,16 +387,22 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
 
   // ---- main loop: two LDS stages, next stage's global loads in flight
   StageRegs<G> regs;
+  dma_weights(0, lds);
   load_stage(0, regs);
-  store_stage(0, regs, lds);
+  store_stage(regs, lds);
+  __builtin_amdgcn_s_waitcnt(0);  // direct-to-LDS copies are counted as loads
   __syncthreads();
   for (int s = 0; s < a.stages; ++s) {
     unsigned char* cur = lds + (s & 1) * G::BUF;
     unsigned char* nxt = lds + ((s + 1) & 1) * G::BUF;
     const bool more = s + 1 < a.stages;
-    if (more) load_stage(s + 1, regs);
+    if (more) {
+      dma_weights(s + 1, nxt);
+      load_stage(s + 1, regs);
+    }
     compute(cur);
-    if (more) store_stage(s + 1, regs, nxt);
+    if (more) store_stage(regs, nxt);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
@@ -374,6 +430,71 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
   }
 }
 
+// ------------------------------------------------------------ weight packing
+// w [K][C][TS] -> wp [G = ceil(C/SE)][TS][Kp][SE] (16 bytes per entry), zero
+// for channels >= C and output channels >= K.  One thread per (output
+// channel, channel group): the group's SE*TS elements are contiguous in w;
+// when C is a multiple of SE they are TS aligned 16-byte vectors, otherwise
+// they are read element by element.  The thread transposes them in registers
+// and writes its TS slot vectors; lanes hold consecutive output channels, so
+// each store instruction of a wave writes 1 KB contiguous.
+struct PackArgs {
+  const void* w;
+  void* wp;
+  int K, C, Kp, G;
+  uint32_t w_bytes, wp_bytes;
+};
+
+template <int SE, int TS, int t>
+__device__ __forceinline__ void store_packed(__amdgpu_buffer_rsrc_t pr, int off, int tstride,
+                                             const u32x4_t (&v)[TS]) {
+  if constexpr (t < TS) {
+    __builtin_amdgcn_raw_buffer_store_b128(transpose_slot<SE, TS, t>(v), pr, off + t * tstride, 0,
+                                           0);
+    store_packed<SE, TS, t + 1>(pr, off, tstride, v);
+  }
+}
+
+template <int DT, int TS>
+__global__ __launch_bounds__(kThreads) void pack_kernel(PackArgs a) {
+  using E = Elem<DT>;
+  constexpr int SE = Mma<DT>::SE;
+  constexpr int EB = E::bytes;
+  constexpr int kOob = 0x7ffffff0;
+  const int u = blockIdx.x * kThreads + threadIdx.x;
+  if (u >= a.G * a.Kp) return;
+  const int g = u / a.Kp, co = u % a.Kp;
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.w, a.w_bytes);
+  const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.wp, a.wp_bytes);
+  const bool co_ok = co < a.K;
+  const int base = (co * a.C + g * SE) * TS;  // first element of the group block
+  u32x4_t v[TS];
+  if (a.C % SE == 0) {
+#pragma unroll
+    for (int k = 0; k < TS; ++k)
+      v[k] = __builtin_bit_cast(
+          u32x4_t,
+          __builtin_amdgcn_raw_buffer_load_b128(wr, co_ok ? base * EB + k * 16 : kOob, 0, 0));
+  } else {
+#pragma unroll
+    for (int k = 0; k < TS; ++k) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int h = 0; h < 4 / EB; ++h) {
+          const int e = k * SE + m * (4 / EB) + h;  // element of the [SE][TS] block
+          const bool ok = co_ok && g * SE + e / TS < a.C;
+          const uint32_t bits = E::load_bits(wr, ok ? (base + e) * EB : kOob);
+          word |= (EB == 2) ? ((bits & 0xffffu) << (16 * h)) : bits;
+        }
+        v[k][m] = word;
+      }
+    }
+  }
+  store_packed<SE, TS, 0>(pr, (g * TS * a.Kp + co) * 16, a.Kp * 16, v);
+}
+
 // ------------------------------------------------------------------ tiles
 using LaunchFn = hipError_t (*)(const IgemmArgs&, unsigned, hipStream_t);
 
@@ -389,6 +510,7 @@ struct TileDesc {
   int KT, KH, KW, SH, SW;
   int flat;       // 1: 1x1 stride-1 pad-0 layer viewed as one long row per plane
   int BM, TH, TW, CG;
+  int packed;     // 1: reads packed weights
   int lds;
   const char* name;
   LaunchFn fn[3];  // by libconv_dtype
@@ -397,40 +519,45 @@ struct TileDesc {
 // Launcher of a tile for one storage dtype, or null when the tile's operand
 // width does not match the dtype.
 template <int DT, int WIDE, int KT, int KH, int KW, int SH, int SW, int BM, int TH, int TW,
-          int WM, int WN, int CG>
+          int WM, int WN, int CG, int PK>
 constexpr LaunchFn launcher() {
   if constexpr ((DT == DT_F32) == (WIDE == 0))
-    return &launch_cfg<Cfg<DT, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG>>;
+    return &launch_cfg<Cfg<DT, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK>>;
   else
     return nullptr;
 }
 
-#define LIBCONV_TILE(ID, WIDE, KT, KH, KW, SH, SW, FLAT, BM, TH, TW, WM, WN, CG, NAME)     \
-  {ID, WIDE, KT, KH, KW, SH, SW, FLAT, BM, TH, TW, CG,                                      \
-   Cfg<WIDE ? DT_F16 : DT_F32, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG>::LDS, NAME,      \
-   {launcher<DT_F32, WIDE, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG>(),                   \
-    launcher<DT_F16, WIDE, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG>(),                   \
-    launcher<DT_BF16, WIDE, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG>()}}
+#define LIBCONV_TILE(ID, WIDE, KT, KH, KW, SH, SW, FLAT, BM, TH, TW, WM, WN, CG, PK, NAME) \
+  {ID, WIDE, KT, KH, KW, SH, SW, FLAT, BM, TH, TW, CG, PK,                                  \
+   Cfg<WIDE ? DT_F16 : DT_F32, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK>::LDS, NAME,  \
+   {launcher<DT_F32, WIDE, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK>(),               \
+    launcher<DT_F16, WIDE, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK>(),               \
+    launcher<DT_BF16, WIDE, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK>()}}
 
 const TileDesc kTiles[] = {
-    // 16-bit operands, 3x3 stride 1
-    LIBCONV_TILE(200, 1, 1, 3, 3, 1, 1, 0, 128, 8, 32, 2, 2, 2, "igemm16_k3s1_m128_n8x32"),
-    LIBCONV_TILE(201, 1, 1, 3, 3, 1, 1, 0, 128, 4, 32, 2, 2, 2, "igemm16_k3s1_m128_n4x32"),
-    LIBCONV_TILE(202, 1, 1, 3, 3, 1, 1, 0, 128, 2, 64, 2, 2, 2, "igemm16_k3s1_m128_n2x64"),
-    LIBCONV_TILE(203, 1, 1, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, "igemm16_k3s1_m64_n8x32"),
+    // 16-bit operands, 3x3 stride 1, weights transposed in the kernel
+    LIBCONV_TILE(200, 1, 1, 3, 3, 1, 1, 0, 128, 8, 32, 2, 2, 2, 0, "igemm16_k3s1_m128_n8x32"),
+    LIBCONV_TILE(201, 1, 1, 3, 3, 1, 1, 0, 128, 4, 32, 2, 2, 2, 0, "igemm16_k3s1_m128_n4x32"),
+    LIBCONV_TILE(202, 1, 1, 3, 3, 1, 1, 0, 128, 2, 64, 2, 2, 2, 0, "igemm16_k3s1_m128_n2x64"),
+    LIBCONV_TILE(203, 1, 1, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 0, "igemm16_k3s1_m64_n8x32"),
     // 16-bit operands, 3x3 stride 2
-    LIBCONV_TILE(210, 1, 1, 3, 3, 2, 2, 0, 64, 4, 32, 2, 2, 2, "igemm16_k3s2_m64_n4x32"),
+    LIBCONV_TILE(210, 1, 1, 3, 3, 2, 2, 0, 64, 4, 32, 2, 2, 2, 0, "igemm16_k3s2_m64_n4x32"),
     // 16-bit operands, 1x1 stride 1 pad 0 (flattened planes)
-    LIBCONV_TILE(220, 1, 1, 1, 1, 1, 1, 1, 128, 1, 256, 2, 2, 8, "igemm16_k1_m128_n256"),
-    LIBCONV_TILE(221, 1, 1, 1, 1, 1, 1, 1, 128, 1, 128, 2, 2, 8, "igemm16_k1_m128_n128"),
-    // 16-bit operands, 3x3x3 stride 1
-    LIBCONV_TILE(230, 1, 3, 3, 3, 1, 1, 0, 128, 8, 32, 2, 2, 1, "igemm16_k333s1_m128_n8x32"),
-    LIBCONV_TILE(231, 1, 3, 3, 3, 1, 1, 0, 128, 4, 32, 2, 2, 1, "igemm16_k333s1_m128_n4x32"),
+    LIBCONV_TILE(220, 1, 1, 1, 1, 1, 1, 1, 128, 1, 256, 2, 2, 8, 0, "igemm16_k1_m128_n256"),
+    LIBCONV_TILE(221, 1, 1, 1, 1, 1, 1, 1, 128, 1, 128, 2, 2, 8, 0, "igemm16_k1_m128_n128"),
     // fp32 operands
-    LIBCONV_TILE(240, 0, 1, 3, 3, 1, 1, 0, 32, 8, 32, 1, 4, 4, "igemm32_k3s1_m32_n8x32"),
-    LIBCONV_TILE(241, 0, 1, 3, 3, 1, 1, 0, 64, 4, 32, 2, 2, 4, "igemm32_k3s1_m64_n4x32"),
-    LIBCONV_TILE(242, 0, 1, 3, 3, 2, 2, 0, 64, 2, 32, 2, 2, 4, "igemm32_k3s2_m64_n2x32"),
-    LIBCONV_TILE(243, 0, 1, 1, 1, 1, 1, 1, 64, 1, 128, 2, 2, 8, "igemm32_k1_m64_n128"),
+    LIBCONV_TILE(240, 0, 1, 3, 3, 1, 1, 0, 32, 8, 32, 1, 4, 4, 0, "igemm32_k3s1_m32_n8x32"),
+    LIBCONV_TILE(241, 0, 1, 3, 3, 1, 1, 0, 64, 4, 32, 2, 2, 4, 0, "igemm32_k3s1_m64_n4x32"),
+    LIBCONV_TILE(242, 0, 1, 3, 3, 2, 2, 0, 64, 2, 32, 2, 2, 4, 0, "igemm32_k3s2_m64_n2x32"),
+    LIBCONV_TILE(243, 0, 1, 1, 1, 1, 1, 1, 64, 1, 128, 2, 2, 8, 0, "igemm32_k1_m64_n128"),
+    // packed weights: 16-bit, 3x3x3 stride 1
+    LIBCONV_TILE(260, 1, 3, 3, 3, 1, 1, 0, 128, 8, 32, 2, 2, 1, 1, "igemm16p_k333s1_m128_n8x32"),
+    LIBCONV_TILE(261, 1, 3, 3, 3, 1, 1, 0, 128, 4, 32, 2, 2, 1, 1, "igemm16p_k333s1_m128_n4x32"),
+    LIBCONV_TILE(262, 1, 3, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 1, 1, "igemm16p_k333s1_m64_n8x32"),
+    // packed weights: 16-bit, 3x3 stride 1
+    LIBCONV_TILE(270, 1, 1, 3, 3, 1, 1, 0, 128, 8, 32, 2, 2, 2, 1, "igemm16p_k3s1_m128_n8x32"),
+    LIBCONV_TILE(271, 1, 1, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 1, "igemm16p_k3s1_m64_n8x32"),
+    LIBCONV_TILE(272, 1, 1, 3, 3, 1, 1, 0, 128, 4, 32, 2, 2, 2, 1, "igemm16p_k3s1_m128_n4x32"),
 };
 
 #undef LIBCONV_TILE
@@ -450,7 +577,9 @@ bool tile_fits(const TileDesc& t, const Problem& p) {
   const int wide = p.dtype == LIBCONV_F32 ? 0 : 1;
   if (t.wide != wide) return false;
   const int se = wide ? 8 : 4;
-  if (p.C % se != 0) return false;  // 16-byte weight vectors must not straddle channels
+  // 16-byte weight vectors read from OIHW must not straddle channels; packed
+  // weights are zero-padded to whole groups instead.
+  if (!t.packed && p.C % se != 0) return false;
   if (t.flat) return is_flat(p);
   return p.KT == t.KT && p.KH == t.KH && p.KW == t.KW && p.sh == t.SH && p.sw == t.SW &&
          (t.KT > 1 || (p.st == 1 && p.pt == 0));
@@ -474,6 +603,29 @@ TileCounts counts(const TileDesc& t, const Problem& p) {
   return c;
 }
 
+using PackFn = hipError_t (*)(const PackArgs&, unsigned, hipStream_t);
+
+template <int DT, int TS>
+hipError_t launch_pack(const PackArgs& a, unsigned grid, hipStream_t s) {
+  hipLaunchKernelGGL((pack_kernel<DT, TS>), dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+PackFn pack_fn(int dtype, int ts) {
+  switch (dtype * 100 + ts) {
+    case LIBCONV_F32 * 100 + 1: return &launch_pack<DT_F32, 1>;
+    case LIBCONV_F32 * 100 + 9: return &launch_pack<DT_F32, 9>;
+    case LIBCONV_F32 * 100 + 27: return &launch_pack<DT_F32, 27>;
+    case LIBCONV_F16 * 100 + 1: return &launch_pack<DT_F16, 1>;
+    case LIBCONV_F16 * 100 + 9: return &launch_pack<DT_F16, 9>;
+    case LIBCONV_F16 * 100 + 27: return &launch_pack<DT_F16, 27>;
+    case LIBCONV_BF16 * 100 + 1: return &launch_pack<DT_BF16, 1>;
+    case LIBCONV_BF16 * 100 + 9: return &launch_pack<DT_BF16, 9>;
+    case LIBCONV_BF16 * 100 + 27: return &launch_pack<DT_BF16, 27>;
+    default: return nullptr;
+  }
+}
+
 }  // namespace
 
 const char* igemm_tile_name(int id) {
@@ -481,19 +633,58 @@ const char* igemm_tile_name(int id) {
   return t ? t->name : nullptr;
 }
 
-bool igemm_plan(const Problem& p, Plan* plan) {
-  // Among the tiles that fit, minimise the critical path on 256 compute
-  // units: rounds of workgroups times the (padded) work of one tile.
+bool igemm_tile_packed(int id) {
+  const TileDesc* t = find_tile(id);
+  return t && t->packed;
+}
+
+long long packed_weight_bytes(int C, int K, int KT, int KH, int KW, int dtype) {
+  const long long se = dtype == LIBCONV_F32 ? 4 : 8;
+  const long long groups = (C + se - 1) / se;
+  const long long kp = (K + kPackAlign - 1) / kPackAlign * kPackAlign;
+  return groups * KT * KH * KW * kp * 16;
+}
+
+bool pack_supported(int KT, int KH, int KW, int dtype) {
+  return pack_fn(dtype, KT * KH * KW) != nullptr;
+}
+
+libconv_status pack_launch(const void* w, void* wp, int C, int K, int KT, int KH, int KW,
+                           int dtype, hipStream_t stream) {
+  const int ts = KT * KH * KW;
+  const PackFn fn = pack_fn(dtype, ts);
+  if (!fn) return LIBCONV_ERR_UNSUPPORTED;
+  PackArgs a;
+  a.w = w;
+  a.wp = wp;
+  a.K = K;
+  a.C = C;
+  const int se = dtype == LIBCONV_F32 ? 4 : 8;
+  a.G = (C + se - 1) / se;
+  a.Kp = (K + kPackAlign - 1) / kPackAlign * kPackAlign;
+  a.w_bytes = (uint32_t)((long long)K * C * ts * dtype_bytes(dtype));
+  a.wp_bytes = (uint32_t)packed_weight_bytes(C, K, KT, KH, KW, dtype);
+  const long long units = (long long)a.G * a.Kp;
+  const hipError_t e = fn(a, (unsigned)((units + kThreads - 1) / kThreads), stream);
+  return e == hipSuccess ? LIBCONV_OK : LIBCONV_ERR_LAUNCH;
+}
+
+// Among the tiles that fit (packed or not, as asked), minimise the critical
+// path on 256 compute units: rounds of workgroups times the (padded) work of
+// one tile.
+static bool plan_among(const Problem& p, int want_packed, Plan* plan) {
   const TileDesc* best = nullptr;
   double best_cost = 0.0;
   long long best_total = 0;
   for (const auto& t : kTiles) {
-    if (!tile_fits(t, p)) continue;
+    if (want_packed >= 0 && t.packed != want_packed) continue;
+    if (!tile_fits(t, p) || !t.fn[p.dtype]) continue;
     const TileCounts c = counts(t, p);
     const double rounds = (double)((c.total + 255) / 256);
     const double cost = rounds * (double)t.BM * t.TH * t.TW;
     if (!best || cost < best_cost * 0.999 ||
-        (cost <= best_cost * 1.001 && (long long)t.BM * t.TH * t.TW > (long long)best->BM * best->TH * best->TW)) {
+        (cost <= best_cost * 1.001 &&
+         (long long)t.BM * t.TH * t.TW > (long long)best->BM * best->TH * best->TW)) {
       best = &t;
       best_cost = cost;
       best_total = c.total;
@@ -506,15 +697,35 @@ bool igemm_plan(const Problem& p, Plan* plan) {
   return true;
 }
 
+bool igemm_plan(const Problem& p, Plan* plan) {
+  // Packed-weight tiles exist only where transposing OIHW weights inside the
+  // kernel does not pay: 3-D layers, whose 27-tap weight groups are too large
+  // to transpose in registers.
+  if (p.KT > 1 && plan_among(p, 1, plan)) return true;
+  return plan_among(p, 0, plan);
+}
+
+bool igemm_plan_packed(const Problem& p, Plan* plan) { return plan_among(p, 1, plan); }
+
+bool igemm_plan_tile(const Problem& p, int tile_id, Plan* plan) {
+  const TileDesc* t = find_tile(tile_id);
+  if (!t || !tile_fits(*t, p) || !t->fn[p.dtype]) return false;
+  plan->algo = LIBCONV_ALGO_IGEMM;
+  plan->tile = t->id;
+  plan->grid = counts(*t, p).total;
+  return true;
+}
+
 libconv_status igemm_launch(const Problem& p, const Plan& plan) {
   const TileDesc* t = find_tile(plan.tile);
   if (!t || !tile_fits(*t, p)) return LIBCONV_ERR_UNSUPPORTED;
   const LaunchFn fn = t->fn[p.dtype];
   if (!fn) return LIBCONV_ERR_UNSUPPORTED;
+  if (t->packed && !p.wp) return LIBCONV_ERR_UNSUPPORTED;
   const TileCounts c = counts(*t, p);
   if (c.total > 0x7fffffffLL) return LIBCONV_ERR_UNSUPPORTED;
   IgemmArgs a;
-  a.x = p.x; a.w = p.w; a.b = p.b; a.y = p.y;
+  a.x = p.x; a.w = t->packed ? p.wp : p.w; a.b = p.b; a.y = p.y;
   a.N = p.N; a.C = p.C; a.T = p.T; a.K = p.K; a.OT = p.OT;
   if (t->flat) {  // a 1x1 layer: each plane is one row of H*W pixels
     a.H = 1; a.W = p.H * p.W; a.OH = 1; a.OW = p.OH * p.OW;
@@ -525,10 +736,12 @@ libconv_status igemm_launch(const Problem& p, const Plan& plan) {
   a.relu = p.act == LIBCONV_ACT_RELU;
   const int ck = t->CG * (t->wide ? 8 : 4);
   a.stages = (p.C + ck - 1) / ck;
+  a.kp = (p.K + kPackAlign - 1) / kPackAlign * kPackAlign;
   a.co_tiles = (int)c.co; a.row_tiles = (int)c.rows; a.col_tiles = (int)c.cols;
   const int eb = dtype_bytes(p.dtype);
   a.x_bytes = (uint32_t)((long long)p.N * p.C * p.T * p.H * p.W * eb);
-  a.w_bytes = (uint32_t)((long long)p.K * p.C * p.KT * p.KH * p.KW * eb);
+  a.w_bytes = t->packed ? (uint32_t)packed_weight_bytes(p.C, p.K, p.KT, p.KH, p.KW, p.dtype)
+                        : (uint32_t)((long long)p.K * p.C * p.KT * p.KH * p.KW * eb);
   a.b_bytes = p.b ? (uint32_t)(p.K * eb) : 0u;
   a.y_bytes = (uint32_t)((long long)p.N * p.K * p.OT * p.OH * p.OW * eb);
   const hipError_t e = fn(a, (unsigned)c.total, p.stream);

@@ -20,8 +20,9 @@ struct Problem {
   int dtype;  // libconv_dtype
   int act;    // libconv_act
   const void* x;
-  const void* w;
-  const void* b;  // may be null
+  const void* w;   // OIHW / OIDHW weights (null when only packed weights are given)
+  const void* wp;  // packed weights (libconv_pack_weights layout), or null
+  const void* b;   // may be null
   void* y;
   hipStream_t stream;
 };
@@ -42,7 +43,20 @@ libconv_status direct_launch(const Problem& p, const Plan& plan);
 // Implicit-GEMM (MFMA) family: a fixed set of geometries; returns false
 // when the shape is not one of them.
 bool igemm_plan(const Problem& p, Plan* plan);
+// Best tile among those that read packed weights.
+bool igemm_plan_packed(const Problem& p, Plan* plan);
+// A specific MFMA tile, if it fits the shape.
+bool igemm_plan_tile(const Problem& p, int tile_id, Plan* plan);
+// Whether a tile reads packed weights (p.wp) instead of OIHW weights.
+bool igemm_tile_packed(int tile_id);
 libconv_status igemm_launch(const Problem& p, const Plan& plan);
+
+// Packed weights: [ceil(C/g)][KT*KH*KW][round_up(K, 128)][g] 16-byte entries,
+// g = 8 channels (16-bit dtypes) or 4 (fp32).
+long long packed_weight_bytes(int C, int K, int KT, int KH, int KW, int dtype);
+bool pack_supported(int KT, int KH, int KW, int dtype);
+libconv_status pack_launch(const void* w, void* wp, int C, int K, int KT, int KH, int KW,
+                           int dtype, hipStream_t stream);
 
 const char* direct_tile_name(int id);
 const char* igemm_tile_name(int id);

@@ -22,14 +22,20 @@
  *   Ownership   x, w, bias and y are DEVICE pointers owned by the caller, in
  *               dense row-major layout (x NCHW / NCDHW, w OIHW / OIDHW,
  *               y NCHW / NCDHW), aligned at least to their element size.
- *               libconv keeps no pointer after the call returns, allocates
- *               nothing, copies nothing between host and device and never
- *               synchronises the host.
+ *               libconv keeps no pointer after the call returns, copies
+ *               nothing between host and device and never synchronises the
+ *               host.
+ *   Memory      libconv_forward_packed and libconv_pack_weights allocate
+ *               nothing.  conv2d_forward / conv3d_forward allocate nothing
+ *               either, except when the dispatcher runs the shape on packed
+ *               weights (3-D layers): the packed copy then lives in a
+ *               stream-ordered temporary (hipMallocAsync / hipFreeAsync on
+ *               `stream`), which needs no device-wide synchronisation.
  *   Stream      work is enqueued on `stream` (a hipStream_t; NULL means the
  *               null stream) and the call returns as soon as it is enqueued.
  *               Inputs must stay valid until the stream reaches the kernel.
- *               The call makes no allocation and no host sync, so it may be
- *               recorded into a HIP graph.
+ *               The calls make no host sync, so they may be recorded into a
+ *               HIP graph.
  *   Dtypes      x, w, bias and y share one storage dtype (libconv_dtype).
  *               Products and sums are formed in fp32 (fp16/bf16 products are
  *               exact in fp32) and y is rounded once, to nearest even.
@@ -38,8 +44,9 @@
  *               prints.  A shape no kernel supports returns
  *               LIBCONV_ERR_UNSUPPORTED; there is no silent fallback to
  *               another device or to the host.
- *   Limits      every tensor must hold fewer than 2^31 elements; all sizes
- *               must be >= 1 except N, which may be 0 (nothing is enqueued).
+ *   Limits      every tensor (and the packed weights) must span fewer than
+ *               2^31 bytes; all sizes must be >= 1 except N, which may be 0
+ *               (nothing is enqueued).
  *   Threads     calls from several host threads are safe; the only shared
  *               state is a per-device property cache filled once.
  */
@@ -80,7 +87,8 @@ typedef enum {
   LIBCONV_ERR_NO_DEVICE = 7,      /* no HIP device, or the current device is not gfx950 */
   LIBCONV_ERR_LAUNCH = 8,         /* the kernel launch failed */
   LIBCONV_ERR_BAD_ALGO = 9,       /* algo is not a libconv_algo */
-  LIBCONV_ERR_TOO_LARGE = 10      /* a tensor holds 2^31 or more elements */
+  LIBCONV_ERR_TOO_LARGE = 10,     /* a tensor (or the packed weights) spans 2^31 bytes or more */
+  LIBCONV_ERR_OUT_OF_MEMORY = 11  /* the stream-ordered temporary for packed weights failed */
 } libconv_status;
 
 /*
@@ -131,6 +139,43 @@ libconv_status libconv_forward_algo(const void* x, const void* w, const void* bi
                                     int pad_t, int pad_h, int pad_w,
                                     int stride_t, int stride_h, int stride_w,
                                     int dtype, int act, int algo, void* stream);
+
+/*
+ * Packed weights: the weights reordered once into the layout the implicit-GEMM
+ * kernels stage from, so that a call copies them into on-chip memory without
+ * rearranging them (the per-layer weight packing of the Convolution3D backend
+ * in "SeedVR2 NCNN Vulkan", section 3.2, does the same at model load).
+ * Layout: [ceil(C_in/g)][KT*KH*KW][round_up(C_out, 128)][g] entries of g
+ * consecutive input channels (16 bytes), g = 8 for 16-bit dtypes and 4 for
+ * fp32; channels beyond C_in / C_out are zero.
+ *
+ * libconv_packed_weight_bytes: size of that buffer, or -1 if the arguments are
+ * out of range, the kernel size has no packed kernels (supported: 1x1x1,
+ * 1x3x3 and 3x3x3 taps) or the buffer would span 2^31 bytes or more.
+ */
+long long libconv_packed_weight_bytes(int C_in, int C_out, int KT, int KH, int KW, int dtype);
+
+/*
+ * Pack OIHW / OIDHW weights w (device, read only) into `packed` (device,
+ * written; caller-owned, packed_bytes >= libconv_packed_weight_bytes(..)).
+ * Enqueued on `stream`; allocates nothing.  The buffers must not overlap.
+ */
+libconv_status libconv_pack_weights(const void* w, void* packed, long long packed_bytes,
+                                    int C_in, int C_out, int KT, int KH, int KW,
+                                    int dtype, void* stream);
+
+/*
+ * conv3d_forward with packed weights (from libconv_pack_weights) in place of
+ * w; always an implicit GEMM on the matrix cores, never allocates.  Returns
+ * LIBCONV_ERR_UNSUPPORTED when no packed kernel fits the shape.  A 2-D
+ * convolution is the case T = KT = 1, pad_t = 0, stride_t = 1.
+ */
+libconv_status libconv_forward_packed(const void* x, const void* packed_w, const void* bias,
+                                      void* y, int N, int C_in, int T, int H, int W,
+                                      int C_out, int KT, int KH, int KW,
+                                      int pad_t, int pad_h, int pad_w,
+                                      int stride_t, int stride_h, int stride_w,
+                                      int dtype, int act, void* stream);
 
 /*
  * Which kernel the dispatcher would launch for this shape, without launching.

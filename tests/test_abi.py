@@ -120,3 +120,44 @@ def test_forced_algorithms():
     # fp16 with C_in not a multiple of 8: direct
     args7 = (1, 12, 1, 20, 20, 32, 1, 3, 3, 0, 1, 1, 1, 1, 1, L.F16, 0)
     assert L.libconv_query_algo(*args7, L.ALGO_AUTO)[1] == L.ALGO_DIRECT
+
+
+def test_packed_weight_bytes():
+    # [ceil(C/g)][taps][round_up(K,128)][g] x 16 bytes
+    assert L.libconv_packed_weight_bytes(128, 128, 3, 3, 3, L.F16) == 16 * 27 * 128 * 16
+    assert L.libconv_packed_weight_bytes(12, 200, 1, 3, 3, L.BF16) == 2 * 9 * 256 * 16
+    assert L.libconv_packed_weight_bytes(6, 5, 1, 1, 1, L.F32) == 2 * 1 * 128 * 16
+    assert L.libconv_packed_weight_bytes(8, 8, 1, 5, 5, L.F16) == -1      # no packed kernels
+    assert L.libconv_packed_weight_bytes(0, 8, 1, 3, 3, L.F16) == -1
+    assert L.libconv_packed_weight_bytes(8, 8, 1, 3, 3, 9) == -1
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(w=None), 1), (dict(packed=None), 1), (dict(dtype=5), 3), (dict(C_in=0), 2),
+    (dict(packed_bytes=100), 2), (dict(KH=5, KW=5), 6), (dict(packed=X + 64), 5),
+])
+def test_pack_weights_validation(kw, code):
+    a = dict(w=X, packed=X + 1 << 24, packed_bytes=1 << 22, C_in=16, C_out=32, KT=1, KH=3,
+             KW=3, dtype=L.F16)
+    a["packed"] = Y
+    a.update(kw)
+    st = L.libconv_pack_weights(a["w"], a["packed"], a["packed_bytes"], a["C_in"], a["C_out"],
+                                a["KT"], a["KH"], a["KW"], a["dtype"], None)
+    assert st == code
+
+
+def test_forward_packed_validation():
+    # null packed pointer; bad dtype; 16-bit 3-D layer on the CPU host: no device
+    assert L.libconv_forward_packed(X, None, None, Y, 1, 8, 3, 8, 8, 8, 3, 3, 3, 1, 1, 1, 1, 1,
+                                    1, L.F16, 0, None) == 1
+    assert L.libconv_forward_packed(X, Wp, None, Y, 1, 8, 3, 8, 8, 8, 3, 3, 3, 1, 1, 1, 1, 1, 1,
+                                    4, 0, None) == 3
+
+
+def test_3d_layers_dispatch_to_packed_tiles():
+    for name in ("c5_A", "c5_B"):
+        l = W.ALL_LAYERS[name]
+        st, algo, tile, grid = L.libconv_query_algo(
+            l.N, l.C_in, l.T, l.H, l.W, l.C_out, l.KT, l.KH, l.KW, *l.pad, *l.stride,
+            W.DTYPE_CODE[l.dtype], W.ACT_CODE[l.act], L.ALGO_AUTO)
+        assert st == 0 and L.libconv_tile_name(tile).startswith("igemm16p_")
