@@ -22,7 +22,9 @@
 namespace libconv {
 namespace {
 
-constexpr long long kMaxBytes = 0x7fffffffLL;  // byte offsets are 32-bit signed in the kernels
+// Byte offsets are 32-bit signed in the kernels, and an offset of 0x7ffffff0
+// or more must lie past the end of every tensor (that is how they read zeros).
+constexpr long long kMaxBytes = 0x7fff0000LL;
 
 // a * b, saturated well below overflow (every factor here is a non-negative int)
 long long mul_sat(long long a, long long b) {
@@ -112,10 +114,10 @@ bool device_ok(int d) {
 
 // The dispatcher.  The vector-ALU direct kernel takes layers whose
 // reduction per output (C_in * taps) is too short to fill an MFMA k-step
-// pipeline -- stems with 3 input channels, thin pointwise layers -- and any
-// geometry the MFMA family has no tile for; everything else is an implicit
-// GEMM on the matrix cores.
-constexpr long long kMinMfmaReduction = 64;
+// pipeline -- stems with 3 input channels, pointwise layers with fewer than
+// 32 input channels -- and any geometry the MFMA family has no tile for;
+// everything else is an implicit GEMM on the matrix cores.
+constexpr long long kMinMfmaReduction = 32;
 
 libconv_status plan_for(const Problem& p, int algo, Plan* plan, bool packed_only = false) {
   const long long red = (long long)p.C * p.KT * p.KH * p.KW;

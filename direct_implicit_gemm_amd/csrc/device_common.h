@@ -27,6 +27,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kBufferWord3);
 }
 
+// Byte offset that reads as zero from any buffer made by make_rsrc (tensors
+// are below 2^31 bytes; offsets are unsigned 32-bit).
+constexpr int kOobOffset = -16;
+
+// `ok ? off : kOobOffset`, computed in a register the optimiser treats as
+// opaque.  Written as a plain select, the compiler may turn
+// load(select(c, a, b)) into two loads on two branches, and the join after
+// them makes the wave wait for every load before the next one issues.
+__device__ __forceinline__ int guard_offset(bool ok, int off) {
+  int v = ok ? off : kOobOffset;
+  asm("" : "+v"(v));
+  return v;
+}
+
 // --- storage element <-> fp32 -------------------------------------------
 template <int DT> struct Elem;
 

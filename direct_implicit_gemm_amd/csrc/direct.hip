@@ -32,6 +32,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kRows = 4;               // output rows per workgroup (one per wave)
 constexpr int kLdsBudget = 60 * 1024;  // bytes of LDS a workgroup may use
+constexpr int kBatch = 16;             // global loads in flight per lane while staging
 
 struct DirectArgs {
   const void* x;
@@ -90,31 +91,61 @@ __global__ __launch_bounds__(kThreads) void direct_kernel(DirectArgs a) {
       const int it = ot * a.st - a.pt + kt;
       if (it < 0 || it >= a.T) continue;  // whole frame is padding: contributes 0
       __syncthreads();                    // previous stage fully consumed
-      // Input halo rows, zero outside the input (this is the padding).
-      for (int rr = wave; rr < ccur * a.hr; rr += kThreads / 64) {
-        const int c = rr / a.hr;
-        const int r = rr - c * a.hr;
-        const int ih = ih0 + r;
-        const bool row_ok = (unsigned)ih < (unsigned)a.H;
-        const int row_base = ((((n * a.C + ci0 + c) * a.T + it) * a.H + ih) * a.W);
-        for (int col = lane; col < a.hc; col += 64) {
-          const int iw = iw0 + col;
-          float v = 0.0f;
-          if (row_ok && (unsigned)iw < (unsigned)a.W) v = E::load(xr, (row_base + iw) * eb);
-          xs[rr * a.hc + col] = v;
+      // Input halo, zero outside the input (this is the padding).  Wave w
+      // takes halo rows w, w+4, ...; a row is read as 64-column segments, one
+      // element per lane.  Loads are issued in batches of kBatch before any
+      // LDS store, so a wave waits for one round trip per batch, not per row.
+      {
+        const int nseg = (a.hc + 63) / 64;
+        const int nrows = ccur * a.hr;
+        const int items = wave < nrows ? ((nrows - 1 - wave) / 4 + 1) * nseg : 0;
+        int m = 0, c = wave / a.hr, r = wave - (wave / a.hr) * a.hr;  // item (row, segment)
+        for (int q0 = 0; q0 < items; q0 += kBatch) {
+          float v[kBatch];
+          int dst[kBatch];
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u) {
+            const int col = m * 64 + lane;
+            const int ih = ih0 + r, iw = iw0 + col;
+            const bool live = q0 + u < items && col < a.hc;
+            const bool ok = live && (unsigned)ih < (unsigned)a.H && (unsigned)iw < (unsigned)a.W;
+            const int off = ((((n * a.C + ci0 + c) * a.T + it) * a.H + ih) * a.W + iw) * eb;
+            v[u] = E::load(xr, guard_offset(ok, off));
+            dst[u] = live ? (c * a.hr + r) * a.hc + col : -1;
+            if (++m == nseg) {  // next row of this wave: 4 halo rows further
+              m = 0;
+              r += 4;
+              while (r >= a.hr) {
+                r -= a.hr;
+                ++c;
+              }
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < kBatch; ++u)
+            if (dst[u] >= 0) xs[dst[u]] = v[u];
         }
       }
       // Weights of this channel chunk and frame tap, as [c][tap][co].
       const int nw = ccur * taps2 * COT;
-      for (int e = threadIdx.x; e < nw; e += kThreads) {
-        const int j = e % COT;
-        const int ctap = e / COT;
-        const int c = ctap / taps2;
-        const int tap = ctap - c * taps2;
-        const int co = co0 + j;
-        float v = 0.0f;
-        if (co < a.K) v = E::load(wr, (((co * a.C + ci0 + c) * a.KT + kt) * taps2 + tap) * eb);
-        ws[e] = v;
+      for (int e0 = 0; e0 < nw; e0 += kThreads * kBatch) {
+        float v[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int e = e0 + u * kThreads + threadIdx.x;
+          const int j = e % COT;
+          const int ctap = e / COT;
+          const int c = ctap / taps2;
+          const int tap = ctap - c * taps2;
+          const int co = co0 + j;
+          const bool ok = e < nw && co < a.K;
+          v[u] = E::load(wr, guard_offset(ok, (((co * a.C + ci0 + c) * a.KT + kt) * taps2 + tap) * eb));
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const int e = e0 + u * kThreads + threadIdx.x;
+          if (e < nw) ws[e] = v[u];
+        }
       }
       __syncthreads();
 
@@ -149,16 +180,20 @@ __global__ __launch_bounds__(kThreads) void direct_kernel(DirectArgs a) {
   if (oh >= a.OH) return;
   const __amdgpu_buffer_rsrc_t yr = make_rsrc(a.y, a.y_bytes);
   const __amdgpu_buffer_rsrc_t br = make_rsrc(a.b, a.b_bytes);
+  // All bias loads are issued before any store (one round trip, not one per
+  // channel); channels beyond C_out read 0 and are not stored.
+  float bias[COT];
+#pragma unroll
+  for (int j = 0; j < COT; ++j)
+    bias[j] = E::load(br, guard_offset(a.b && co0 + j < a.K, (co0 + j) * eb));
 #pragma unroll
   for (int j = 0; j < COT; ++j) {
     const int co = co0 + j;
-    if (co >= a.K) break;
-    const float bias = a.b ? E::load(br, co * eb) : 0.0f;
     const int row = (((n * a.K + co) * a.OT + ot) * a.OH + oh) * a.OW;
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       const int ow = ow0 + p * 64 + lane;
-      if (ow < a.OW) E::store(epilogue(acc[j][p], bias, a.relu), yr, (row + ow) * eb);
+      if (co < a.K && ow < a.OW) E::store(epilogue(acc[j][p], bias[j], a.relu), yr, (row + ow) * eb);
     }
   }
 }

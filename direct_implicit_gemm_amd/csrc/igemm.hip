@@ -13,27 +13,32 @@
 // plane (n, ot); four waves in a WM x WN grid, each owning (BM/WM) x (BN/WN)
 // outputs as 32x32 MFMA blocks held in fp32 accumulators.
 //
-// K loop: stages of CK = CG * SE input channels (SE = 8 for 16-bit types,
-// 4 for fp32: one 16-byte "slot"), all taps at once.  Per stage:
+// K loop: one stage = CK = CG * SE input channels (SE = 8 for 16-bit types,
+// 4 for fp32: one 16-byte "slot") at one frame tap kt, with all KH x KW
+// spatial taps.  Stages whose input frame lies wholly in the time padding are
+// skipped (they contribute zero).  Per stage:
 //   * weights land in LDS as Wl[slot][co][SE], slot = tap*CG + g (the SE
-//     channels of group g at one tap, for each output channel).  Two ways:
-//       - from OIHW weights: each thread reads one channel's TS contiguous
-//         16-byte vectors and transposes them in registers (16-byte LDS
-//         stores, lanes on consecutive channels);
+//     channels of group g at one spatial tap, for each output channel):
+//       - from OIHW weights (2-D tiles): each thread reads one channel's
+//         KH*KW contiguous 16-byte vectors and transposes them in registers
+//         (16-byte LDS stores, lanes on consecutive channels);
 //       - from packed weights ([C/SE][taps][C_out padded][SE], made by the
 //         pack kernel below -- the per-layer weight packing of the
 //         Convolution3D work in "SeedVR2 NCNN Vulkan", section 3.2): a stage
-//         is NSLOT contiguous runs that are copied straight into LDS with
-//         direct-to-LDS loads (no registers, no arithmetic);
-//   * the input halo (KT frames x HR rows x HC cols) is read row-contiguously
-//     and written channel-innermost as Xl[g][kt][hr][hc][SE]; taps outside
-//     the input are zero (this is the padding);
+//         is NSLOT contiguous runs copied straight into LDS by direct-to-LDS
+//         loads (no registers, no arithmetic);
+//   * the input halo (HR rows x HC cols of one frame) is read
+//     row-contiguously and written channel-innermost as Xl[g][hr][hc][SE];
+//     taps outside the input are zero (this is the padding);
 //   * the stage's slots are consumed in pairs by one MFMA k-step (32x32x16
 //     f16/bf16: lanes 0-31 carry slot 2p, lanes 32-63 slot 2p+1) or by four
 //     (32x32x2 f32, one element of each slot per step).  Both operands of a
 //     slot are single 16-byte LDS reads.
 // LDS holds two stages; the global loads of stage s+1 are in flight while
-// stage s is multiplied.
+// stage s is multiplied.  Each lane's load offsets are computed once; the
+// per-stage part of every address is wave-uniform and moves the base of the
+// buffer descriptor (scalar arithmetic), so staging costs almost no vector
+// arithmetic and every access stays range-checked.
 //
 // Epilogue (shared with the direct kernel): fp32 accumulator + bias ->
 // optional ReLU -> one round-to-nearest-even conversion -> store, with the
@@ -46,7 +51,8 @@ namespace libconv {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kPackAlign = 128;  // output channels of packed weights are padded to this
+constexpr int kPackAlign = 128;   // output channels of packed weights are padded to this
+constexpr int kFar = 0x7ffffff0;  // offset past the end of every tensor (all are < 0x7fff0000 bytes)
 
 // One MFMA k-step over a pair of 16-byte slots.  KSUB is the number of
 // instructions a slot pair takes; step(.., k) issues sub-step k.
@@ -97,7 +103,7 @@ struct IgemmArgs {
   int pt, ph, pw;
   int st;             // time stride (the spatial strides are template parameters)
   int relu;
-  int stages;         // ceil(C / CK)
+  int chunks;         // ceil(C / CK)
   int kp;             // packed weights: output-channel stride (C_out rounded up)
   int co_tiles, row_tiles, col_tiles;
   uint32_t x_bytes, w_bytes, b_bytes, y_bytes;
@@ -112,13 +118,14 @@ struct Cfg {
   static constexpr int EB = Elem<DT>::bytes;
   static constexpr int SE = Mma<DT>::SE;
   static constexpr int CK = CG * SE;
-  static constexpr int TS = KT * KH * KW;
-  static constexpr int NSLOT = TS * CG;
+  static constexpr int TS = KT * KH * KW;          // all taps (weight layout)
+  static constexpr int TS2 = KH * KW;              // spatial taps of one stage
+  static constexpr int NSLOT = TS2 * CG;
   static constexpr int NPAIR = (NSLOT + 1) / 2;
   static constexpr int BN = TH * TW;
   static constexpr int HR = (TH - 1) * SH + KH;
   static constexpr int HC = (TW - 1) * SW + KW;
-  static constexpr int XPLANE = KT * HR * HC;      // halo pixels per channel group
+  static constexpr int XPLANE = HR * HC;           // halo pixels per channel group
   static constexpr int WBYTES = NSLOT * BM * 16;
   static constexpr int XBYTES = CG * XPLANE * 16;
   static constexpr int BUF = WBYTES + XBYTES;
@@ -142,15 +149,19 @@ struct Cfg {
   static_assert(TW % 32 == 0, "tile rows are whole 32-pixel blocks");
   static_assert(BM % 64 == 0 || !PK, "packed tiles move whole 64-channel chunks");
   static_assert(BM <= kPackAlign, "packed channel padding covers one tile");
+  static_assert(PK || KT == 1, "weights from OIHW: 2-D tiles only");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
 // Global -> registers for one stage (weights only when they are transposed
-// here; packed weights go straight to LDS).
+// here; packed weights go straight to LDS).  Input elements are kept exactly
+// as loaded and only packed into 16-byte words when they are written to LDS,
+// after the current stage's MFMAs: any arithmetic on them right after the
+// loads would make the wave wait for the loads before computing.
 template <class G>
 struct StageRegs {
   u32x4_t wv[G::WPASS > 0 ? G::WPASS : 1][G::TS];
-  u32x4_t xv[G::XPASS];
+  uint32_t xe[G::XPASS][G::SE];
 };
 
 // Slot vector of tap t from a unit's TS vectors: the unit holds
@@ -199,7 +210,7 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int il = lane & 31;   // row (A) / column (B) inside a 32x32 block
   const int hf = lane >> 5;   // which slot of the pair this lane carries
 
@@ -223,74 +234,88 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
   const int ih0 = oh0 * G::SH - a.ph;
   const int iw0 = ow0 * G::SW - a.pw;
   const int it0 = ot * a.st - a.pt;
+  // frame taps whose input frame exists; the others are time padding
+  const int kt_lo = it0 < 0 ? -it0 : 0;
+  const int kt_hi = min(G::KT, a.T - it0);
+  const int nkt = kt_hi > kt_lo ? kt_hi - kt_lo : 0;
+  const int nstages = a.chunks * nkt;
 
-  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, a.x_bytes);
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.w, a.w_bytes);
-  constexpr int kOob = 0x7ffffff0;  // byte offset beyond any tensor: reads 0
 
-  const int cstride = a.C * G::TS;       // elements between output channels in w
-  const int plane = a.T * a.H * a.W;     // elements between input channels in x
+  const int hw = a.H * a.W;
+  const int plane = a.T * hw;            // elements between input channels in x
 
-  // Packed weights of stage s straight into LDS buffer `buf`: chunk c covers
-  // 64 channels of one slot; a wave moves one chunk per instruction, lane l
-  // landing at chunk base + 16 l.
-  auto dma_weights = [&](int s, unsigned char* buf) {
+  // ---- per-lane, stage-invariant load offsets (bytes).  The per-stage part
+  // of every address is wave-uniform: it moves the base of the buffer
+  // descriptor (scalar arithmetic), while the range check keeps covering
+  // every access up to the end of the tensor.
+  // input halo unit u = (g * HR + hr) * HC + hc, channel j of its group
+  int xoff[G::XPASS][SE];                // kFar when the position is padding
+  int xgrp[G::XPASS];
+#pragma unroll
+  for (int i = 0; i < G::XPASS; ++i) {
+    const int u = tid + i * kThreads;
+    const int hc = u % G::HC;
+    const int hr = (u / G::HC) % G::HR;
+    const int g = u / (G::HC * G::HR);
+    const int ih = ih0 + hr, iw = iw0 + hc;
+    const bool ok = u < G::XUNITS && (unsigned)ih < (unsigned)a.H && (unsigned)iw < (unsigned)a.W;
+#pragma unroll
+    for (int j = 0; j < SE; ++j)
+      xoff[i][j] = guard_offset(true, ok ? ((g * SE + j) * plane + ih * a.W + iw) * EB : kFar);
+    xgrp[i] = g;
+  }
+  // OIHW weight unit u = g * BM + col
+  int woff[G::WPASS > 0 ? G::WPASS : 1];
+  int wgrp[G::WPASS > 0 ? G::WPASS : 1];
+#pragma unroll
+  for (int i = 0; i < G::WPASS; ++i) {
+    const int u = tid + i * kThreads;
+    const int g = u / G::BM, col = u % G::BM;
+    const int co = co0 + col;
+    const bool ok = u < G::WUNITS && co < a.K;
+    woff[i] = guard_offset(true, ok ? (co * a.C * G::TS + g * SE * G::TS) * EB : kFar);
+    wgrp[i] = g;
+  }
+  const int n_base = n * a.C * plane * EB;
+
+  // Issue the global reads of stage (chunk, kt): packed weights straight into
+  // LDS buffer `buf`, everything else into registers.
+  auto load_stage = [&](int chunk, int kt, StageRegs<G>& r, unsigned char* buf) {
+    const int ci0 = chunk * G::CK;
+    const bool full = ci0 + G::CK <= a.C;  // uniform: no channel of the stage is past C
     if constexpr (G::PK) {
+      // chunk c = 64 channels of one slot; lane l lands at chunk base + 16 l
       for (int c = wave; c < G::WCHUNKS; c += kThreads / 64) {
         const int slot = c / (G::BM / 64), part = c % (G::BM / 64);
-        const int t = slot / G::CG, g = slot % G::CG;
-        const int gabs = s * G::CG + g;
-        const int src = ((gabs * G::TS + t) * a.kp + co0 + part * 64 + lane) * 16;
+        const int t2 = slot / G::CG, g = slot % G::CG;
+        const int run = ((chunk * G::CG + g) * G::TS + kt * G::TS2 + t2) * a.kp + co0 + part * 64;
         unsigned char* dst = buf + (slot * G::BM + part * 64) * 16;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            wr, (__attribute__((address_space(3))) void*)dst, 16, src, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (__attribute__((address_space(3))) void*)dst,
+                                                 16, (run + lane) * 16, 0, 0, 0);
+      }
+    } else {
+      const int sb = ci0 * G::TS * EB;
+      const __amdgpu_buffer_rsrc_t ws = make_rsrc((const char*)a.w + sb, a.w_bytes - sb);
+#pragma unroll
+      for (int i = 0; i < G::WPASS; ++i) {
+        int v = woff[i];
+        if (!full && ci0 + wgrp[i] * SE >= a.C) v = guard_offset(true, kFar);
+#pragma unroll
+        for (int k = 0; k < G::TS; ++k)
+          r.wv[i][k] = __builtin_bit_cast(
+              u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ws, v + k * 16, 0, 0));
       }
     }
-  };
-
-  auto load_stage = [&](int s, StageRegs<G>& r) {
-    const int ci0 = s * G::CK;
-    // weights from OIHW: unit u = g * BM + col -> TS vectors of
-    // w[co0 + col][ci0 + g*SE ..][..] (C is a multiple of SE, so a group is
-    // wholly inside or outside C)
-#pragma unroll
-    for (int i = 0; i < G::WPASS; ++i) {
-      const int u = tid + i * kThreads;
-      const int g = u / G::BM, col = u % G::BM;
-      const int co = co0 + col;
-      const int cg = ci0 + g * SE;
-      const bool ok = u < G::WUNITS && co < a.K && cg < a.C;
-      const int base = (co * cstride + cg * G::TS) * EB;
-#pragma unroll
-      for (int k = 0; k < G::TS; ++k)
-        r.wv[i][k] = __builtin_bit_cast(
-            u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(wr, ok ? base + k * 16 : kOob, 0, 0));
-    }
-    // input halo: unit u = ((g * KT + kt) * HR + hr) * HC + hc
+    const int sb = n_base + (ci0 * plane + (it0 + kt) * hw) * EB;
+    const __amdgpu_buffer_rsrc_t xs = make_rsrc((const char*)a.x + sb, a.x_bytes - sb);
 #pragma unroll
     for (int i = 0; i < G::XPASS; ++i) {
-      const int u = tid + i * kThreads;
-      int v = u;
-      const int hc = v % G::HC;
-      v /= G::HC;
-      const int hr = v % G::HR;
-      v /= G::HR;
-      const int kt = v % G::KT;
-      const int g = v / G::KT;
-      const int ih = ih0 + hr, iw = iw0 + hc, it = it0 + kt;
-      const int cbase = ci0 + g * SE;
-      const bool ok = u < G::XUNITS && (unsigned)ih < (unsigned)a.H &&
-                      (unsigned)iw < (unsigned)a.W && (unsigned)it < (unsigned)a.T;
-      const int base = (((n * a.C + cbase) * a.T + it) * a.H + ih) * a.W + iw;
-      uint32_t e[SE];
 #pragma unroll
-      for (int j = 0; j < SE; ++j)
-        e[j] = E::load_bits(xr, (ok && cbase + j < a.C) ? (base + j * plane) * EB : kOob);
-      if constexpr (SE == 8) {
-        r.xv[i] = u32x4_t{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
-                          e[6] | (e[7] << 16)};
-      } else {
-        r.xv[i] = u32x4_t{e[0], e[1], e[2], e[3]};
+      for (int j = 0; j < SE; ++j) {
+        int v = xoff[i][j];
+        if (!full && ci0 + xgrp[i] * SE + j >= a.C) v = guard_offset(true, kFar);
+        r.xe[i][j] = E::load_bits(xs, v);
       }
     }
   };
@@ -306,12 +331,19 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
         store_slots<SE, G::TS, 0>(buf + ((u / G::BM) * G::BM + u % G::BM) * 16,
                                   G::CG * G::BM * 16, r.wv[i]);
     }
-    // input halo
+    // input halo: pack the SE channels of each unit into one 16-byte word
     unsigned char* xbuf = buf + G::WBYTES;
 #pragma unroll
     for (int i = 0; i < G::XPASS; ++i) {
       const int u = tid + i * kThreads;
-      if (u < G::XUNITS) *reinterpret_cast<u32x4_t*>(xbuf + u * 16) = r.xv[i];
+      const uint32_t* e = r.xe[i];
+      u32x4_t v;
+      if constexpr (SE == 8)
+        v = u32x4_t{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
+                    e[6] | (e[7] << 16)};
+      else
+        v = u32x4_t{e[0], e[1], e[2], e[3]};
+      if (u < G::XUNITS) *reinterpret_cast<u32x4_t*>(xbuf + u * 16) = v;
     }
   };
 
@@ -323,7 +355,7 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
   const int prow0 = blk0 / G::BPR, pcol0 = (blk0 % G::BPR) * 32;
   // A: Wl[slot][co][16 B]; lanes of half hf read slot 2p + hf.
   const int a_lane = ((hf * G::BM) + co_w0 + il) * 16;
-  // B: Xl[g][kt][hr][hc][16 B] at the lane's pixel.
+  // B: Xl[g][hr][hc][16 B] at the lane's pixel.
   const int b_lane = ((prow0 * G::SH) * G::HC + (pcol0 + il) * G::SW) * 16;
 
   float16_t acc[G::FA][G::FB];
@@ -337,10 +369,9 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
   // byte offset of slot s inside the halo area (pixel (0,0) of the tile)
   auto xslot = [](int s) constexpr -> int {
     const int tap = s / G::CG, g = s % G::CG;
-    const int kt = tap / (G::KH * G::KW);
-    const int kh = (tap / G::KW) % G::KH;
+    const int kh = tap / G::KW;
     const int kw = tap % G::KW;
-    return (((g * G::KT + kt) * G::HR + kh) * G::HC + kw) * 16;
+    return ((g * G::HR + kh) * G::HC + kw) * 16;
   };
   // byte offset of block j of this wave relative to its first block
   auto xblock = [&](int j) -> int {
@@ -385,46 +416,61 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
     }
   };
 
-  // ---- main loop: two LDS stages, next stage's global loads in flight
-  StageRegs<G> regs;
-  dma_weights(0, lds);
-  load_stage(0, regs);
-  store_stage(regs, lds);
-  __builtin_amdgcn_s_waitcnt(0);  // direct-to-LDS copies are counted as loads
-  __syncthreads();
-  for (int s = 0; s < a.stages; ++s) {
-    unsigned char* cur = lds + (s & 1) * G::BUF;
-    unsigned char* nxt = lds + ((s + 1) & 1) * G::BUF;
-    const bool more = s + 1 < a.stages;
-    if (more) {
-      dma_weights(s + 1, nxt);
-      load_stage(s + 1, regs);
-    }
-    compute(cur);
-    if (more) store_stage(regs, nxt);
-    __builtin_amdgcn_s_waitcnt(0);
+  // ---- main loop over stages (chunk, kt), chunk-major: two LDS buffers,
+  // the next stage's global reads in flight during the current MFMAs
+  if (nstages > 0) {
+    StageRegs<G> regs;
+    int chunk = 0, kt = kt_lo;
+    load_stage(chunk, kt, regs, lds);
+    store_stage(regs, lds);
+    __builtin_amdgcn_s_waitcnt(0);  // direct-to-LDS copies are counted as loads
     __syncthreads();
+    for (int s = 0; s < nstages; ++s) {
+      unsigned char* cur = lds + (s & 1) * G::BUF;
+      unsigned char* nxt = lds + ((s + 1) & 1) * G::BUF;
+      const bool more = s + 1 < nstages;
+      if (more) {
+        if (++kt == kt_hi) {
+          kt = kt_lo;
+          ++chunk;
+        }
+        load_stage(chunk, kt, regs, nxt);
+      }
+      compute(cur);
+      if (more) store_stage(regs, nxt);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
   }
 
   // ---- epilogue
   const __amdgpu_buffer_rsrc_t yr = make_rsrc(a.y, a.y_bytes);
   const __amdgpu_buffer_rsrc_t br = make_rsrc(a.b, a.b_bytes);
   const int ohw = a.OH * a.OW;
+  // All bias loads first (one round trip); channels beyond C_out read 0 and
+  // are not stored.
+  float bias[G::FA][16];
+#pragma unroll
+  for (int i = 0; i < G::FA; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int co = co0 + co_w0 + i * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+      bias[i][r] = E::load(br, guard_offset(a.b && co < a.K, co * EB));
+    }
 #pragma unroll
   for (int i = 0; i < G::FA; ++i) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int co = co0 + co_w0 + i * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-      if (co >= a.K) continue;
-      const float bias = a.b ? E::load(br, co * EB) : 0.0f;
       const int cbase = ((n * a.K + co) * a.OT + ot) * ohw;
 #pragma unroll
       for (int j = 0; j < G::FB; ++j) {
         const int b = blk0 + j;
         const int oh = oh0 + b / G::BPR;
         const int ow = ow0 + (b % G::BPR) * 32 + il;
-        if (oh < a.OH && ow < a.OW)
-          E::store(epilogue(acc[i][j][r], bias, a.relu), yr, (cbase + oh * a.OW + ow) * EB);
+        if (co < a.K && oh < a.OH && ow < a.OW)
+          E::store(epilogue(acc[i][j][r], bias[i][r], a.relu), yr,
+                   (cbase + oh * a.OW + ow) * EB);
       }
     }
   }
@@ -460,7 +506,6 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackArgs a) {
   using E = Elem<DT>;
   constexpr int SE = Mma<DT>::SE;
   constexpr int EB = E::bytes;
-  constexpr int kOob = 0x7ffffff0;
   const int u = blockIdx.x * kThreads + threadIdx.x;
   if (u >= a.G * a.Kp) return;
   const int g = u / a.Kp, co = u % a.Kp;
@@ -474,7 +519,7 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackArgs a) {
     for (int k = 0; k < TS; ++k)
       v[k] = __builtin_bit_cast(
           u32x4_t,
-          __builtin_amdgcn_raw_buffer_load_b128(wr, co_ok ? base * EB + k * 16 : kOob, 0, 0));
+          __builtin_amdgcn_raw_buffer_load_b128(wr, guard_offset(co_ok, base * EB + k * 16), 0, 0));
   } else {
 #pragma unroll
     for (int k = 0; k < TS; ++k) {
@@ -485,7 +530,7 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackArgs a) {
         for (int h = 0; h < 4 / EB; ++h) {
           const int e = k * SE + m * (4 / EB) + h;  // element of the [SE][TS] block
           const bool ok = co_ok && g * SE + e / TS < a.C;
-          const uint32_t bits = E::load_bits(wr, ok ? (base + e) * EB : kOob);
+          const uint32_t bits = E::load_bits(wr, guard_offset(ok, (base + e) * EB));
           word |= (EB == 2) ? ((bits & 0xffffu) << (16 * h)) : bits;
         }
         v[k][m] = word;
@@ -511,6 +556,8 @@ struct TileDesc {
   int flat;       // 1: 1x1 stride-1 pad-0 layer viewed as one long row per plane
   int BM, TH, TW, CG;
   int packed;     // 1: reads packed weights
+  int eff;        // fraction of MFMA peak one CU reaches on this tile, in percent
+                  // (measured on MI355X on large grids; used to rank tiles)
   int lds;
   const char* name;
   LaunchFn fn[3];  // by libconv_dtype
@@ -527,8 +574,8 @@ constexpr LaunchFn launcher() {
     return nullptr;
 }
 
-#define LIBCONV_TILE(ID, WIDE, KT, KH, KW, SH, SW, FLAT, BM, TH, TW, WM, WN, CG, PK, NAME) \
-  {ID, WIDE, KT, KH, KW, SH, SW, FLAT, BM, TH, TW, CG, PK,                                  \
+#define LIBCONV_TILE(ID, WIDE, KT, KH, KW, SH, SW, FLAT, BM, TH, TW, WM, WN, CG, PK, EFF, NAME) \
+  {ID, WIDE, KT, KH, KW, SH, SW, FLAT, BM, TH, TW, CG, PK, EFF,                                  \
    Cfg<WIDE ? DT_F16 : DT_F32, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK>::LDS, NAME,  \
    {launcher<DT_F32, WIDE, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK>(),               \
     launcher<DT_F16, WIDE, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK>(),               \
@@ -536,28 +583,35 @@ constexpr LaunchFn launcher() {
 
 const TileDesc kTiles[] = {
     // 16-bit operands, 3x3 stride 1, weights transposed in the kernel
-    LIBCONV_TILE(200, 1, 1, 3, 3, 1, 1, 0, 128, 8, 32, 2, 2, 2, 0, "igemm16_k3s1_m128_n8x32"),
-    LIBCONV_TILE(201, 1, 1, 3, 3, 1, 1, 0, 128, 4, 32, 2, 2, 2, 0, "igemm16_k3s1_m128_n4x32"),
-    LIBCONV_TILE(202, 1, 1, 3, 3, 1, 1, 0, 128, 2, 64, 2, 2, 2, 0, "igemm16_k3s1_m128_n2x64"),
-    LIBCONV_TILE(203, 1, 1, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 0, "igemm16_k3s1_m64_n8x32"),
+    LIBCONV_TILE(200, 1, 1, 3, 3, 1, 1, 0, 128, 8, 32, 2, 2, 2, 0, 20, "igemm16_k3s1_m128_n8x32"),
+    LIBCONV_TILE(201, 1, 1, 3, 3, 1, 1, 0, 128, 4, 32, 2, 2, 2, 0, 17, "igemm16_k3s1_m128_n4x32"),
+    LIBCONV_TILE(202, 1, 1, 3, 3, 1, 1, 0, 128, 2, 64, 2, 2, 2, 0, 14, "igemm16_k3s1_m128_n2x64"),
+    LIBCONV_TILE(203, 1, 1, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 0, 28, "igemm16_k3s1_m64_n8x32"),
     // 16-bit operands, 3x3 stride 2
-    LIBCONV_TILE(210, 1, 1, 3, 3, 2, 2, 0, 64, 4, 32, 2, 2, 2, 0, "igemm16_k3s2_m64_n4x32"),
+    LIBCONV_TILE(210, 1, 1, 3, 3, 2, 2, 0, 64, 4, 32, 2, 2, 2, 0, 20, "igemm16_k3s2_m64_n4x32"),
     // 16-bit operands, 1x1 stride 1 pad 0 (flattened planes)
-    LIBCONV_TILE(220, 1, 1, 1, 1, 1, 1, 1, 128, 1, 256, 2, 2, 8, 0, "igemm16_k1_m128_n256"),
-    LIBCONV_TILE(221, 1, 1, 1, 1, 1, 1, 1, 128, 1, 128, 2, 2, 8, 0, "igemm16_k1_m128_n128"),
+    LIBCONV_TILE(220, 1, 1, 1, 1, 1, 1, 1, 128, 1, 256, 2, 2, 8, 0, 20, "igemm16_k1_m128_n256"),
+    LIBCONV_TILE(221, 1, 1, 1, 1, 1, 1, 1, 128, 1, 128, 2, 2, 8, 0, 20, "igemm16_k1_m128_n128"),
     // fp32 operands
-    LIBCONV_TILE(240, 0, 1, 3, 3, 1, 1, 0, 32, 8, 32, 1, 4, 4, 0, "igemm32_k3s1_m32_n8x32"),
-    LIBCONV_TILE(241, 0, 1, 3, 3, 1, 1, 0, 64, 4, 32, 2, 2, 4, 0, "igemm32_k3s1_m64_n4x32"),
-    LIBCONV_TILE(242, 0, 1, 3, 3, 2, 2, 0, 64, 2, 32, 2, 2, 4, 0, "igemm32_k3s2_m64_n2x32"),
-    LIBCONV_TILE(243, 0, 1, 1, 1, 1, 1, 1, 64, 1, 128, 2, 2, 8, 0, "igemm32_k1_m64_n128"),
-    // packed weights: 16-bit, 3x3x3 stride 1
-    LIBCONV_TILE(260, 1, 3, 3, 3, 1, 1, 0, 128, 8, 32, 2, 2, 1, 1, "igemm16p_k333s1_m128_n8x32"),
-    LIBCONV_TILE(261, 1, 3, 3, 3, 1, 1, 0, 128, 4, 32, 2, 2, 1, 1, "igemm16p_k333s1_m128_n4x32"),
-    LIBCONV_TILE(262, 1, 3, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 1, 1, "igemm16p_k333s1_m64_n8x32"),
+    LIBCONV_TILE(240, 0, 1, 3, 3, 1, 1, 0, 32, 8, 32, 1, 4, 4, 0, 50, "igemm32_k3s1_m32_n8x32"),
+    LIBCONV_TILE(241, 0, 1, 3, 3, 1, 1, 0, 64, 4, 32, 2, 2, 4, 0, 40, "igemm32_k3s1_m64_n4x32"),
+    LIBCONV_TILE(242, 0, 1, 3, 3, 2, 2, 0, 64, 2, 32, 2, 2, 4, 0, 35, "igemm32_k3s2_m64_n2x32"),
+    LIBCONV_TILE(243, 0, 1, 1, 1, 1, 1, 1, 64, 1, 128, 2, 2, 8, 0, 15, "igemm32_k1_m64_n128"),
+    // fp32, 8 channels per stage: small LDS stages, several workgroups per CU
+    LIBCONV_TILE(244, 0, 1, 3, 3, 1, 1, 0, 32, 8, 32, 1, 4, 2, 0, 48, "igemm32_k3s1_m32_n8x32_c8"),
+    LIBCONV_TILE(245, 0, 1, 3, 3, 2, 2, 0, 64, 2, 32, 2, 2, 2, 0, 44, "igemm32_k3s2_m64_n2x32_c8"),
+    LIBCONV_TILE(246, 0, 1, 3, 3, 2, 2, 0, 64, 4, 32, 2, 2, 2, 0, 44, "igemm32_k3s2_m64_n4x32_c8"),
+    LIBCONV_TILE(247, 0, 1, 3, 3, 1, 1, 0, 32, 4, 32, 1, 4, 2, 0, 48, "igemm32_k3s1_m32_n4x32_c8"),
+    // packed weights: 16-bit, 3x3x3 stride 1 (one frame tap per stage)
+    LIBCONV_TILE(260, 1, 3, 3, 3, 1, 1, 0, 128, 8, 32, 2, 2, 2, 1, 30, "igemm16p_k333s1_m128_n8x32"),
+    LIBCONV_TILE(261, 1, 3, 3, 3, 1, 1, 0, 128, 4, 32, 2, 2, 2, 1, 23, "igemm16p_k333s1_m128_n4x32"),
+    LIBCONV_TILE(262, 1, 3, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 1, 33, "igemm16p_k333s1_m64_n8x32"),
+    LIBCONV_TILE(263, 1, 3, 3, 3, 1, 1, 0, 64, 4, 32, 1, 4, 2, 1, 30, "igemm16p_k333s1_m64_n4x32"),
+    LIBCONV_TILE(264, 1, 3, 3, 3, 1, 1, 0, 128, 8, 32, 2, 2, 1, 1, 24, "igemm16p_k333s1_m128_n8x32_c8"),
     // packed weights: 16-bit, 3x3 stride 1
-    LIBCONV_TILE(270, 1, 1, 3, 3, 1, 1, 0, 128, 8, 32, 2, 2, 2, 1, "igemm16p_k3s1_m128_n8x32"),
-    LIBCONV_TILE(271, 1, 1, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 1, "igemm16p_k3s1_m64_n8x32"),
-    LIBCONV_TILE(272, 1, 1, 3, 3, 1, 1, 0, 128, 4, 32, 2, 2, 2, 1, "igemm16p_k3s1_m128_n4x32"),
+    LIBCONV_TILE(270, 1, 1, 3, 3, 1, 1, 0, 128, 8, 32, 2, 2, 2, 1, 30, "igemm16p_k3s1_m128_n8x32"),
+    LIBCONV_TILE(271, 1, 1, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 1, 36, "igemm16p_k3s1_m64_n8x32"),
+    LIBCONV_TILE(272, 1, 1, 3, 3, 1, 1, 0, 128, 4, 32, 2, 2, 2, 1, 23, "igemm16p_k3s1_m128_n4x32"),
 };
 
 #undef LIBCONV_TILE
@@ -669,9 +723,28 @@ libconv_status pack_launch(const void* w, void* wp, int C, int K, int KT, int KH
   return e == hipSuccess ? LIBCONV_OK : LIBCONV_ERR_LAUNCH;
 }
 
-// Among the tiles that fit (packed or not, as asked), minimise the critical
-// path on 256 compute units: rounds of workgroups times the (padded) work of
-// one tile.
+// Estimated time of a tile on this shape, in microseconds: rounds of
+// workgroups on 256 compute units times the (padded) MFMA work of one tile at
+// the tile's measured efficiency, plus -- for packed tiles when the caller
+// gave OIHW weights -- the pack kernel (a launch plus reading and writing the
+// weights once).
+static double estimate_us(const TileDesc& t, const Problem& p, const TileCounts& c) {
+  const double ck = t.CG * (t.wide ? 8 : 4);
+  const double chunks = std::ceil(p.C / ck);
+  const double kred = chunks * ck * p.KT * p.KH * p.KW;
+  const double tile_flop = 2.0 * t.BM * t.TH * t.TW * kred;
+  const double cu_flop_per_us = (t.wide ? 4096.0 : 256.0) * 2400.0 * (t.eff / 100.0);
+  const double rounds = std::ceil(c.total / 256.0);
+  double us = rounds * tile_flop / cu_flop_per_us;
+  if (t.packed && !p.wp) {
+    const double wbytes = (double)packed_weight_bytes(p.C, p.K, p.KT, p.KH, p.KW, p.dtype);
+    us += 6.0 + 2.0 * wbytes / 3.0e6;
+  }
+  return us;
+}
+
+// Among the tiles that fit (packed or not, as asked), the one with the
+// smallest estimated time.
 static bool plan_among(const Problem& p, int want_packed, Plan* plan) {
   const TileDesc* best = nullptr;
   double best_cost = 0.0;
@@ -680,11 +753,8 @@ static bool plan_among(const Problem& p, int want_packed, Plan* plan) {
     if (want_packed >= 0 && t.packed != want_packed) continue;
     if (!tile_fits(t, p) || !t.fn[p.dtype]) continue;
     const TileCounts c = counts(t, p);
-    const double rounds = (double)((c.total + 255) / 256);
-    const double cost = rounds * (double)t.BM * t.TH * t.TW;
-    if (!best || cost < best_cost * 0.999 ||
-        (cost <= best_cost * 1.001 &&
-         (long long)t.BM * t.TH * t.TW > (long long)best->BM * best->TH * best->TW)) {
+    const double cost = estimate_us(t, p, c);
+    if (!best || cost < best_cost) {
       best = &t;
       best_cost = cost;
       best_total = c.total;
@@ -697,13 +767,7 @@ static bool plan_among(const Problem& p, int want_packed, Plan* plan) {
   return true;
 }
 
-bool igemm_plan(const Problem& p, Plan* plan) {
-  // Packed-weight tiles exist only where transposing OIHW weights inside the
-  // kernel does not pay: 3-D layers, whose 27-tap weight groups are too large
-  // to transpose in registers.
-  if (p.KT > 1 && plan_among(p, 1, plan)) return true;
-  return plan_among(p, 0, plan);
-}
+bool igemm_plan(const Problem& p, Plan* plan) { return plan_among(p, -1, plan); }
 
 bool igemm_plan_packed(const Problem& p, Plan* plan) { return plan_among(p, 1, plan); }
 
@@ -735,7 +799,7 @@ libconv_status igemm_launch(const Problem& p, const Plan& plan) {
   a.pt = p.pt; a.ph = p.ph; a.pw = p.pw; a.st = p.st;
   a.relu = p.act == LIBCONV_ACT_RELU;
   const int ck = t->CG * (t->wide ? 8 : 4);
-  a.stages = (p.C + ck - 1) / ck;
+  a.chunks = (p.C + ck - 1) / ck;
   a.kp = (p.K + kPackAlign - 1) / kPackAlign * kPackAlign;
   a.co_tiles = (int)c.co; a.row_tiles = (int)c.rows; a.col_tiles = (int)c.cols;
   const int eb = dtype_bytes(p.dtype);

@@ -90,7 +90,7 @@ def test_query_algo_validation():
 
 EXPECTED_ALGO = {  # the dispatcher's choice per workload layer
     "c1": L.ALGO_DIRECT, "c2_L1": L.ALGO_DIRECT, "c2_L2": L.ALGO_IGEMM,
-    "c2_L3": L.ALGO_DIRECT, "c2_L4": L.ALGO_IGEMM, "c3_A": L.ALGO_IGEMM,
+    "c2_L3": L.ALGO_IGEMM, "c2_L4": L.ALGO_IGEMM, "c3_A": L.ALGO_IGEMM,
     "c3_B": L.ALGO_IGEMM, "c4_A": L.ALGO_IGEMM, "c4_B": L.ALGO_IGEMM,
     "c5_A": L.ALGO_IGEMM, "c5_B": L.ALGO_IGEMM,
 }
@@ -117,9 +117,15 @@ def test_forced_algorithms():
     args5 = (1, 32, 1, 20, 20, 32, 1, 5, 5, 0, 2, 2, 1, 1, 1, L.F16, 0)
     assert L.libconv_query_algo(*args5, L.ALGO_IGEMM)[0] == 6
     assert L.libconv_query_algo(*args5, L.ALGO_AUTO)[1] == L.ALGO_DIRECT
-    # fp16 with C_in not a multiple of 8: direct
+    # fp16 with C_in not a multiple of 8: only the packed-weight MFMA tiles
+    # (whose channel groups are zero-padded) or the direct kernel can run it
     args7 = (1, 12, 1, 20, 20, 32, 1, 3, 3, 0, 1, 1, 1, 1, 1, L.F16, 0)
-    assert L.libconv_query_algo(*args7, L.ALGO_AUTO)[1] == L.ALGO_DIRECT
+    st, algo, tile, _ = L.libconv_query_algo(*args7, L.ALGO_AUTO)
+    assert st == 0
+    assert algo == L.ALGO_DIRECT or L.libconv_tile_name(tile).startswith("igemm16p_")
+    # a pointwise layer with 16 input channels: too short a reduction for MFMA
+    args1 = (1, 16, 1, 64, 64, 64, 1, 1, 1, 0, 0, 0, 1, 1, 1, L.F32, 0)
+    assert L.libconv_query_algo(*args1, L.ALGO_AUTO)[1] == L.ALGO_DIRECT
 
 
 def test_packed_weight_bytes():
@@ -137,9 +143,8 @@ def test_packed_weight_bytes():
     (dict(packed_bytes=100), 2), (dict(KH=5, KW=5), 6), (dict(packed=X + 64), 5),
 ])
 def test_pack_weights_validation(kw, code):
-    a = dict(w=X, packed=X + 1 << 24, packed_bytes=1 << 22, C_in=16, C_out=32, KT=1, KH=3,
-             KW=3, dtype=L.F16)
-    a["packed"] = Y
+    a = dict(w=X, packed=Y, packed_bytes=1 << 22, C_in=16, C_out=32, KT=1, KH=3, KW=3,
+             dtype=L.F16)
     a.update(kw)
     st = L.libconv_pack_weights(a["w"], a["packed"], a["packed_bytes"], a["C_in"], a["C_out"],
                                 a["KT"], a["KH"], a["KW"], a["dtype"], None)

@@ -56,6 +56,8 @@ PACKED_CASES = [
     (260, 3, "f16", 1, 16, (5, 9, 40), 128, False),
     (261, 3, "bf16", 1, 24, (3, 7, 33), 200, True),    # C % 8 != 0 (zero-padded group)
     (262, 3, "f16", 2, 8, (4, 10, 35), 64, False),
+    (263, 3, "bf16", 1, 40, (3, 6, 70), 96, True),
+    (264, 3, "f16", 1, 16, (2, 9, 37), 130, False),     # K % 128 != 0
     (270, 2, "bf16", 1, 32, (11, 40), 128, True),
     (271, 2, "f16", 2, 20, (9, 33), 72, False),        # C % 8 != 0, K % 64 != 0
     (272, 2, "f16", 1, 64, (7, 70), 256, True),
