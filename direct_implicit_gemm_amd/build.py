@@ -47,6 +47,17 @@ def _compile(src: str, obj: str) -> None:
         sys.stderr.write(err + "\n")
 
 
+def _check_stubs(lib: str) -> None:
+    """Fail when a kernel's host launch stub is missing from the library (the
+    host pass can drop one silently; the library would then not load)."""
+    r = subprocess.run(["nm", "-D", "--undefined-only", lib], capture_output=True, text=True)
+    if r.returncode != 0:
+        return  # no nm: the load test catches it
+    missing = [l.split()[-1] for l in r.stdout.splitlines() if "__device_stub__" in l]
+    if missing:
+        raise RuntimeError("kernel launch stubs missing from libconv.so:\n" + "\n".join(missing))
+
+
 def build(verbose: bool = True) -> str:
     with tempfile.TemporaryDirectory(prefix="libconv_build_") as tmp:
         objs = [os.path.join(tmp, s.rsplit(".", 1)[0] + ".o") for s in SOURCES]
@@ -55,6 +66,7 @@ def build(verbose: bool = True) -> str:
         out_tmp = LIB_PATH + ".tmp"
         cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", out_tmp, *objs]
         subprocess.run(cmd, check=True, capture_output=True, text=True)
+        _check_stubs(out_tmp)
         os.replace(out_tmp, LIB_PATH)
     if verbose:
         print(f"built {LIB_PATH}")

@@ -22,6 +22,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kBufferWord3);
@@ -56,10 +57,19 @@ template <> struct Elem<DT_F32> {
     return __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0);
   }
   __device__ static __forceinline__ float bits_to_f32(uint32_t b) { return __builtin_bit_cast(float, b); }
+  // the element exactly as loaded, in its own width
+  using raw_t = uint32_t;
+  __device__ static __forceinline__ raw_t load_raw(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0);
+  }
 };
 
 template <> struct Elem<DT_F16> {
   static constexpr int bytes = 2;
+  using raw_t = uint16_t;
+  __device__ static __forceinline__ raw_t load_raw(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, byte_off, 0, 0);
+  }
   __device__ static __forceinline__ float bits_to_f32(uint32_t b) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
   }
@@ -80,6 +90,10 @@ template <> struct Elem<DT_F16> {
 
 template <> struct Elem<DT_BF16> {
   static constexpr int bytes = 2;
+  using raw_t = uint16_t;
+  __device__ static __forceinline__ raw_t load_raw(__amdgpu_buffer_rsrc_t r, int byte_off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, byte_off, 0, 0);
+  }
   __device__ static __forceinline__ float bits_to_f32(uint32_t b) {
     return __builtin_bit_cast(float, (uint32_t)(b & 0xffffu) << 16);
   }

@@ -28,17 +28,20 @@
 //         is NSLOT contiguous runs copied straight into LDS by direct-to-LDS
 //         loads (no registers, no arithmetic);
 //   * the input halo (HR rows x HC cols of one frame) is read
-//     row-contiguously and written channel-innermost as Xl[g][hr][hc][SE];
-//     taps outside the input are zero (this is the padding);
+//     row-contiguously -- as aligned 16-byte runs of one channel where the
+//     row length allows, else element by element -- and written
+//     channel-innermost as Xl[g][hr][col][SE]; taps outside the input are
+//     zero (this is the padding);
 //   * the stage's slots are consumed in pairs by one MFMA k-step (32x32x16
 //     f16/bf16: lanes 0-31 carry slot 2p, lanes 32-63 slot 2p+1) or by four
 //     (32x32x2 f32, one element of each slot per step).  Both operands of a
 //     slot are single 16-byte LDS reads.
-// LDS holds two stages; the global loads of stage s+1 are in flight while
-// stage s is multiplied.  Each lane's load offsets are computed once; the
-// per-stage part of every address is wave-uniform and moves the base of the
-// buffer descriptor (scalar arithmetic), so staging costs almost no vector
-// arithmetic and every access stays range-checked.
+// While stage s is multiplied, the reads of stage s+2 into registers and the
+// direct-to-LDS copy of stage s+1's packed weights (which come from L2) are
+// in flight; LDS holds two stages.  Each lane's load offsets are computed
+// once; the per-stage part of every address is wave-uniform and moves the
+// base of the buffer descriptor (scalar arithmetic), so staging costs almost
+// no vector arithmetic and every access stays range-checked.
 //
 // Epilogue (shared with the direct kernel): fp32 accumulator + bias ->
 // optional ReLU -> one round-to-nearest-even conversion -> store, with the
@@ -52,7 +55,9 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kPackAlign = 128;   // output channels of packed weights are padded to this
-constexpr int kFar = 0x7ffffff0;  // offset past the end of every tensor (all are < 0x7fff0000 bytes)
+// Offset past the end of every tensor (all are below 0x7fff0000 bytes), with
+// room to add the offsets of a unit's 16-byte vectors without overflow.
+constexpr int kFar = 0x7ffff000;
 
 // One MFMA k-step over a pair of 16-byte slots.  KSUB is the number of
 // instructions a slot pair takes; step(.., k) issues sub-step k.
@@ -106,15 +111,17 @@ struct IgemmArgs {
   int chunks;         // ceil(C / CK)
   int kp;             // packed weights: output-channel stride (C_out rounded up)
   int co_tiles, row_tiles, col_tiles;
+  int co_group;       // output-channel tiles per group of the launch order
   uint32_t x_bytes, w_bytes, b_bytes, y_bytes;
 };
 
 template <int DT_, int KT_, int KH_, int KW_, int SH_, int SW_, int BM_, int TH_, int TW_,
-          int WM_, int WN_, int CG_, int PK_>
+          int WM_, int WN_, int CG_, int PK_, int VX_>
 struct Cfg {
   static constexpr int DT = DT_, KT = KT_, KH = KH_, KW = KW_, SH = SH_, SW = SW_;
   static constexpr int BM = BM_, TH = TH_, TW = TW_, WM = WM_, WN = WN_, CG = CG_;
   static constexpr bool PK = PK_ != 0;
+  static constexpr bool VX = VX_ != 0;
   static constexpr int EB = Elem<DT>::bytes;
   static constexpr int SE = Mma<DT>::SE;
   static constexpr int CK = CG * SE;
@@ -125,11 +132,17 @@ struct Cfg {
   static constexpr int BN = TH * TW;
   static constexpr int HR = (TH - 1) * SH + KH;
   static constexpr int HC = (TW - 1) * SW + KW;
-  static constexpr int XPLANE = HR * HC;           // halo pixels per channel group
+  // Input staging.  VX tiles read the halo as aligned runs of RUN pixels of
+  // one channel (one 16-byte read per channel and run); the halo rows are
+  // widened to whole runs, starting up to MAXSHIFT columns left of the first
+  // tap column.  Other tiles read one element per channel and pixel.
+  static constexpr int RUN = 16 / EB;
+  static constexpr int MAXSHIFT = (VX && KW > 1) ? RUN - 1 : 0;
+  static constexpr int XCOLS = VX ? (HC + MAXSHIFT + RUN - 1) / RUN * RUN : HC;
+  static constexpr int NRUN = XCOLS / RUN;
+  static constexpr int XPLANE = HR * XCOLS;        // halo pixels per channel group in LDS
   static constexpr int WBYTES = NSLOT * BM * 16;
   static constexpr int XBYTES = CG * XPLANE * 16;
-  static constexpr int BUF = WBYTES + XBYTES;
-  static constexpr int LDS = 2 * BUF;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int FA = WTM / 32, FB = WTN / 32;
   static constexpr int BPR = TW / 32;              // 32-pixel blocks per tile row
@@ -138,11 +151,19 @@ struct Cfg {
   static constexpr int WUNITS = PK ? 0 : BM * CG;
   static constexpr int WPASS = PK ? 0 : (WUNITS + kThreads - 1) / kThreads;
   // weight staging from packed weights: NSLOT runs of BM 16-byte vectors,
-  // moved as 1 KB chunks (one wave, one instruction each)
+  // moved as 1 KB chunks (one wave, one instruction each), NDMA per wave; when
+  // the chunks do not divide evenly, the spare copies read nothing (zeros)
+  // into a 1 KB scratch area at the end of LDS
   static constexpr int WCHUNKS = NSLOT * BM / 64;
-  // input staging: one unit = one halo pixel of one channel group
-  static constexpr int XUNITS = CG * XPLANE;
+  static constexpr int NDMA = (WCHUNKS + 3) / 4;
+  static constexpr int DMA_PAD = (PK && WCHUNKS % 4 != 0) ? 1024 : 0;
+  // LDS: two weight and two input buffers
+  static constexpr int LDS = 2 * WBYTES + 2 * XBYTES + DMA_PAD;
+  // input staging: one unit = one run (VX) or one halo pixel of one channel group
+  static constexpr int XUNITS = VX ? CG * HR * NRUN : CG * XPLANE;
   static constexpr int XPASS = (XUNITS + kThreads - 1) / kThreads;
+  // global reads into registers each wave issues per stage
+  static constexpr int REG_LOADS = XPASS * SE + WPASS * TS;
 
   static_assert(WM * WN == 4, "four waves");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
@@ -160,9 +181,55 @@ struct Cfg {
 // loads would make the wave wait for the loads before computing.
 template <class G>
 struct StageRegs {
+  using XE = typename Elem<G::DT>::raw_t;
   u32x4_t wv[G::WPASS > 0 ? G::WPASS : 1][G::TS];
-  uint32_t xe[G::XPASS][G::SE];
+  XE xe[G::VX ? 1 : G::XPASS][G::VX ? 1 : G::SE];       // one element per read
+  u32x4_t xr[G::VX ? G::XPASS : 1][G::VX ? G::SE : 1];  // one run per read
 };
+
+// Make a register's value opaque to the optimiser at this point.  Applied to
+// staged values right before they are repacked, it keeps the repacking (and
+// the wait for the loads) from being moved up next to the loads.
+template <class T>
+__device__ __forceinline__ void pin(T& v) {
+  asm volatile("" : "+v"(v));
+}
+
+// f(std::integral_constant<int, i>) for i = B .. E-1, unrolled at compile time.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Wait until at most N of this wave's global reads are outstanding (gfx9
+// s_waitcnt encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left
+// at their maxima, i.e. not waited for).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  constexpr int n = N > 63 ? 63 : N;
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for LDS hand-over: this wave's LDS writes complete, then
+// s_barrier.  Unlike __syncthreads() it does not wait for outstanding global
+// reads (those of later stages stay in flight); the "memory" clobber keeps the
+// compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One 16-byte global read per lane written straight into LDS: lane l's
+// vector lands at dst + 16 l (dst is wave-uniform).  Kept out of the generic
+// lambdas of the kernel: inside them the host pass drops the kernel's launch
+// stub.
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, unsigned char* dst,
+                                              int off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16,
+                                           off, 0, 0, 0);
+}
 
 // Slot vector of tap t from a unit's TS vectors: the unit holds
 // w[co][c0 .. c0+SE)[0 .. TS) with the tap index fastest; the slot wants the
@@ -215,19 +282,34 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
   const int hf = lane >> 5;   // which slot of the pair this lane carries
 
   // ---- tile coordinates; XCD-aware order: the hardware deals workgroups to
-  // the 8 XCDs round-robin, so consecutive logical tiles (same output-channel
-  // tile, neighbouring pixel tiles) are gathered onto one XCD and its L2.
+  // the 8 XCDs round-robin, so consecutive logical tiles are gathered onto one
+  // XCD and its L2.  Logical order: groups of co_group output-channel tiles
+  // (whose weights fit in L2 together); inside a group the output-channel
+  // tile varies fastest, so the tiles that read the same input pixels run
+  // side by side, then the pixel tile.
   const int G_ = gridDim.x;
   int bid = blockIdx.x;
   if ((G_ & 7) == 0) bid = (bid & 7) * (G_ >> 3) + (bid >> 3);
+  const int pix_tiles = a.col_tiles * a.row_tiles * a.OT * a.N;
+  const int full_groups = a.co_tiles / a.co_group;
+  int cot;
+  if (bid < full_groups * a.co_group * pix_tiles) {
+    const int gt = a.co_group * pix_tiles;
+    const int grp = bid / gt, rem = bid % gt;
+    cot = grp * a.co_group + rem % a.co_group;
+    bid = rem / a.co_group;
+  } else {
+    const int rem = bid - full_groups * a.co_group * pix_tiles;
+    const int last = a.co_tiles - full_groups * a.co_group;
+    cot = full_groups * a.co_group + rem % last;
+    bid = rem / last;
+  }
   const int ctile = bid % a.col_tiles;
   bid /= a.col_tiles;
   const int rtile = bid % a.row_tiles;
   bid /= a.row_tiles;
   const int ot = bid % a.OT;
-  bid /= a.OT;
-  const int n = bid % a.N;
-  const int cot = bid / a.N;
+  const int n = bid / a.OT;
   const int co0 = cot * G::BM;
   const int oh0 = rtile * G::TH;
   const int ow0 = ctile * G::TW;
@@ -249,22 +331,42 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
   // of every address is wave-uniform: it moves the base of the buffer
   // descriptor (scalar arithmetic), while the range check keeps covering
   // every access up to the end of the tensor.
-  // input halo unit u = (g * HR + hr) * HC + hc, channel j of its group
-  int xoff[G::XPASS][SE];                // kFar when the position is padding
+  // VX: halo unit u = (g * HR + hr) * NRUN + run, one offset per unit (the
+  // channel j of its group is added as the scalar offset j * plane).  The
+  // runs start at a multiple of RUN columns, `shift` columns left of the
+  // first tap column; with W a multiple of RUN a run lies wholly inside or
+  // wholly outside the row.
+  // Otherwise: unit u = (g * HR + hr) * HC + hc, one offset per channel.
+  const int shift = G::VX ? (iw0 & (G::RUN - 1)) : 0;
+  int xoff[G::VX ? 1 : G::XPASS][G::VX ? 1 : SE];  // kFar when the position is padding
+  int xv[G::VX ? G::XPASS : 1];
   int xgrp[G::XPASS];
 #pragma unroll
   for (int i = 0; i < G::XPASS; ++i) {
     const int u = tid + i * kThreads;
-    const int hc = u % G::HC;
-    const int hr = (u / G::HC) % G::HR;
-    const int g = u / (G::HC * G::HR);
-    const int ih = ih0 + hr, iw = iw0 + hc;
-    const bool ok = u < G::XUNITS && (unsigned)ih < (unsigned)a.H && (unsigned)iw < (unsigned)a.W;
+    if constexpr (G::VX) {
+      const int run = u % G::NRUN;
+      const int hr = (u / G::NRUN) % G::HR;
+      const int g = u / (G::NRUN * G::HR);
+      const int ih = ih0 + hr, iw = iw0 - shift + run * G::RUN;
+      const bool ok =
+          u < G::XUNITS && (unsigned)ih < (unsigned)a.H && (unsigned)iw < (unsigned)a.W;
+      xv[i] = guard_offset(true, ok ? (g * SE * plane + ih * a.W + iw) * EB : kFar);
+      xgrp[i] = g;
+    } else {
+      const int hc = u % G::HC;
+      const int hr = (u / G::HC) % G::HR;
+      const int g = u / (G::HC * G::HR);
+      const int ih = ih0 + hr, iw = iw0 + hc;
+      const bool ok =
+          u < G::XUNITS && (unsigned)ih < (unsigned)a.H && (unsigned)iw < (unsigned)a.W;
 #pragma unroll
-    for (int j = 0; j < SE; ++j)
-      xoff[i][j] = guard_offset(true, ok ? ((g * SE + j) * plane + ih * a.W + iw) * EB : kFar);
-    xgrp[i] = g;
+      for (int j = 0; j < SE; ++j)
+        xoff[i][j] = guard_offset(true, ok ? ((g * SE + j) * plane + ih * a.W + iw) * EB : kFar);
+      xgrp[i] = g;
+    }
   }
+  const int ch_bytes = plane * EB;       // scalar offset between channels
   // OIHW weight unit u = g * BM + col
   int woff[G::WPASS > 0 ? G::WPASS : 1];
   int wgrp[G::WPASS > 0 ? G::WPASS : 1];
@@ -279,48 +381,97 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
   }
   const int n_base = n * a.C * plane * EB;
 
-  // Issue the global reads of stage (chunk, kt): packed weights straight into
-  // LDS buffer `buf`, everything else into registers.
-  auto load_stage = [&](int chunk, int kt, StageRegs<G>& r, unsigned char* buf) {
-    const int ci0 = chunk * G::CK;
-    const bool full = ci0 + G::CK <= a.C;  // uniform: no channel of the stage is past C
+  // The global reads of a stage, as pieces of one instruction each that are
+  // spread over the MFMA work of an earlier stage: pieces [0, NWP) read the
+  // weights (packed ones straight into the LDS weight buffer `wdst`, OIHW ones
+  // into registers), pieces [NWP, NWP + NXP) the input into registers.  When
+  // C is a multiple of the stage's channel count (`ragged` false) every
+  // channel exists and the reads are unguarded; otherwise every read is
+  // guarded per channel.
+  constexpr int NWP = G::PK ? G::NDMA : G::WPASS * G::TS;
+  constexpr int NXP = G::XPASS * SE;
+  struct Src {  // wave-uniform addressing of one stage
+    __amdgpu_buffer_rsrc_t rs;  // input or OIHW weights, based at the stage's first channel
+    int ci0;
+    int wrun;                   // packed weights: first 16-byte entry of the stage's slots
+  };
+  auto w_src = [&](int chunk, int kt) -> Src {
+    Src q;
+    q.ci0 = chunk * G::CK;
+    if constexpr (G::PK) {
+      q.rs = wr;
+      q.wrun = (chunk * G::CG * G::TS + kt * G::TS2) * a.kp + co0;
+    } else {
+      const int sb = q.ci0 * G::TS * EB;
+      q.rs = make_rsrc((const char*)a.w + sb, a.w_bytes - sb);
+      q.wrun = 0;
+    }
+    return q;
+  };
+  auto x_src = [&](int chunk, int kt) -> Src {
+    Src q;
+    q.ci0 = chunk * G::CK;
+    const int sb = n_base + (q.ci0 * plane + (it0 + kt) * hw) * EB;
+    q.rs = make_rsrc((const char*)a.x + sb, a.x_bytes - sb);
+    q.wrun = 0;
+    return q;
+  };
+  auto read_w = [&](auto ragged, auto kc, const Src& q, StageRegs<G>& r, unsigned char* wdst)
+      __attribute__((always_inline)) {
+    constexpr int k = decltype(kc)::value;
     if constexpr (G::PK) {
       // chunk c = 64 channels of one slot; lane l lands at chunk base + 16 l
-      for (int c = wave; c < G::WCHUNKS; c += kThreads / 64) {
-        const int slot = c / (G::BM / 64), part = c % (G::BM / 64);
-        const int t2 = slot / G::CG, g = slot % G::CG;
-        const int run = ((chunk * G::CG + g) * G::TS + kt * G::TS2 + t2) * a.kp + co0 + part * 64;
-        unsigned char* dst = buf + (slot * G::BM + part * 64) * 16;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (__attribute__((address_space(3))) void*)dst,
-                                                 16, (run + lane) * 16, 0, 0, 0);
-      }
+      const int c = wave + k * (kThreads / 64);
+      const int slot = c / (G::BM / 64), part = c % (G::BM / 64);
+      const int t2 = slot / G::CG, g = slot % G::CG;
+      const int run = q.wrun + (g * G::TS + t2) * a.kp + part * 64;
+      const bool real = c < G::WCHUNKS;  // wave-uniform
+      unsigned char* dst = real ? wdst + (slot * G::BM + part * 64) * 16 : lds + G::LDS - 1024;
+      copy16_to_lds(q.rs, dst, guard_offset(true, real ? (run + lane) * 16 : kFar));
     } else {
-      const int sb = ci0 * G::TS * EB;
-      const __amdgpu_buffer_rsrc_t ws = make_rsrc((const char*)a.w + sb, a.w_bytes - sb);
-#pragma unroll
-      for (int i = 0; i < G::WPASS; ++i) {
-        int v = woff[i];
-        if (!full && ci0 + wgrp[i] * SE >= a.C) v = guard_offset(true, kFar);
-#pragma unroll
-        for (int k = 0; k < G::TS; ++k)
-          r.wv[i][k] = __builtin_bit_cast(
-              u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ws, v + k * 16, 0, 0));
-      }
+      constexpr int i = k / G::TS, t = k % G::TS;
+      int v = woff[i];
+      if constexpr (decltype(ragged)::value)
+        v = guard_offset(true, q.ci0 + wgrp[i] * SE < a.C ? v : kFar);
+      r.wv[i][t] = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(q.rs, v + t * 16, 0, 0));
     }
-    const int sb = n_base + (ci0 * plane + (it0 + kt) * hw) * EB;
-    const __amdgpu_buffer_rsrc_t xs = make_rsrc((const char*)a.x + sb, a.x_bytes - sb);
-#pragma unroll
-    for (int i = 0; i < G::XPASS; ++i) {
-#pragma unroll
-      for (int j = 0; j < SE; ++j) {
-        int v = xoff[i][j];
-        if (!full && ci0 + xgrp[i] * SE + j >= a.C) v = guard_offset(true, kFar);
-        r.xe[i][j] = E::load_bits(xs, v);
-      }
+  };
+  auto read_x = [&](auto ragged, auto kc, const Src& q, StageRegs<G>& r)
+      __attribute__((always_inline)) {
+    constexpr int k = decltype(kc)::value;
+    constexpr int i = k / SE, j = k % SE;
+    constexpr bool rg = decltype(ragged)::value;
+    if constexpr (G::VX) {
+      int v = xv[i];
+      if constexpr (rg) v = guard_offset(true, q.ci0 + xgrp[i] * SE + j < a.C ? v : kFar);
+      r.xr[i][j] = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(q.rs, v, j * ch_bytes, 0));
+    } else {
+      int v = xoff[i][j];
+      if constexpr (rg) v = guard_offset(q.ci0 + xgrp[i] * SE + j < a.C, v);
+      r.xe[i][j] = E::load_raw(q.rs, v);
     }
   };
 
-  auto store_stage = [&](const StageRegs<G>& r, unsigned char* buf) {
+  // Registers of a stage -> LDS (weights into `wdst` unless they were copied
+  // there directly, the input halo into `xdst`).
+  auto store_stage = [&](StageRegs<G>& r, unsigned char* wdst, unsigned char* xdst)
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < G::WPASS; ++i)
+#pragma unroll
+      for (int k = 0; k < G::TS; ++k) pin(r.wv[i][k]);
+#pragma unroll
+    for (int i = 0; i < G::XPASS; ++i)
+#pragma unroll
+      for (int j = 0; j < SE; ++j) {
+        if constexpr (G::VX) {
+          pin(r.xr[i][j]);
+        } else {
+          pin(r.xe[i][j]);
+        }
+      }
     // weights from OIHW: [ci][tap] per unit -> Wl[slot = tap * CG + g][co][SE];
     // lanes of a wave hold consecutive channels, so each 16-byte store is
     // conflict-free
@@ -328,22 +479,39 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
     for (int i = 0; i < G::WPASS; ++i) {
       const int u = tid + i * kThreads;
       if (u < G::WUNITS)
-        store_slots<SE, G::TS, 0>(buf + ((u / G::BM) * G::BM + u % G::BM) * 16,
+        store_slots<SE, G::TS, 0>(wdst + ((u / G::BM) * G::BM + u % G::BM) * 16,
                                   G::CG * G::BM * 16, r.wv[i]);
     }
-    // input halo: pack the SE channels of each unit into one 16-byte word
-    unsigned char* xbuf = buf + G::WBYTES;
+    // input halo: gather the SE channels of each pixel into one 16-byte word
 #pragma unroll
     for (int i = 0; i < G::XPASS; ++i) {
       const int u = tid + i * kThreads;
-      const uint32_t* e = r.xe[i];
-      u32x4_t v;
-      if constexpr (SE == 8)
-        v = u32x4_t{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
-                    e[6] | (e[7] << 16)};
-      else
-        v = u32x4_t{e[0], e[1], e[2], e[3]};
-      if (u < G::XUNITS) *reinterpret_cast<u32x4_t*>(xbuf + u * 16) = v;
+      if constexpr (G::VX) {
+        // run u covers LDS pixels 4u .. 4u+3 of its group
+#pragma unroll
+        for (int q = 0; q < G::RUN; ++q) {
+          u32x4_t v;
+          if constexpr (SE == 8) {
+            const uint32_t sel = (q & 1) ? 0x07060302u : 0x05040100u;  // high or low halves
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+              v[m] = __builtin_amdgcn_perm(r.xr[i][2 * m + 1][q >> 1], r.xr[i][2 * m][q >> 1], sel);
+          } else {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) v[m] = r.xr[i][m][q];
+          }
+          if (u < G::XUNITS) *reinterpret_cast<u32x4_t*>(xdst + (u * G::RUN + q) * 16) = v;
+        }
+      } else {
+        const auto* e = r.xe[i];
+        u32x4_t v;
+        if constexpr (SE == 8)
+          v = u32x4_t{e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16),
+                      e[4] | ((uint32_t)e[5] << 16), e[6] | ((uint32_t)e[7] << 16)};
+        else
+          v = u32x4_t{e[0], e[1], e[2], e[3]};
+        if (u < G::XUNITS) *reinterpret_cast<u32x4_t*>(xdst + u * 16) = v;
+      }
     }
   };
 
@@ -355,8 +523,8 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
   const int prow0 = blk0 / G::BPR, pcol0 = (blk0 % G::BPR) * 32;
   // A: Wl[slot][co][16 B]; lanes of half hf read slot 2p + hf.
   const int a_lane = ((hf * G::BM) + co_w0 + il) * 16;
-  // B: Xl[g][hr][hc][16 B] at the lane's pixel.
-  const int b_lane = ((prow0 * G::SH) * G::HC + (pcol0 + il) * G::SW) * 16;
+  // B: Xl[g][hr][col][16 B] at the lane's pixel (col = hc + shift).
+  const int b_lane = ((prow0 * G::SH) * G::XCOLS + (pcol0 + il) * G::SW + shift) * 16;
 
   float16_t acc[G::FA][G::FB];
 #pragma unroll
@@ -371,18 +539,19 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
     const int tap = s / G::CG, g = s % G::CG;
     const int kh = tap / G::KW;
     const int kw = tap % G::KW;
-    return ((g * G::HR + kh) * G::HC + kw) * 16;
+    return ((g * G::HR + kh) * G::XCOLS + kw) * 16;
   };
   // byte offset of block j of this wave relative to its first block
   auto xblock = [&](int j) -> int {
     const int b = blk0 + j;
     const int r = b / G::BPR, c = (b % G::BPR) * 32;
-    return ((r - prow0) * G::SH * G::HC + (c - pcol0) * G::SW) * 16;
+    return ((r - prow0) * G::SH * G::XCOLS + (c - pcol0) * G::SW) * 16;
   };
 
-  auto compute = [&](const unsigned char* buf) {
-    const unsigned char* wl = buf;
-    const unsigned char* xl = buf + G::WBYTES;
+  // The MFMA work of one stage; hook(p) runs before the MFMAs of slot pair p
+  // (it issues pieces of later stages' reads).
+  auto compute = [&](const unsigned char* wl, const unsigned char* xl, auto&& hook)
+      __attribute__((always_inline)) {
     u32x4_t fa[2][G::FA], fb[2][G::FB];
     auto load_frags = [&](int p, int k) {
       const int s0 = 2 * p;
@@ -403,9 +572,14 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
       }
     };
     load_frags(0, 0);
-#pragma unroll
-    for (int p = 0; p < G::NPAIR; ++p) {
-      if (p + 1 < G::NPAIR) load_frags(p + 1, (p + 1) & 1);
+    static_for<0, G::NPAIR>([&](auto pc) {
+      constexpr int p = decltype(pc)::value;
+      if constexpr (p + 1 < G::NPAIR) load_frags(p + 1, (p + 1) & 1);
+      hook(pc);
+      // keep the next pair's LDS reads (and the hook's global reads) ahead of
+      // this pair's MFMAs: left alone, the scheduler sinks them below the
+      // MFMAs and every pair waits out the LDS latency
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int k = 0; k < Mma<G::DT>::KSUB; ++k)
 #pragma unroll
@@ -413,34 +587,94 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
 #pragma unroll
           for (int j = 0; j < G::FB; ++j)
             Mma<G::DT>::step(fa[p & 1][i], fb[p & 1][j], acc[i][j], k);
-    }
+    });
   };
 
-  // ---- main loop over stages (chunk, kt), chunk-major: two LDS buffers,
-  // the next stage's global reads in flight during the current MFMAs
-  if (nstages > 0) {
-    StageRegs<G> regs;
-    int chunk = 0, kt = kt_lo;
-    load_stage(chunk, kt, regs, lds);
-    store_stage(regs, lds);
-    __builtin_amdgcn_s_waitcnt(0);  // direct-to-LDS copies are counted as loads
-    __syncthreads();
-    for (int s = 0; s < nstages; ++s) {
-      unsigned char* cur = lds + (s & 1) * G::BUF;
-      unsigned char* nxt = lds + ((s + 1) & 1) * G::BUF;
-      const bool more = s + 1 < nstages;
-      if (more) {
-        if (++kt == kt_hi) {
-          kt = kt_lo;
-          ++chunk;
-        }
-        load_stage(chunk, kt, regs, nxt);
+  // ---- main loop over stages (chunk, kt), chunk-major.  Stage s+1 is written
+  // to LDS after stage s's MFMAs, then one barrier hands it over.
+  auto wbuf = [&](int i) -> unsigned char* { return lds + i * G::WBYTES; };
+  auto xbuf = [&](int i) -> unsigned char* { return lds + 2 * G::WBYTES + i * G::XBYTES; };
+  // Stage s: packed weights are copied into LDS one stage ahead (they are
+  // read from L2), everything else goes through registers two stages ahead.
+  // Every step issues the same instructions, so that the compiler can track
+  // the outstanding reads exactly: past the last stage the reads repeat the
+  // last stage into buffers nobody reads again.
+  struct Cursor {
+    int chunk, kt, idx;
+  };
+  auto advance = [&](Cursor& c) {
+    if (c.idx + 1 < nstages) {
+      ++c.idx;
+      if (++c.kt == kt_hi) {
+        c.kt = kt_lo;
+        ++c.chunk;
       }
-      compute(cur);
-      if (more) store_stage(regs, nxt);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
     }
+  };
+  auto main_loop = [&](auto ragged) __attribute__((always_inline)) {
+    StageRegs<G> ra, rb;
+    Cursor cw{0, kt_lo, 0}, cx{0, kt_lo, 0};  // next stage to read: weights, input
+    // all reads of the stage at cursor cx (and, for packed weights, of the
+    // stage at cw) at once
+    auto read_all = [&](StageRegs<G>& r, unsigned char* wdst) __attribute__((always_inline)) {
+      const Src qw = G::PK ? w_src(cw.chunk, cw.kt) : w_src(cx.chunk, cx.kt);
+      const Src qx = x_src(cx.chunk, cx.kt);
+      static_for<0, NWP>([&](auto kc) { read_w(ragged, kc, qw, r, wdst); });
+      static_for<0, NXP>([&](auto kc) { read_x(ragged, kc, qx, r); });
+      if constexpr (G::PK) advance(cw);
+      advance(cx);
+    };
+    if constexpr (G::PK) {
+      read_all(ra, wbuf(0));              // weights of stage 0, input of stage 0
+      const Src qx = x_src(cx.chunk, cx.kt);
+      static_for<0, NXP>([&](auto kc) { read_x(ragged, kc, qx, rb); });  // input of stage 1
+      advance(cx);
+    } else {
+      read_all(ra, nullptr);
+      read_all(rb, nullptr);
+    }
+    wait_vmcnt<G::REG_LOADS>();
+    store_stage(ra, wbuf(0), xbuf(0));
+    lds_barrier();
+    // Stage s: `mine` is free and receives the input (and OIHW weights) of
+    // stage s+2, packed weights of stage s+1 go to the free LDS weight
+    // buffer; `other` holds stage s+1.  The reads are spread over the slot
+    // pairs, weights first.
+    auto step = [&](int s, StageRegs<G>& mine, StageRegs<G>& other)
+        __attribute__((always_inline)) {
+      const Src qw = G::PK ? w_src(cw.chunk, cw.kt) : w_src(cx.chunk, cx.kt);
+      const Src qx = x_src(cx.chunk, cx.kt);
+      unsigned char* wdst = wbuf((s + 1) & 1);
+      compute(wbuf(s & 1), xbuf(s & 1), [&](auto pc) {
+        constexpr int p = decltype(pc)::value;
+        constexpr int lo = p * (NWP + NXP) / G::NPAIR, hi = (p + 1) * (NWP + NXP) / G::NPAIR;
+        static_for<lo, hi>([&](auto kc) {
+          constexpr int k = decltype(kc)::value;
+          if constexpr (k < NWP)
+            read_w(ragged, kc, qw, mine, wdst);
+          else
+            read_x(ragged, std::integral_constant<int, k - NWP>{}, qx, mine);
+        });
+      });
+      if constexpr (G::PK) advance(cw);
+      advance(cx);
+      wait_vmcnt<G::REG_LOADS>();
+      store_stage(other, wbuf((s + 1) & 1), xbuf((s + 1) & 1));
+      lds_barrier();
+    };
+    int s = 0;
+    for (; s + 1 < nstages; s += 2) {
+      step(s, ra, rb);
+      step(s + 1, rb, ra);
+    }
+    if (s < nstages) step(s, ra, rb);
+    wait_vmcnt<0>();  // no copy into LDS may outlive the workgroup
+  };
+  if (nstages > 0) {
+    if (a.C % G::CK == 0)
+      main_loop(std::false_type{});
+    else
+      main_loop(std::true_type{});
   }
 
   // ---- epilogue
@@ -556,6 +790,7 @@ struct TileDesc {
   int flat;       // 1: 1x1 stride-1 pad-0 layer viewed as one long row per plane
   int BM, TH, TW, CG;
   int packed;     // 1: reads packed weights
+  int vx;         // 1: reads the input as aligned 16-byte runs (W a multiple of the run)
   int eff;        // fraction of MFMA peak one CU reaches on this tile, in percent
                   // (measured on MI355X on large grids; used to rank tiles)
   int lds;
@@ -566,52 +801,61 @@ struct TileDesc {
 // Launcher of a tile for one storage dtype, or null when the tile's operand
 // width does not match the dtype.
 template <int DT, int WIDE, int KT, int KH, int KW, int SH, int SW, int BM, int TH, int TW,
-          int WM, int WN, int CG, int PK>
+          int WM, int WN, int CG, int PK, int VX>
 constexpr LaunchFn launcher() {
   if constexpr ((DT == DT_F32) == (WIDE == 0))
-    return &launch_cfg<Cfg<DT, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK>>;
+    return &launch_cfg<Cfg<DT, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK, VX>>;
   else
     return nullptr;
 }
 
-#define LIBCONV_TILE(ID, WIDE, KT, KH, KW, SH, SW, FLAT, BM, TH, TW, WM, WN, CG, PK, EFF, NAME) \
-  {ID, WIDE, KT, KH, KW, SH, SW, FLAT, BM, TH, TW, CG, PK, EFF,                                  \
-   Cfg<WIDE ? DT_F16 : DT_F32, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK>::LDS, NAME,  \
-   {launcher<DT_F32, WIDE, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK>(),               \
-    launcher<DT_F16, WIDE, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK>(),               \
-    launcher<DT_BF16, WIDE, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK>()}}
+#define LIBCONV_TILE(ID, WIDE, KT, KH, KW, SH, SW, FLAT, BM, TH, TW, WM, WN, CG, PK, VX, EFF,   \
+                     NAME)                                                                      \
+  {ID, WIDE, KT, KH, KW, SH, SW, FLAT, BM, TH, TW, CG, PK, VX, EFF,                              \
+   Cfg<WIDE ? DT_F16 : DT_F32, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK, VX>::LDS, NAME, \
+   {launcher<DT_F32, WIDE, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK, VX>(),               \
+    launcher<DT_F16, WIDE, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK, VX>(),               \
+    launcher<DT_BF16, WIDE, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK, VX>()}}
 
 const TileDesc kTiles[] = {
     // 16-bit operands, 3x3 stride 1, weights transposed in the kernel
-    LIBCONV_TILE(200, 1, 1, 3, 3, 1, 1, 0, 128, 8, 32, 2, 2, 2, 0, 20, "igemm16_k3s1_m128_n8x32"),
-    LIBCONV_TILE(201, 1, 1, 3, 3, 1, 1, 0, 128, 4, 32, 2, 2, 2, 0, 17, "igemm16_k3s1_m128_n4x32"),
-    LIBCONV_TILE(202, 1, 1, 3, 3, 1, 1, 0, 128, 2, 64, 2, 2, 2, 0, 14, "igemm16_k3s1_m128_n2x64"),
-    LIBCONV_TILE(203, 1, 1, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 0, 28, "igemm16_k3s1_m64_n8x32"),
+    LIBCONV_TILE(200, 1, 1, 3, 3, 1, 1, 0, 128, 8, 32, 2, 2, 2, 0, 1, 20, "igemm16_k3s1_m128_n8x32"),
+    LIBCONV_TILE(201, 1, 1, 3, 3, 1, 1, 0, 128, 4, 32, 2, 2, 2, 0, 1, 17, "igemm16_k3s1_m128_n4x32"),
+    LIBCONV_TILE(202, 1, 1, 3, 3, 1, 1, 0, 128, 2, 64, 2, 2, 2, 0, 1, 14, "igemm16_k3s1_m128_n2x64"),
+    LIBCONV_TILE(203, 1, 1, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 0, 1, 28, "igemm16_k3s1_m64_n8x32"),
+    LIBCONV_TILE(205, 1, 1, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 0, 0, 18, "igemm16_k3s1_m64_n8x32_e"),
     // 16-bit operands, 3x3 stride 2
-    LIBCONV_TILE(210, 1, 1, 3, 3, 2, 2, 0, 64, 4, 32, 2, 2, 2, 0, 20, "igemm16_k3s2_m64_n4x32"),
+    LIBCONV_TILE(210, 1, 1, 3, 3, 2, 2, 0, 64, 4, 32, 2, 2, 2, 0, 1, 20, "igemm16_k3s2_m64_n4x32"),
+    LIBCONV_TILE(215, 1, 1, 3, 3, 2, 2, 0, 64, 4, 32, 2, 2, 2, 0, 0, 13, "igemm16_k3s2_m64_n4x32_e"),
     // 16-bit operands, 1x1 stride 1 pad 0 (flattened planes)
-    LIBCONV_TILE(220, 1, 1, 1, 1, 1, 1, 1, 128, 1, 256, 2, 2, 8, 0, 20, "igemm16_k1_m128_n256"),
-    LIBCONV_TILE(221, 1, 1, 1, 1, 1, 1, 1, 128, 1, 128, 2, 2, 8, 0, 20, "igemm16_k1_m128_n128"),
+    LIBCONV_TILE(220, 1, 1, 1, 1, 1, 1, 1, 128, 1, 256, 2, 2, 8, 0, 1, 20, "igemm16_k1_m128_n256"),
+    LIBCONV_TILE(221, 1, 1, 1, 1, 1, 1, 1, 128, 1, 128, 2, 2, 8, 0, 1, 20, "igemm16_k1_m128_n128"),
+    LIBCONV_TILE(225, 1, 1, 1, 1, 1, 1, 1, 128, 1, 128, 2, 2, 8, 0, 0, 13, "igemm16_k1_m128_n128_e"),
     // fp32 operands
-    LIBCONV_TILE(240, 0, 1, 3, 3, 1, 1, 0, 32, 8, 32, 1, 4, 4, 0, 50, "igemm32_k3s1_m32_n8x32"),
-    LIBCONV_TILE(241, 0, 1, 3, 3, 1, 1, 0, 64, 4, 32, 2, 2, 4, 0, 40, "igemm32_k3s1_m64_n4x32"),
-    LIBCONV_TILE(242, 0, 1, 3, 3, 2, 2, 0, 64, 2, 32, 2, 2, 4, 0, 35, "igemm32_k3s2_m64_n2x32"),
-    LIBCONV_TILE(243, 0, 1, 1, 1, 1, 1, 1, 64, 1, 128, 2, 2, 8, 0, 15, "igemm32_k1_m64_n128"),
+    LIBCONV_TILE(240, 0, 1, 3, 3, 1, 1, 0, 32, 8, 32, 1, 4, 4, 0, 1, 50, "igemm32_k3s1_m32_n8x32"),
+    LIBCONV_TILE(241, 0, 1, 3, 3, 1, 1, 0, 64, 4, 32, 2, 2, 4, 0, 1, 40, "igemm32_k3s1_m64_n4x32"),
+    LIBCONV_TILE(242, 0, 1, 3, 3, 2, 2, 0, 64, 2, 32, 2, 2, 4, 0, 1, 35, "igemm32_k3s2_m64_n2x32"),
+    LIBCONV_TILE(243, 0, 1, 1, 1, 1, 1, 1, 64, 1, 128, 2, 2, 8, 0, 1, 15, "igemm32_k1_m64_n128"),
+    LIBCONV_TILE(250, 0, 1, 1, 1, 1, 1, 1, 64, 1, 128, 2, 2, 8, 0, 0, 10, "igemm32_k1_m64_n128_e"),
     // fp32, 8 channels per stage: small LDS stages, several workgroups per CU
-    LIBCONV_TILE(244, 0, 1, 3, 3, 1, 1, 0, 32, 8, 32, 1, 4, 2, 0, 48, "igemm32_k3s1_m32_n8x32_c8"),
-    LIBCONV_TILE(245, 0, 1, 3, 3, 2, 2, 0, 64, 2, 32, 2, 2, 2, 0, 44, "igemm32_k3s2_m64_n2x32_c8"),
-    LIBCONV_TILE(246, 0, 1, 3, 3, 2, 2, 0, 64, 4, 32, 2, 2, 2, 0, 44, "igemm32_k3s2_m64_n4x32_c8"),
-    LIBCONV_TILE(247, 0, 1, 3, 3, 1, 1, 0, 32, 4, 32, 1, 4, 2, 0, 48, "igemm32_k3s1_m32_n4x32_c8"),
+    LIBCONV_TILE(244, 0, 1, 3, 3, 1, 1, 0, 32, 8, 32, 1, 4, 2, 0, 1, 48, "igemm32_k3s1_m32_n8x32_c8"),
+    LIBCONV_TILE(245, 0, 1, 3, 3, 2, 2, 0, 64, 2, 32, 2, 2, 2, 0, 1, 44, "igemm32_k3s2_m64_n2x32_c8"),
+    LIBCONV_TILE(246, 0, 1, 3, 3, 2, 2, 0, 64, 4, 32, 2, 2, 2, 0, 1, 44, "igemm32_k3s2_m64_n4x32_c8"),
+    LIBCONV_TILE(247, 0, 1, 3, 3, 1, 1, 0, 32, 4, 32, 1, 4, 2, 0, 1, 48, "igemm32_k3s1_m32_n4x32_c8"),
+    LIBCONV_TILE(248, 0, 1, 3, 3, 1, 1, 0, 32, 8, 32, 1, 4, 2, 0, 0, 32, "igemm32_k3s1_m32_n8x32_c8_e"),
+    LIBCONV_TILE(249, 0, 1, 3, 3, 2, 2, 0, 64, 2, 32, 2, 2, 2, 0, 0, 29, "igemm32_k3s2_m64_n2x32_c8_e"),
     // packed weights: 16-bit, 3x3x3 stride 1 (one frame tap per stage)
-    LIBCONV_TILE(260, 1, 3, 3, 3, 1, 1, 0, 128, 8, 32, 2, 2, 2, 1, 30, "igemm16p_k333s1_m128_n8x32"),
-    LIBCONV_TILE(261, 1, 3, 3, 3, 1, 1, 0, 128, 4, 32, 2, 2, 2, 1, 23, "igemm16p_k333s1_m128_n4x32"),
-    LIBCONV_TILE(262, 1, 3, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 1, 33, "igemm16p_k333s1_m64_n8x32"),
-    LIBCONV_TILE(263, 1, 3, 3, 3, 1, 1, 0, 64, 4, 32, 1, 4, 2, 1, 30, "igemm16p_k333s1_m64_n4x32"),
-    LIBCONV_TILE(264, 1, 3, 3, 3, 1, 1, 0, 128, 8, 32, 2, 2, 1, 1, 24, "igemm16p_k333s1_m128_n8x32_c8"),
+    LIBCONV_TILE(260, 1, 3, 3, 3, 1, 1, 0, 128, 8, 32, 2, 2, 2, 1, 1, 30, "igemm16p_k333s1_m128_n8x32"),
+    LIBCONV_TILE(261, 1, 3, 3, 3, 1, 1, 0, 128, 4, 32, 2, 2, 2, 1, 1, 23, "igemm16p_k333s1_m128_n4x32"),
+    LIBCONV_TILE(262, 1, 3, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 1, 1, 33, "igemm16p_k333s1_m64_n8x32"),
+    LIBCONV_TILE(263, 1, 3, 3, 3, 1, 1, 0, 64, 4, 32, 1, 4, 2, 1, 1, 30, "igemm16p_k333s1_m64_n4x32"),
+    LIBCONV_TILE(264, 1, 3, 3, 3, 1, 1, 0, 128, 8, 32, 2, 2, 1, 1, 1, 24, "igemm16p_k333s1_m128_n8x32_c8"),
+    LIBCONV_TILE(265, 1, 3, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 1, 0, 22, "igemm16p_k333s1_m64_n8x32_e"),
     // packed weights: 16-bit, 3x3 stride 1
-    LIBCONV_TILE(270, 1, 1, 3, 3, 1, 1, 0, 128, 8, 32, 2, 2, 2, 1, 30, "igemm16p_k3s1_m128_n8x32"),
-    LIBCONV_TILE(271, 1, 1, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 1, 36, "igemm16p_k3s1_m64_n8x32"),
-    LIBCONV_TILE(272, 1, 1, 3, 3, 1, 1, 0, 128, 4, 32, 2, 2, 2, 1, 23, "igemm16p_k3s1_m128_n4x32"),
+    LIBCONV_TILE(270, 1, 1, 3, 3, 1, 1, 0, 128, 8, 32, 2, 2, 2, 1, 1, 30, "igemm16p_k3s1_m128_n8x32"),
+    LIBCONV_TILE(271, 1, 1, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 1, 1, 36, "igemm16p_k3s1_m64_n8x32"),
+    LIBCONV_TILE(272, 1, 1, 3, 3, 1, 1, 0, 128, 4, 32, 2, 2, 2, 1, 1, 23, "igemm16p_k3s1_m128_n4x32"),
+    LIBCONV_TILE(275, 1, 1, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 1, 0, 24, "igemm16p_k3s1_m64_n8x32_e"),
 };
 
 #undef LIBCONV_TILE
@@ -634,6 +878,13 @@ bool tile_fits(const TileDesc& t, const Problem& p) {
   // 16-byte weight vectors read from OIHW must not straddle channels; packed
   // weights are zero-padded to whole groups instead.
   if (!t.packed && p.C % se != 0) return false;
+  // 16-byte runs (8 pixels of a 16-bit type, 4 of fp32): rows (flattened
+  // planes for 1x1 tiles) of whole runs, and an input aligned for 16-byte reads
+  if (t.vx) {
+    const long long row = t.flat ? (long long)p.H * p.W : p.W;
+    if (row % (16 / dtype_bytes(p.dtype)) != 0 || (reinterpret_cast<uintptr_t>(p.x) & 15) != 0)
+      return false;
+  }
   if (t.flat) return is_flat(p);
   return p.KT == t.KT && p.KH == t.KH && p.KW == t.KW && p.sh == t.SH && p.sw == t.SW &&
          (t.KT > 1 || (p.st == 1 && p.pt == 0));
@@ -803,6 +1054,10 @@ libconv_status igemm_launch(const Problem& p, const Plan& plan) {
   a.kp = (p.K + kPackAlign - 1) / kPackAlign * kPackAlign;
   a.co_tiles = (int)c.co; a.row_tiles = (int)c.rows; a.col_tiles = (int)c.cols;
   const int eb = dtype_bytes(p.dtype);
+  // as many output-channel tiles side by side as keep their weights within
+  // about 2 MB (half an XCD's L2)
+  const long long w_tile = (long long)t->BM * p.C * p.KT * p.KH * p.KW * eb;
+  a.co_group = (int)std::max(1LL, std::min<long long>(c.co, (2LL << 20) / std::max(1LL, w_tile)));
   a.x_bytes = (uint32_t)((long long)p.N * p.C * p.T * p.H * p.W * eb);
   a.w_bytes = t->packed ? (uint32_t)packed_weight_bytes(p.C, p.K, p.KT, p.KH, p.KW, p.dtype)
                         : (uint32_t)((long long)p.K * p.C * p.KT * p.KH * p.KW * eb);

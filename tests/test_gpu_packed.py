@@ -52,15 +52,18 @@ def test_pack_layout(dt, C, K, ks):
 
 
 PACKED_CASES = [
-    # (tile, dims, dtype, N, C, spatial, K, relu)
+    # (tile, dims, dtype, N, C, spatial, K, relu); tiles reading 16-byte runs
+    # need W % 8 == 0, the "_e" tiles (265, 275) take any W
     (260, 3, "f16", 1, 16, (5, 9, 40), 128, False),
-    (261, 3, "bf16", 1, 24, (3, 7, 33), 200, True),    # C % 8 != 0 (zero-padded group)
-    (262, 3, "f16", 2, 8, (4, 10, 35), 64, False),
-    (263, 3, "bf16", 1, 40, (3, 6, 70), 96, True),
-    (264, 3, "f16", 1, 16, (2, 9, 37), 130, False),     # K % 128 != 0
+    (261, 3, "bf16", 1, 24, (3, 7, 48), 200, True),    # C % 8 != 0 (zero-padded group)
+    (262, 3, "f16", 2, 8, (4, 10, 56), 64, False),
+    (263, 3, "bf16", 1, 40, (3, 6, 72), 96, True),
+    (264, 3, "f16", 1, 16, (2, 9, 88), 130, False),     # K % 128 != 0
+    (265, 3, "bf16", 1, 20, (3, 9, 35), 72, True),      # odd W, C % 16 != 0
     (270, 2, "bf16", 1, 32, (11, 40), 128, True),
-    (271, 2, "f16", 2, 20, (9, 33), 72, False),        # C % 8 != 0, K % 64 != 0
-    (272, 2, "f16", 1, 64, (7, 70), 256, True),
+    (271, 2, "f16", 2, 20, (9, 48), 72, False),        # C % 8 != 0, K % 64 != 0
+    (272, 2, "f16", 1, 64, (7, 72), 256, True),
+    (275, 2, "f16", 1, 24, (9, 33), 64, False),        # odd W
 ]
 
 
