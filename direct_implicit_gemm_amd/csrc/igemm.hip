@@ -140,7 +140,12 @@ struct Cfg {
   static constexpr int MAXSHIFT = (VX && KW > 1) ? RUN - 1 : 0;
   static constexpr int XCOLS = VX ? (HC + MAXSHIFT + RUN - 1) / RUN * RUN : HC;
   static constexpr int NRUN = XCOLS / RUN;
-  static constexpr int XPLANE = HR * XCOLS;        // halo pixels per channel group in LDS
+  // LDS row pitch in 16-byte words.  A VX unit writes RUN consecutive words
+  // of one row; eight lanes side by side hold eight consecutive rows, and an
+  // odd pitch puts their words in eight different bank groups.
+  static constexpr int PITCH = VX ? XCOLS + 1 : XCOLS;
+  static constexpr int NROWS = CG * HR;            // halo rows of a stage (all groups)
+  static constexpr int XPLANE = HR * PITCH;        // LDS words per channel group
   static constexpr int WBYTES = NSLOT * BM * 16;
   static constexpr int XBYTES = CG * XPLANE * 16;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -159,8 +164,9 @@ struct Cfg {
   static constexpr int DMA_PAD = (PK && WCHUNKS % 4 != 0) ? 1024 : 0;
   // LDS: two weight and two input buffers
   static constexpr int LDS = 2 * WBYTES + 2 * XBYTES + DMA_PAD;
-  // input staging: one unit = one run (VX) or one halo pixel of one channel group
-  static constexpr int XUNITS = VX ? CG * HR * NRUN : CG * XPLANE;
+  // input staging: one unit = one run (VX) or one halo pixel of one channel
+  // group; VX units come in blocks of 8 rows x NRUN runs
+  static constexpr int XUNITS = VX ? (NROWS + 7) / 8 * 8 * NRUN : CG * HR * HC;
   static constexpr int XPASS = (XUNITS + kThreads - 1) / kThreads;
   // global reads into registers each wave issues per stage
   static constexpr int REG_LOADS = XPASS * SE + WPASS * TS;
@@ -331,11 +337,11 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
   // of every address is wave-uniform: it moves the base of the buffer
   // descriptor (scalar arithmetic), while the range check keeps covering
   // every access up to the end of the tensor.
-  // VX: halo unit u = (g * HR + hr) * NRUN + run, one offset per unit (the
-  // channel j of its group is added as the scalar offset j * plane).  The
-  // runs start at a multiple of RUN columns, `shift` columns left of the
-  // first tap column; with W a multiple of RUN a run lies wholly inside or
-  // wholly outside the row.
+  // VX: halo unit u holds run (u / 8) % NRUN of row 8 * (u / (8 * NRUN)) +
+  // u % 8, row = g * HR + hr; one offset per unit (the channel j of its group
+  // is added as the scalar offset j * plane).  The runs start at a multiple
+  // of RUN columns, `shift` columns left of the first tap column; with W a
+  // multiple of RUN a run lies wholly inside or wholly outside the row.
   // Otherwise: unit u = (g * HR + hr) * HC + hc, one offset per channel.
   const int shift = G::VX ? (iw0 & (G::RUN - 1)) : 0;
   int xoff[G::VX ? 1 : G::XPASS][G::VX ? 1 : SE];  // kFar when the position is padding
@@ -345,12 +351,13 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
   for (int i = 0; i < G::XPASS; ++i) {
     const int u = tid + i * kThreads;
     if constexpr (G::VX) {
-      const int run = u % G::NRUN;
-      const int hr = (u / G::NRUN) % G::HR;
-      const int g = u / (G::NRUN * G::HR);
+      const int run = (u >> 3) % G::NRUN;
+      const int row = (u >> 3) / G::NRUN * 8 + (u & 7);
+      const int hr = row % G::HR;
+      const int g = row / G::HR;
       const int ih = ih0 + hr, iw = iw0 - shift + run * G::RUN;
-      const bool ok =
-          u < G::XUNITS && (unsigned)ih < (unsigned)a.H && (unsigned)iw < (unsigned)a.W;
+      const bool ok = u < G::XUNITS && row < G::NROWS && (unsigned)ih < (unsigned)a.H &&
+                      (unsigned)iw < (unsigned)a.W;
       xv[i] = guard_offset(true, ok ? (g * SE * plane + ih * a.W + iw) * EB : kFar);
       xgrp[i] = g;
     } else {
@@ -487,7 +494,10 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
     for (int i = 0; i < G::XPASS; ++i) {
       const int u = tid + i * kThreads;
       if constexpr (G::VX) {
-        // run u covers LDS pixels 4u .. 4u+3 of its group
+        // unit u covers the RUN words of its run in its row
+        const int run = (u >> 3) % G::NRUN;
+        const int row = (u >> 3) / G::NRUN * 8 + (u & 7);
+        unsigned char* dst = xdst + (row * G::PITCH + run * G::RUN) * 16;
 #pragma unroll
         for (int q = 0; q < G::RUN; ++q) {
           u32x4_t v;
@@ -500,7 +510,7 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
 #pragma unroll
             for (int m = 0; m < 4; ++m) v[m] = r.xr[i][m][q];
           }
-          if (u < G::XUNITS) *reinterpret_cast<u32x4_t*>(xdst + (u * G::RUN + q) * 16) = v;
+          if (u < G::XUNITS && row < G::NROWS) *reinterpret_cast<u32x4_t*>(dst + q * 16) = v;
         }
       } else {
         const auto* e = r.xe[i];
@@ -523,8 +533,9 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
   const int prow0 = blk0 / G::BPR, pcol0 = (blk0 % G::BPR) * 32;
   // A: Wl[slot][co][16 B]; lanes of half hf read slot 2p + hf.
   const int a_lane = ((hf * G::BM) + co_w0 + il) * 16;
-  // B: Xl[g][hr][col][16 B] at the lane's pixel (col = hc + shift).
-  const int b_lane = ((prow0 * G::SH) * G::XCOLS + (pcol0 + il) * G::SW + shift) * 16;
+  // B: Xl[g][hr][col][16 B] (rows PITCH words apart) at the lane's pixel
+  // (col = hc + shift).
+  const int b_lane = ((prow0 * G::SH) * G::PITCH + (pcol0 + il) * G::SW + shift) * 16;
 
   float16_t acc[G::FA][G::FB];
 #pragma unroll
@@ -539,13 +550,13 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
     const int tap = s / G::CG, g = s % G::CG;
     const int kh = tap / G::KW;
     const int kw = tap % G::KW;
-    return ((g * G::HR + kh) * G::XCOLS + kw) * 16;
+    return ((g * G::HR + kh) * G::PITCH + kw) * 16;
   };
   // byte offset of block j of this wave relative to its first block
   auto xblock = [&](int j) -> int {
     const int b = blk0 + j;
     const int r = b / G::BPR, c = (b % G::BPR) * 32;
-    return ((r - prow0) * G::SH * G::XCOLS + (c - pcol0) * G::SW) * 16;
+    return ((r - prow0) * G::SH * G::PITCH + (c - pcol0) * G::SW) * 16;
   };
 
   // The MFMA work of one stage; hook(p) runs before the MFMAs of slot pair p
