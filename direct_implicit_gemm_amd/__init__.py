@@ -64,6 +64,8 @@ def load() -> ctypes.CDLL:
     lib.libconv_query_algo.restype = I
     lib.libconv_tile_name.argtypes = [I]
     lib.libconv_tile_name.restype = ctypes.c_char_p
+    lib.libconv_tile_occupancy.argtypes = [I, I, I]
+    lib.libconv_tile_occupancy.restype = I
     lib.libconv_out_size.argtypes = [I, I, I, I]
     lib.libconv_out_size.restype = I
     lib.libconv_status_string.argtypes = [I]
@@ -140,6 +142,10 @@ def libconv_query_algo(N, C_in, T, H, W, C_out, KT, KH, KW, pad_t, pad_h, pad_w,
 
 def libconv_tile_name(tile_id: int) -> str:
     return load().libconv_tile_name(tile_id).decode()
+
+
+def libconv_tile_occupancy(tile_id: int, dtype: int, measured: bool = False) -> int:
+    return load().libconv_tile_occupancy(tile_id, dtype, int(measured))
 
 
 def libconv_out_size(n_in: int, k: int, pad: int, stride: int) -> int:

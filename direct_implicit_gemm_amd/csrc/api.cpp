@@ -93,6 +93,7 @@ constexpr int kMaxDevices = 64;
 std::once_flag g_dev_once;
 int g_dev_count = 0;
 bool g_dev_ok[kMaxDevices];
+int g_dev_cus[kMaxDevices];
 
 void init_devices() {
   int n = 0;
@@ -102,6 +103,7 @@ void init_devices() {
     hipDeviceProp_t prop;
     g_dev_ok[d] = hipGetDeviceProperties(&prop, d) == hipSuccess &&
                   std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    g_dev_cus[d] = g_dev_ok[d] && prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
   }
   g_dev_count = n;
   (void)hipGetLastError();  // a host without GPUs leaves an error behind: clear it
@@ -127,6 +129,10 @@ libconv_status plan_for(const Problem& p, int algo, Plan* plan, bool packed_only
     Plan forced;
     if (igemm_plan_tile(p, std::atoi(ft), &forced) && algo != LIBCONV_ALGO_DIRECT &&
         (!packed_only || igemm_tile_packed(forced.tile))) {
+      *plan = forced;
+      return LIBCONV_OK;
+    }
+    if (!packed_only && algo != LIBCONV_ALGO_IGEMM && direct_plan_tile(p, std::atoi(ft), &forced)) {
       *plan = forced;
       return LIBCONV_OK;
     }
@@ -172,6 +178,7 @@ libconv_status run(Problem& p, int algo) {
     (void)hipGetLastError();
     return LIBCONV_ERR_NO_DEVICE;
   }
+  p.cus = g_dev_cus[dev];
   Plan plan;
   st = plan_for(p, algo, &plan, p.w == nullptr);
   if (st != LIBCONV_OK) return st;
@@ -214,6 +221,7 @@ Problem make_problem(const void* x, const void* w, const void* bias, void* y, in
   p.dtype = dtype; p.act = act;
   p.x = x; p.w = w; p.b = bias; p.y = y;
   p.stream = reinterpret_cast<hipStream_t>(stream);
+  p.cus = 256;  // MI355X; the device's own count replaces it before a launch
   return p;
 }
 
@@ -315,6 +323,17 @@ const char* libconv_tile_name(int tile_id) {
   const char* n = direct_tile_name(tile_id);
   if (!n) n = igemm_tile_name(tile_id);
   return n ? n : "?";
+}
+
+int libconv_tile_occupancy(int tile_id, int dtype, int measured) {
+  if (measured) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || !device_ok(dev)) {
+      (void)hipGetLastError();
+      return -1;
+    }
+  }
+  return igemm_tile_occupancy(tile_id, dtype, measured != 0);
 }
 
 int libconv_out_size(int in, int k, int pad, int stride) {

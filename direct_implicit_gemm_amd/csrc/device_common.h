@@ -32,6 +32,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
 // are below 2^31 bytes; offsets are unsigned 32-bit).
 constexpr int kOobOffset = -16;
 
+// An offset past the end of every tensor (all are below 0x7fff0000 bytes)
+// that stays past the end when a scalar offset below 2^31 is added to it
+// (the range check covers the sum, and it must not wrap around 2^32).
+constexpr int kFarOffset = 0x7ffff000;
+
 // `ok ? off : kOobOffset`, computed in a register the optimiser treats as
 // opaque.  Written as a plain select, the compiler may turn
 // load(select(c, a, b)) into two loads on two branches, and the join after

@@ -794,6 +794,20 @@ hipError_t launch_cfg(const IgemmArgs& a, unsigned grid, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Workgroups of a tile kernel one compute unit holds at once, from the
+// runtime (registers and LDS of the built kernel); -1 if the query fails.
+using OccFn = int (*)();
+template <class G>
+int occupancy_cfg() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, igemm_kernel<G>, kThreads, 0) !=
+      hipSuccess) {
+    (void)hipGetLastError();
+    return -1;
+  }
+  return n;
+}
+
 struct TileDesc {
   int id;
   int wide;       // 0: fp32 operands, 1: 16-bit operands
@@ -804,9 +818,12 @@ struct TileDesc {
   int vx;         // 1: reads the input as aligned 16-byte runs (W a multiple of the run)
   int eff;        // fraction of MFMA peak one CU reaches on this tile, in percent
                   // (measured on MI355X on large grids; used to rank tiles)
+  int occ;        // workgroups one CU holds at once (registers and LDS of the
+                  // built kernel; checked against the runtime by a GPU test)
   int lds;
   const char* name;
   LaunchFn fn[3];  // by libconv_dtype
+  OccFn occ_fn[3];
 };
 
 // Launcher of a tile for one storage dtype, or null when the tile's operand
@@ -819,54 +836,65 @@ constexpr LaunchFn launcher() {
   else
     return nullptr;
 }
+template <int DT, int WIDE, int KT, int KH, int KW, int SH, int SW, int BM, int TH, int TW,
+          int WM, int WN, int CG, int PK, int VX>
+constexpr OccFn occupier() {
+  if constexpr ((DT == DT_F32) == (WIDE == 0))
+    return &occupancy_cfg<Cfg<DT, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK, VX>>;
+  else
+    return nullptr;
+}
 
 #define LIBCONV_TILE(ID, WIDE, KT, KH, KW, SH, SW, FLAT, BM, TH, TW, WM, WN, CG, PK, VX, EFF,   \
-                     NAME)                                                                      \
-  {ID, WIDE, KT, KH, KW, SH, SW, FLAT, BM, TH, TW, CG, PK, VX, EFF,                              \
+                     OCC, NAME)                                                                 \
+  {ID, WIDE, KT, KH, KW, SH, SW, FLAT, BM, TH, TW, CG, PK, VX, EFF, OCC,                         \
    Cfg<WIDE ? DT_F16 : DT_F32, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK, VX>::LDS, NAME, \
    {launcher<DT_F32, WIDE, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK, VX>(),               \
     launcher<DT_F16, WIDE, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK, VX>(),               \
-    launcher<DT_BF16, WIDE, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK, VX>()}}
+    launcher<DT_BF16, WIDE, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK, VX>()},              \
+   {occupier<DT_F32, WIDE, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK, VX>(),               \
+    occupier<DT_F16, WIDE, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK, VX>(),               \
+    occupier<DT_BF16, WIDE, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK, VX>()}}
 
 const TileDesc kTiles[] = {
     // 16-bit operands, 3x3 stride 1, weights transposed in the kernel
-    LIBCONV_TILE(200, 1, 1, 3, 3, 1, 1, 0, 128, 8, 32, 2, 2, 2, 0, 1, 20, "igemm16_k3s1_m128_n8x32"),
-    LIBCONV_TILE(201, 1, 1, 3, 3, 1, 1, 0, 128, 4, 32, 2, 2, 2, 0, 1, 17, "igemm16_k3s1_m128_n4x32"),
-    LIBCONV_TILE(202, 1, 1, 3, 3, 1, 1, 0, 128, 2, 64, 2, 2, 2, 0, 1, 14, "igemm16_k3s1_m128_n2x64"),
-    LIBCONV_TILE(203, 1, 1, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 0, 1, 28, "igemm16_k3s1_m64_n8x32"),
-    LIBCONV_TILE(205, 1, 1, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 0, 0, 18, "igemm16_k3s1_m64_n8x32_e"),
+    LIBCONV_TILE(200, 1, 1, 3, 3, 1, 1, 0, 128, 8, 32, 2, 2, 2, 0, 1, 20, 1, "igemm16_k3s1_m128_n8x32"),
+    LIBCONV_TILE(201, 1, 1, 3, 3, 1, 1, 0, 128, 4, 32, 2, 2, 2, 0, 1, 17, 1, "igemm16_k3s1_m128_n4x32"),
+    LIBCONV_TILE(202, 1, 1, 3, 3, 1, 1, 0, 128, 2, 64, 2, 2, 2, 0, 1, 14, 1, "igemm16_k3s1_m128_n2x64"),
+    LIBCONV_TILE(203, 1, 1, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 0, 1, 28, 1, "igemm16_k3s1_m64_n8x32"),
+    LIBCONV_TILE(205, 1, 1, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 0, 0, 18, 1, "igemm16_k3s1_m64_n8x32_e"),
     // 16-bit operands, 3x3 stride 2
-    LIBCONV_TILE(210, 1, 1, 3, 3, 2, 2, 0, 64, 4, 32, 2, 2, 2, 0, 1, 20, "igemm16_k3s2_m64_n4x32"),
-    LIBCONV_TILE(215, 1, 1, 3, 3, 2, 2, 0, 64, 4, 32, 2, 2, 2, 0, 0, 13, "igemm16_k3s2_m64_n4x32_e"),
+    LIBCONV_TILE(210, 1, 1, 3, 3, 2, 2, 0, 64, 4, 32, 2, 2, 2, 0, 1, 20, 2, "igemm16_k3s2_m64_n4x32"),
+    LIBCONV_TILE(215, 1, 1, 3, 3, 2, 2, 0, 64, 4, 32, 2, 2, 2, 0, 0, 13, 1, "igemm16_k3s2_m64_n4x32_e"),
     // 16-bit operands, 1x1 stride 1 pad 0 (flattened planes)
-    LIBCONV_TILE(220, 1, 1, 1, 1, 1, 1, 1, 128, 1, 256, 2, 2, 8, 0, 1, 20, "igemm16_k1_m128_n256"),
-    LIBCONV_TILE(221, 1, 1, 1, 1, 1, 1, 1, 128, 1, 128, 2, 2, 8, 0, 1, 20, "igemm16_k1_m128_n128"),
-    LIBCONV_TILE(225, 1, 1, 1, 1, 1, 1, 1, 128, 1, 128, 2, 2, 8, 0, 0, 13, "igemm16_k1_m128_n128_e"),
+    LIBCONV_TILE(220, 1, 1, 1, 1, 1, 1, 1, 128, 1, 256, 2, 2, 8, 0, 1, 20, 1, "igemm16_k1_m128_n256"),
+    LIBCONV_TILE(221, 1, 1, 1, 1, 1, 1, 1, 128, 1, 128, 2, 2, 8, 0, 1, 20, 2, "igemm16_k1_m128_n128"),
+    LIBCONV_TILE(225, 1, 1, 1, 1, 1, 1, 1, 128, 1, 128, 2, 2, 8, 0, 0, 13, 2, "igemm16_k1_m128_n128_e"),
     // fp32 operands
-    LIBCONV_TILE(240, 0, 1, 3, 3, 1, 1, 0, 32, 8, 32, 1, 4, 4, 0, 1, 50, "igemm32_k3s1_m32_n8x32"),
-    LIBCONV_TILE(241, 0, 1, 3, 3, 1, 1, 0, 64, 4, 32, 2, 2, 4, 0, 1, 40, "igemm32_k3s1_m64_n4x32"),
-    LIBCONV_TILE(242, 0, 1, 3, 3, 2, 2, 0, 64, 2, 32, 2, 2, 4, 0, 1, 35, "igemm32_k3s2_m64_n2x32"),
-    LIBCONV_TILE(243, 0, 1, 1, 1, 1, 1, 1, 64, 1, 128, 2, 2, 8, 0, 1, 15, "igemm32_k1_m64_n128"),
-    LIBCONV_TILE(250, 0, 1, 1, 1, 1, 1, 1, 64, 1, 128, 2, 2, 8, 0, 0, 10, "igemm32_k1_m64_n128_e"),
+    LIBCONV_TILE(240, 0, 1, 3, 3, 1, 1, 0, 32, 8, 32, 1, 4, 4, 0, 1, 50, 1, "igemm32_k3s1_m32_n8x32"),
+    LIBCONV_TILE(241, 0, 1, 3, 3, 1, 1, 0, 64, 4, 32, 2, 2, 4, 0, 1, 40, 1, "igemm32_k3s1_m64_n4x32"),
+    LIBCONV_TILE(242, 0, 1, 3, 3, 2, 2, 0, 64, 2, 32, 2, 2, 4, 0, 1, 35, 1, "igemm32_k3s2_m64_n2x32"),
+    LIBCONV_TILE(243, 0, 1, 1, 1, 1, 1, 1, 64, 1, 128, 2, 2, 8, 0, 1, 15, 3, "igemm32_k1_m64_n128"),
+    LIBCONV_TILE(250, 0, 1, 1, 1, 1, 1, 1, 64, 1, 128, 2, 2, 8, 0, 0, 10, 3, "igemm32_k1_m64_n128_e"),
     // fp32, 8 channels per stage: small LDS stages, several workgroups per CU
-    LIBCONV_TILE(244, 0, 1, 3, 3, 1, 1, 0, 32, 8, 32, 1, 4, 2, 0, 1, 48, "igemm32_k3s1_m32_n8x32_c8"),
-    LIBCONV_TILE(245, 0, 1, 3, 3, 2, 2, 0, 64, 2, 32, 2, 2, 2, 0, 1, 44, "igemm32_k3s2_m64_n2x32_c8"),
-    LIBCONV_TILE(246, 0, 1, 3, 3, 2, 2, 0, 64, 4, 32, 2, 2, 2, 0, 1, 44, "igemm32_k3s2_m64_n4x32_c8"),
-    LIBCONV_TILE(247, 0, 1, 3, 3, 1, 1, 0, 32, 4, 32, 1, 4, 2, 0, 1, 48, "igemm32_k3s1_m32_n4x32_c8"),
-    LIBCONV_TILE(248, 0, 1, 3, 3, 1, 1, 0, 32, 8, 32, 1, 4, 2, 0, 0, 32, "igemm32_k3s1_m32_n8x32_c8_e"),
-    LIBCONV_TILE(249, 0, 1, 3, 3, 2, 2, 0, 64, 2, 32, 2, 2, 2, 0, 0, 29, "igemm32_k3s2_m64_n2x32_c8_e"),
+    LIBCONV_TILE(244, 0, 1, 3, 3, 1, 1, 0, 32, 8, 32, 1, 4, 2, 0, 1, 48, 2, "igemm32_k3s1_m32_n8x32_c8"),
+    LIBCONV_TILE(245, 0, 1, 3, 3, 2, 2, 0, 64, 2, 32, 2, 2, 2, 0, 1, 44, 2, "igemm32_k3s2_m64_n2x32_c8"),
+    LIBCONV_TILE(246, 0, 1, 3, 3, 2, 2, 0, 64, 4, 32, 2, 2, 2, 0, 1, 44, 2, "igemm32_k3s2_m64_n4x32_c8"),
+    LIBCONV_TILE(247, 0, 1, 3, 3, 1, 1, 0, 32, 4, 32, 1, 4, 2, 0, 1, 48, 2, "igemm32_k3s1_m32_n4x32_c8"),
+    LIBCONV_TILE(248, 0, 1, 3, 3, 1, 1, 0, 32, 8, 32, 1, 4, 2, 0, 0, 32, 2, "igemm32_k3s1_m32_n8x32_c8_e"),
+    LIBCONV_TILE(249, 0, 1, 3, 3, 2, 2, 0, 64, 2, 32, 2, 2, 2, 0, 0, 29, 2, "igemm32_k3s2_m64_n2x32_c8_e"),
     // packed weights: 16-bit, 3x3x3 stride 1 (one frame tap per stage)
-    LIBCONV_TILE(260, 1, 3, 3, 3, 1, 1, 0, 128, 8, 32, 2, 2, 2, 1, 1, 30, "igemm16p_k333s1_m128_n8x32"),
-    LIBCONV_TILE(261, 1, 3, 3, 3, 1, 1, 0, 128, 4, 32, 2, 2, 2, 1, 1, 23, "igemm16p_k333s1_m128_n4x32"),
-    LIBCONV_TILE(262, 1, 3, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 1, 1, 33, "igemm16p_k333s1_m64_n8x32"),
-    LIBCONV_TILE(263, 1, 3, 3, 3, 1, 1, 0, 64, 4, 32, 1, 4, 2, 1, 1, 30, "igemm16p_k333s1_m64_n4x32"),
-    LIBCONV_TILE(264, 1, 3, 3, 3, 1, 1, 0, 128, 8, 32, 2, 2, 1, 1, 1, 24, "igemm16p_k333s1_m128_n8x32_c8"),
-    LIBCONV_TILE(265, 1, 3, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 1, 0, 22, "igemm16p_k333s1_m64_n8x32_e"),
+    LIBCONV_TILE(260, 1, 3, 3, 3, 1, 1, 0, 128, 8, 32, 2, 2, 2, 1, 1, 30, 1, "igemm16p_k333s1_m128_n8x32"),
+    LIBCONV_TILE(261, 1, 3, 3, 3, 1, 1, 0, 128, 4, 32, 2, 2, 2, 1, 1, 23, 1, "igemm16p_k333s1_m128_n4x32"),
+    LIBCONV_TILE(262, 1, 3, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 1, 1, 33, 2, "igemm16p_k333s1_m64_n8x32"),
+    LIBCONV_TILE(263, 1, 3, 3, 3, 1, 1, 0, 64, 4, 32, 1, 4, 2, 1, 1, 30, 2, "igemm16p_k333s1_m64_n4x32"),
+    LIBCONV_TILE(264, 1, 3, 3, 3, 1, 1, 0, 128, 8, 32, 2, 2, 1, 1, 1, 24, 1, "igemm16p_k333s1_m128_n8x32_c8"),
+    LIBCONV_TILE(265, 1, 3, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 1, 0, 22, 2, "igemm16p_k333s1_m64_n8x32_e"),
     // packed weights: 16-bit, 3x3 stride 1
-    LIBCONV_TILE(270, 1, 1, 3, 3, 1, 1, 0, 128, 8, 32, 2, 2, 2, 1, 1, 30, "igemm16p_k3s1_m128_n8x32"),
-    LIBCONV_TILE(271, 1, 1, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 1, 1, 36, "igemm16p_k3s1_m64_n8x32"),
-    LIBCONV_TILE(272, 1, 1, 3, 3, 1, 1, 0, 128, 4, 32, 2, 2, 2, 1, 1, 23, "igemm16p_k3s1_m128_n4x32"),
-    LIBCONV_TILE(275, 1, 1, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 1, 0, 24, "igemm16p_k3s1_m64_n8x32_e"),
+    LIBCONV_TILE(270, 1, 1, 3, 3, 1, 1, 0, 128, 8, 32, 2, 2, 2, 1, 1, 30, 1, "igemm16p_k3s1_m128_n8x32"),
+    LIBCONV_TILE(271, 1, 1, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 1, 1, 36, 2, "igemm16p_k3s1_m64_n8x32"),
+    LIBCONV_TILE(272, 1, 1, 3, 3, 1, 1, 0, 128, 4, 32, 2, 2, 2, 1, 1, 23, 1, "igemm16p_k3s1_m128_n4x32"),
+    LIBCONV_TILE(275, 1, 1, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 1, 0, 24, 2, "igemm16p_k3s1_m64_n8x32_e"),
 };
 
 #undef LIBCONV_TILE
@@ -949,6 +977,12 @@ const char* igemm_tile_name(int id) {
   return t ? t->name : nullptr;
 }
 
+int igemm_tile_occupancy(int id, int dtype, bool measured) {
+  const TileDesc* t = find_tile(id);
+  if (!t || dtype < 0 || dtype > 2 || !t->fn[dtype]) return -1;
+  return measured ? t->occ_fn[dtype]() : t->occ;
+}
+
 bool igemm_tile_packed(int id) {
   const TileDesc* t = find_tile(id);
   return t && t->packed;
@@ -985,22 +1019,27 @@ libconv_status pack_launch(const void* w, void* wp, int C, int K, int KT, int KH
   return e == hipSuccess ? LIBCONV_OK : LIBCONV_ERR_LAUNCH;
 }
 
-// Estimated time of a tile on this shape, in microseconds: rounds of
-// workgroups on 256 compute units times the (padded) MFMA work of one tile at
-// the tile's measured efficiency, plus -- for packed tiles when the caller
-// gave OIHW weights -- the pack kernel (a launch plus reading and writing the
-// weights once).
+// Estimated time of a tile on this shape, in microseconds.  The busiest
+// compute unit runs ceil(tiles / CUs) tiles; occ of them at a time share its
+// matrix cores, so their MFMA work adds up at the tile's measured efficiency,
+// while the fixed latency of a workgroup (first reads, last stores: about
+// kRoundUs) is paid once per round of occ concurrent workgroups.  Packed
+// tiles on OIHW weights add the pack step: a stream-ordered temporary
+// (allocate, free) and the pack kernel, about 20 us on MI355X, plus reading
+// and writing the weights once.
+constexpr double kRoundUs = 4.0;
 static double estimate_us(const TileDesc& t, const Problem& p, const TileCounts& c) {
   const double ck = t.CG * (t.wide ? 8 : 4);
   const double chunks = std::ceil(p.C / ck);
   const double kred = chunks * ck * p.KT * p.KH * p.KW;
   const double tile_flop = 2.0 * t.BM * t.TH * t.TW * kred;
   const double cu_flop_per_us = (t.wide ? 4096.0 : 256.0) * 2400.0 * (t.eff / 100.0);
-  const double rounds = std::ceil(c.total / 256.0);
-  double us = rounds * tile_flop / cu_flop_per_us;
+  const double cus = p.cus > 0 ? p.cus : 256.0;
+  const double per_cu = std::ceil(c.total / cus);
+  double us = per_cu * tile_flop / cu_flop_per_us + std::ceil(per_cu / t.occ) * kRoundUs;
   if (t.packed && !p.wp) {
     const double wbytes = (double)packed_weight_bytes(p.C, p.K, p.KT, p.KH, p.KW, p.dtype);
-    us += 6.0 + 2.0 * wbytes / 3.0e6;
+    us += 20.0 + 2.0 * wbytes / 3.0e6;
   }
   return us;
 }

@@ -25,6 +25,7 @@ struct Problem {
   const void* b;   // may be null
   void* y;
   hipStream_t stream;
+  int cus;         // compute units of the current device (filled before a launch)
 };
 
 // What the dispatcher decided.
@@ -38,6 +39,8 @@ inline int dtype_bytes(int dt) { return dt == LIBCONV_F32 ? 4 : 2; }
 
 // Direct (vector ALU) family: every shape is supported.
 bool direct_plan(const Problem& p, Plan* plan);
+// A specific direct tile (the fixed-geometry tap tiles), if it fits the shape.
+bool direct_plan_tile(const Problem& p, int tile_id, Plan* plan);
 libconv_status direct_launch(const Problem& p, const Plan& plan);
 
 // Implicit-GEMM (MFMA) family: a fixed set of geometries; returns false
@@ -47,6 +50,10 @@ bool igemm_plan(const Problem& p, Plan* plan);
 bool igemm_plan_packed(const Problem& p, Plan* plan);
 // A specific MFMA tile, if it fits the shape.
 bool igemm_plan_tile(const Problem& p, int tile_id, Plan* plan);
+// Workgroups per compute unit of an MFMA tile for a dtype: the value the
+// dispatcher assumes, or (measured) the runtime's figure for the built
+// kernel; -1 for an unknown tile or dtype.
+int igemm_tile_occupancy(int id, int dtype, bool measured);
 // Whether a tile reads packed weights (p.wp) instead of OIHW weights.
 bool igemm_tile_packed(int tile_id);
 libconv_status igemm_launch(const Problem& p, const Plan& plan);

@@ -195,6 +195,14 @@ libconv_status libconv_query_algo(int N, int C_in, int T, int H, int W,
 /* Human-readable name of a tile configuration id; "?" if unknown. */
 const char* libconv_tile_name(int tile_id);
 
+/* Workgroups one compute unit holds at once for an MFMA tile configuration
+ * and dtype: with measured = 0, the figure the dispatcher's cost model uses
+ * (pure host, works without a GPU); with measured != 0, the HIP runtime's
+ * occupancy query for the built kernel on the current device.  -1 for an
+ * unknown tile id, a dtype the tile does not run, or (measured) no gfx950
+ * device. */
+int libconv_tile_occupancy(int tile_id, int dtype, int measured);
+
 /* floor((in + 2*pad - k) / stride) + 1, or -1 if an argument is out of range
  * (in < 1, k < 1, pad < 0, stride < 1) or the window does not fit. */
 int libconv_out_size(int in, int k, int pad, int stride);

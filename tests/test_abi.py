@@ -166,3 +166,20 @@ def test_3d_layers_dispatch_to_packed_tiles():
             l.N, l.C_in, l.T, l.H, l.W, l.C_out, l.KT, l.KH, l.KW, *l.pad, *l.stride,
             W.DTYPE_CODE[l.dtype], W.ACT_CODE[l.act], L.ALGO_AUTO)
         assert st == 0 and L.libconv_tile_name(tile).startswith("igemm16p_")
+
+
+def test_tile_occupancy_query_without_gpu():
+    """The cost model's occupancy column is a host query; unknown ids and
+    dtypes a tile does not run give -1."""
+    for tid in range(200, 300):
+        name = L.libconv_tile_name(tid)
+        if name == "?":
+            assert L.libconv_tile_occupancy(tid, 0, 0) == -1
+            continue
+        wide = name.startswith("igemm16")
+        for dt in (0, 1, 2):
+            occ = L.libconv_tile_occupancy(tid, dt, 0)
+            if (dt == 0) == (not wide):
+                assert 1 <= occ <= 8, (name, dt, occ)
+            else:
+                assert occ == -1, (name, dt, occ)

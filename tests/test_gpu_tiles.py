@@ -92,3 +92,76 @@ def test_every_tile(ragged, monkeypatch):
         m = metrics(to_f64(y), ref, s, layer.dtype)
         note(f"  {m}")
         assert_gates(m, layer.dtype, name)
+
+
+def _tap_tiles():
+    import direct_implicit_gemm_amd as L
+    out = []
+    for tid in range(100, 200):
+        name = L.libconv_tile_name(tid)
+        if name.startswith("tap_"):
+            out.append((tid, name))
+    return out
+
+
+def _tap_layer_for(i: int, name: str, ragged: bool) -> W.Layer:
+    """A small layer that the tap tile `name` fits: ragged output rows,
+    columns and channels; some with frames (3-D, one frame tap), some with
+    more input channels than one LDS stage holds."""
+    m = re.match(r"tap_k(\d)(s(\d))?_cot(\d+)_r(\d+)(_e)?$", name)
+    assert m, name
+    k, s = int(m.group(1)), int(m.group(3) or 1)
+    cot, elem = int(m.group(4)), m.group(6) is not None
+    dtype = ("f32", "f16", "bf16")[i % 3]
+    c = 3 if not ragged else 5
+    kout = cot + cot // 2 + 1 if ragged else 2 * cot
+    wd = 72 * s if not elem else 67 * s + 1
+    h = 13 * s + 1 if ragged else 16 * s
+    pad = (k - 1) // 2
+    relu = "relu" if i % 2 else "none"
+    if ragged:  # frames: a 3-D layer with one frame tap
+        return W.Layer("t", dtype, 1, c, 2, h, wd, kout, 1, k, k, (0, pad, pad), (1, s, s),
+                       relu, 3, "N01", "N01", "U0.05")
+    return W.Layer("t", dtype, 2, c, 1, h, wd, kout, 1, k, k, (0, pad, pad), (1, s, s),
+                   relu, 2, "N01", "N01", "U0.05")
+
+
+@pytest.mark.parametrize("ragged", [False, True])
+def test_every_tap_tile(ragged, monkeypatch):
+    import direct_implicit_gemm_amd as L
+    tiles = _tap_tiles()
+    assert len(tiles) >= 6
+    for i, (tid, name) in enumerate(tiles):
+        layer = _tap_layer_for(i, name, ragged)
+        monkeypatch.setenv("LIBCONV_FORCE_TILE", str(tid))
+        q = L.libconv_query_algo(layer.N, layer.C_in, layer.T, layer.H, layer.W, layer.C_out,
+                                 layer.KT, layer.KH, layer.KW, *layer.pad, *layer.stride,
+                                 W.DTYPE_CODE[layer.dtype], W.ACT_CODE[layer.act], 1)
+        assert q[0] == 0 and q[2] == tid, (name, layer, q)
+        note(f"tap tile {tid} {name} ragged={ragged}: x={layer.x_shape} w={layer.w_shape} "
+             f"{layer.dtype} {layer.act}")
+        x, w, b = W.make_inputs(layer, 700 + 2 * i + ragged)
+        st, pd = (layer.stride[1:], layer.pad[1:]) if layer.dims == 2 else (layer.stride,
+                                                                           layer.pad)
+        y = L.conv_nd(x.torch("cuda"), w.torch("cuda"), b.torch("cuda"), st, pd, layer.act,
+                      "direct")
+        torch.cuda.synchronize()
+        ref, s = oracle.conv(x.f64(), w.f64(), b.f64(), *oracle_args(layer),
+                             relu=layer.act == "relu")
+        m = metrics(to_f64(y), ref, s, layer.dtype)
+        note(f"  {m}")
+        assert_gates(m, layer.dtype, name)
+
+
+def test_tile_occupancy_table_matches_runtime():
+    """The dispatcher's per-tile workgroups-per-CU figures against the HIP
+    runtime's occupancy query for the built kernels."""
+    import direct_implicit_gemm_amd as L
+    for tid, name in _tiles():
+        for dt in (0, 1, 2):
+            table = L.libconv_tile_occupancy(tid, dt, False)
+            if table < 0:
+                continue
+            measured = L.libconv_tile_occupancy(tid, dt, True)
+            note(f"occupancy {tid} {name} dtype {dt}: table {table} runtime {measured}")
+            assert measured == table, (name, dt, table, measured)
