@@ -114,6 +114,34 @@ bool device_ok(int d) {
   return d >= 0 && d < g_dev_count && g_dev_ok[d];
 }
 
+// Per-device pool for the stream-ordered temporaries of a call.  Its release
+// threshold keeps freed blocks cached in the pool, so once a size has been
+// used, later calls take their temporaries without a driver allocation.  If
+// the pool cannot be made, the device's default pool is used.
+std::once_flag g_pool_once[kMaxDevices];
+hipMemPool_t g_pool[kMaxDevices];
+
+hipMemPool_t device_pool(int d) {
+  std::call_once(g_pool_once[d], [d] {
+    hipMemPoolProps props;
+    std::memset(&props, 0, sizeof(props));
+    props.allocType = hipMemAllocationTypePinned;
+    props.handleTypes = hipMemHandleTypeNone;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = d;
+    hipMemPool_t pool = nullptr;
+    if (hipMemPoolCreate(&pool, &props) == hipSuccess) {
+      uint64_t keep = ~0ull;
+      (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+      g_pool[d] = pool;
+    } else {
+      g_pool[d] = nullptr;
+    }
+    (void)hipGetLastError();
+  });
+  return g_pool[d];
+}
+
 // The dispatcher.  The vector-ALU direct kernel takes layers whose
 // reduction per output (C_in * taps) is too short to fill an MFMA k-step
 // pipeline -- stems with 3 input channels, pointwise layers with fewer than
@@ -185,8 +213,10 @@ libconv_status run(Problem& p, int algo) {
   if (std::getenv("LIBCONV_LOG")) {
     const char* name = plan.algo == LIBCONV_ALGO_DIRECT ? direct_tile_name(plan.tile)
                                                         : igemm_tile_name(plan.tile);
-    std::fprintf(stderr, "libconv: %s grid=%lld (N=%d C=%d T=%d H=%d W=%d K=%d k=%dx%dx%d)\n",
-                 name ? name : "?", plan.grid, p.N, p.C, p.T, p.H, p.W, p.K, p.KT, p.KH, p.KW);
+    std::fprintf(stderr,
+                 "libconv: %s grid=%lld ksplit=%d (N=%d C=%d T=%d H=%d W=%d K=%d k=%dx%dx%d)\n",
+                 name ? name : "?", plan.grid, plan.ksplit, p.N, p.C, p.T, p.H, p.W, p.K, p.KT,
+                 p.KH, p.KW);
   }
   if (plan.algo == LIBCONV_ALGO_DIRECT) return direct_launch(p, plan);
   if (!igemm_tile_packed(plan.tile) || p.wp) return igemm_launch(p, plan);
@@ -195,16 +225,13 @@ libconv_status run(Problem& p, int algo) {
   // synchronisation; recordable in a HIP graph), run, and release it.
   const long long pb = packed_weight_bytes(p.C, p.K, p.KT, p.KH, p.KW, p.dtype);
   void* tmp = nullptr;
-  if (hipMallocAsync(&tmp, (size_t)pb, p.stream) != hipSuccess || !tmp) {
-    (void)hipGetLastError();
-    return LIBCONV_ERR_OUT_OF_MEMORY;
-  }
+  if (stream_alloc((size_t)pb, p.stream, &tmp) != LIBCONV_OK) return LIBCONV_ERR_OUT_OF_MEMORY;
   st = pack_launch(p.w, tmp, p.C, p.K, p.KT, p.KH, p.KW, p.dtype, p.stream);
   if (st == LIBCONV_OK) {
     p.wp = tmp;
     st = igemm_launch(p, plan);
   }
-  if (hipFreeAsync(tmp, p.stream) != hipSuccess && st == LIBCONV_OK) st = LIBCONV_ERR_LAUNCH;
+  if (stream_free(tmp, p.stream) != LIBCONV_OK && st == LIBCONV_OK) st = LIBCONV_ERR_LAUNCH;
   return st;
 }
 
@@ -226,6 +253,34 @@ Problem make_problem(const void* x, const void* w, const void* bias, void* y, in
 }
 
 }  // namespace
+
+libconv_status stream_alloc(size_t bytes, hipStream_t stream, void** out) {
+  *out = nullptr;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return LIBCONV_ERR_NO_DEVICE;
+  }
+  const hipMemPool_t pool = device_pool(dev);
+  const hipError_t e = pool ? hipMallocFromPoolAsync(out, bytes, pool, stream)
+                            : hipMallocAsync(out, bytes, stream);
+  if (e != hipSuccess || !*out) {
+    (void)hipGetLastError();
+    *out = nullptr;
+    return LIBCONV_ERR_OUT_OF_MEMORY;
+  }
+  return LIBCONV_OK;
+}
+
+libconv_status stream_free(void* p, hipStream_t stream) {
+  if (!p) return LIBCONV_OK;
+  if (hipFreeAsync(p, stream) != hipSuccess) {
+    (void)hipGetLastError();
+    return LIBCONV_ERR_LAUNCH;
+  }
+  return LIBCONV_OK;
+}
+
 }  // namespace libconv
 
 using namespace libconv;

@@ -112,7 +112,12 @@ struct IgemmArgs {
   int kp;             // packed weights: output-channel stride (C_out rounded up)
   int co_tiles, row_tiles, col_tiles;
   int co_group;       // output-channel tiles per group of the launch order
-  uint32_t x_bytes, w_bytes, b_bytes, y_bytes;
+  // split-K: `ksplit` workgroups share a tile, each summing a contiguous range
+  // of `cps` channel chunks and writing its fp32 partial sums (no bias, no
+  // activation) to part[split][n][co][ot][oh][ow]; 1 = no split
+  int ksplit, cps;
+  float* part;
+  uint32_t x_bytes, w_bytes, b_bytes, y_bytes, part_bytes;
 };
 
 template <int DT_, int KT_, int KH_, int KW_, int SH_, int SW_, int BM_, int TH_, int TW_,
@@ -293,10 +298,15 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
   // (whose weights fit in L2 together); inside a group the output-channel
   // tile varies fastest, so the tiles that read the same input pixels run
   // side by side, then the pixel tile.
+  // With split-K the split index is the slowest part of the logical order,
+  // so an XCD mostly works on one split's channels.
   const int G_ = gridDim.x;
   int bid = blockIdx.x;
   if ((G_ & 7) == 0) bid = (bid & 7) * (G_ >> 3) + (bid >> 3);
   const int pix_tiles = a.col_tiles * a.row_tiles * a.OT * a.N;
+  const int tiles = a.co_tiles * pix_tiles;
+  const int split = bid / tiles;
+  bid -= split * tiles;
   const int full_groups = a.co_tiles / a.co_group;
   int cot;
   if (bid < full_groups * a.co_group * pix_tiles) {
@@ -326,7 +336,8 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
   const int kt_lo = it0 < 0 ? -it0 : 0;
   const int kt_hi = min(G::KT, a.T - it0);
   const int nkt = kt_hi > kt_lo ? kt_hi - kt_lo : 0;
-  const int nstages = a.chunks * nkt;
+  const int chunk0 = split * a.cps;  // this workgroup's channel chunks
+  const int nstages = max(0, min(a.chunks - chunk0, a.cps)) * nkt;
 
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.w, a.w_bytes);
 
@@ -624,7 +635,7 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
   };
   auto main_loop = [&](auto ragged) __attribute__((always_inline)) {
     StageRegs<G> ra, rb;
-    Cursor cw{0, kt_lo, 0}, cx{0, kt_lo, 0};  // next stage to read: weights, input
+    Cursor cw{chunk0, kt_lo, 0}, cx{chunk0, kt_lo, 0};  // next stage to read: weights, input
     // all reads of the stage at cursor cx (and, for packed weights, of the
     // stage at cw) at once
     auto read_all = [&](StageRegs<G>& r, unsigned char* wdst) __attribute__((always_inline)) {
@@ -689,9 +700,28 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
   }
 
   // ---- epilogue
+  const int ohw = a.OH * a.OW;
+  if (a.ksplit > 1) {  // fp32 partial sums of this split, one writer per element
+    const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.part, a.part_bytes);
+#pragma unroll
+    for (int i = 0; i < G::FA; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int co = co0 + co_w0 + i * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+        const int cbase = (((split * a.N + n) * a.K + co) * a.OT + ot) * ohw;
+#pragma unroll
+        for (int j = 0; j < G::FB; ++j) {
+          const int b = blk0 + j;
+          const int oh = oh0 + b / G::BPR;
+          const int ow = ow0 + (b % G::BPR) * 32 + il;
+          if (co < a.K && oh < a.OH && ow < a.OW)
+            Elem<DT_F32>::store(acc[i][j][r], pr, (cbase + oh * a.OW + ow) * 4);
+        }
+      }
+    return;
+  }
   const __amdgpu_buffer_rsrc_t yr = make_rsrc(a.y, a.y_bytes);
   const __amdgpu_buffer_rsrc_t br = make_rsrc(a.b, a.b_bytes);
-  const int ohw = a.OH * a.OW;
   // All bias loads first (one round trip); channels beyond C_out read 0 and
   // are not stored.
   float bias[G::FA][16];
@@ -783,6 +813,47 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackArgs a) {
     }
   }
   store_packed<SE, TS, 0>(pr, (g * TS * a.Kp + co) * 16, a.Kp * 16, v);
+}
+
+// ------------------------------------------------------------ split-K sum
+// y[e] = act(b[co] + sum_{s < S} part[s][e]) rounded once to the storage
+// dtype, the slices added in order s = 0, 1, ... (so the result does not
+// depend on timing).  Thread i takes 4 consecutive outputs of one channel
+// plane when the plane length is a multiple of 4, else one output.
+struct ReduceArgs {
+  const float* part;
+  const void* b;
+  void* y;
+  int S, K, plane, relu;
+  long long n_out;  // N * K * plane
+  uint32_t part_bytes, b_bytes, y_bytes;
+};
+
+template <int DT, int V>
+__global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(ReduceArgs a) {
+  using E = Elem<DT>;
+  const long long e0 = ((long long)blockIdx.x * kThreads + threadIdx.x) * V;
+  if (e0 >= a.n_out) return;
+  const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.part, a.part_bytes);
+  const __amdgpu_buffer_rsrc_t br = make_rsrc(a.b, a.b_bytes);
+  const __amdgpu_buffer_rsrc_t yr = make_rsrc(a.y, a.y_bytes);
+  const int co = (int)((e0 / a.plane) % a.K);
+  const float bias = E::load(br, guard_offset(a.b != nullptr, co * E::bytes));
+  float v[V];
+#pragma unroll
+  for (int m = 0; m < V; ++m) v[m] = 0.0f;
+  for (int sp = 0; sp < a.S; ++sp) {
+    const int off = (int)((sp * a.n_out + e0) * 4);
+    if constexpr (V == 4) {
+      const float4_t q = __builtin_bit_cast(float4_t, __builtin_amdgcn_raw_buffer_load_b128(pr, off, 0, 0));
+#pragma unroll
+      for (int m = 0; m < 4; ++m) v[m] += q[m];
+    } else {
+      v[0] += Elem<DT_F32>::load(pr, off);
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < V; ++m) E::store(epilogue(v[m], bias, a.relu), yr, (int)((e0 + m) * E::bytes));
 }
 
 // ------------------------------------------------------------------ tiles
@@ -1019,52 +1090,86 @@ libconv_status pack_launch(const void* w, void* wp, int C, int K, int KT, int KH
   return e == hipSuccess ? LIBCONV_OK : LIBCONV_ERR_LAUNCH;
 }
 
-// Estimated time of a tile on this shape, in microseconds.  The busiest
-// compute unit runs ceil(tiles / CUs) tiles; occ of them at a time share its
-// matrix cores, so their MFMA work adds up at the tile's measured efficiency,
-// while the fixed latency of a workgroup (first reads, last stores: about
-// kRoundUs) is paid once per round of occ concurrent workgroups.  Packed
-// tiles on OIHW weights add the pack step: a stream-ordered temporary
-// (allocate, free) and the pack kernel, about 20 us on MI355X, plus reading
-// and writing the weights once.
+// Output elements and fp32 partial-sum bytes of a split-K launch.
+static long long out_elems(const Problem& p) { return (long long)p.N * p.K * p.OT * p.OH * p.OW; }
+static long long part_bytes(const Problem& p, int ksplit) { return ksplit * out_elems(p) * 4; }
+
+// Chunks of channels per split, and whether a split count is usable: every
+// split gets at least two chunks and the partial sums stay addressable.
+static int chunks_of(const TileDesc& t, const Problem& p) {
+  const int ck = t.CG * (t.wide ? 8 : 4);
+  return (p.C + ck - 1) / ck;
+}
+static bool split_ok(const TileDesc& t, const Problem& p, int ksplit) {
+  if (ksplit == 1) return true;
+  const int chunks = chunks_of(t, p);
+  const int cps = (chunks + ksplit - 1) / ksplit;
+  return cps >= 2 && (long long)(ksplit - 1) * cps < chunks && part_bytes(p, ksplit) < 0x7fff0000LL;
+}
+
+// Estimated time of a tile and split on this shape, in microseconds.  The
+// busiest compute unit runs ceil(units / CUs) work units (tiles, times the
+// split count); occ of them at a time share its matrix cores, so their MFMA
+// work adds up at the tile's measured efficiency, while the fixed latency of
+// a workgroup (first reads, last stores: about kRoundUs) is paid once per
+// round of occ concurrent workgroups.  Packed tiles on OIHW weights add the
+// pack step: a stream-ordered temporary (allocate, free) and the pack kernel,
+// about 8 us on MI355X, plus reading and writing the weights once.  A split
+// adds the sum kernel: a launch and its temporary, plus writing and reading
+// the fp32 partial sums once and writing the output.
 constexpr double kRoundUs = 4.0;
-static double estimate_us(const TileDesc& t, const Problem& p, const TileCounts& c) {
+static double estimate_us(const TileDesc& t, const Problem& p, const TileCounts& c, int ksplit) {
   const double ck = t.CG * (t.wide ? 8 : 4);
-  const double chunks = std::ceil(p.C / ck);
-  const double kred = chunks * ck * p.KT * p.KH * p.KW;
-  const double tile_flop = 2.0 * t.BM * t.TH * t.TW * kred;
+  const int chunks = chunks_of(t, p);
+  const double cps = std::ceil((double)chunks / ksplit);
+  const double unit_flop = 2.0 * t.BM * t.TH * t.TW * cps * ck * p.KT * p.KH * p.KW;
   const double cu_flop_per_us = (t.wide ? 4096.0 : 256.0) * 2400.0 * (t.eff / 100.0);
   const double cus = p.cus > 0 ? p.cus : 256.0;
-  const double per_cu = std::ceil(c.total / cus);
-  double us = per_cu * tile_flop / cu_flop_per_us + std::ceil(per_cu / t.occ) * kRoundUs;
+  const double per_cu = std::ceil(c.total * ksplit / cus);
+  double us = per_cu * unit_flop / cu_flop_per_us + std::ceil(per_cu / t.occ) * kRoundUs;
   if (t.packed && !p.wp) {
     const double wbytes = (double)packed_weight_bytes(p.C, p.K, p.KT, p.KH, p.KW, p.dtype);
-    us += 20.0 + 2.0 * wbytes / 3.0e6;
+    us += 8.0 + 2.0 * wbytes / 6.0e6;
   }
+  if (ksplit > 1)
+    us += 10.0 + (2.0 * part_bytes(p, ksplit) + out_elems(p) * dtype_bytes(p.dtype)) / 4.0e6;
   return us;
 }
 
-// Among the tiles that fit (packed or not, as asked), the one with the
-// smallest estimated time.
+// Split count forced for tests and A/B runs (LIBCONV_FORCE_KSPLIT), else 0.
+static int forced_ksplit() {
+  const char* e = std::getenv("LIBCONV_FORCE_KSPLIT");
+  return e ? std::atoi(e) : 0;
+}
+
+// Among the tiles that fit (packed or not, as asked) and the split counts
+// 1..4, the pair with the smallest estimated time.
 static bool plan_among(const Problem& p, int want_packed, Plan* plan) {
   const TileDesc* best = nullptr;
   double best_cost = 0.0;
   long long best_total = 0;
+  int best_split = 1;
+  const int fk = forced_ksplit();
   for (const auto& t : kTiles) {
     if (want_packed >= 0 && t.packed != want_packed) continue;
     if (!tile_fits(t, p) || !t.fn[p.dtype]) continue;
     const TileCounts c = counts(t, p);
-    const double cost = estimate_us(t, p, c);
-    if (!best || cost < best_cost) {
-      best = &t;
-      best_cost = cost;
-      best_total = c.total;
+    for (int ks = 1; ks <= 4; ++ks) {
+      if ((fk > 0 && ks != fk) || !split_ok(t, p, ks)) continue;
+      const double cost = estimate_us(t, p, c, ks);
+      if (!best || cost < best_cost) {
+        best = &t;
+        best_cost = cost;
+        best_total = c.total;
+        best_split = ks;
+      }
     }
   }
   if (!best) return false;
   plan->algo = LIBCONV_ALGO_IGEMM;
   plan->tile = best->id;
-  plan->grid = best_total;
+  plan->ksplit = best_split;
+  plan->grid = best_total * best_split;
   return true;
 }
 
@@ -1075,10 +1180,19 @@ bool igemm_plan_packed(const Problem& p, Plan* plan) { return plan_among(p, 1, p
 bool igemm_plan_tile(const Problem& p, int tile_id, Plan* plan) {
   const TileDesc* t = find_tile(tile_id);
   if (!t || !tile_fits(*t, p) || !t->fn[p.dtype]) return false;
+  const int fk = forced_ksplit();
   plan->algo = LIBCONV_ALGO_IGEMM;
   plan->tile = t->id;
-  plan->grid = counts(*t, p).total;
+  plan->ksplit = fk > 1 && split_ok(*t, p, fk) ? fk : 1;
+  plan->grid = counts(*t, p).total * plan->ksplit;
   return true;
+}
+
+using ReduceFn = hipError_t (*)(const ReduceArgs&, unsigned, hipStream_t);
+template <int DT, int V>
+hipError_t launch_reduce(const ReduceArgs& a, unsigned grid, hipStream_t s) {
+  hipLaunchKernelGGL((splitk_reduce_kernel<DT, V>), dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
 }
 
 libconv_status igemm_launch(const Problem& p, const Plan& plan) {
@@ -1087,8 +1201,10 @@ libconv_status igemm_launch(const Problem& p, const Plan& plan) {
   const LaunchFn fn = t->fn[p.dtype];
   if (!fn) return LIBCONV_ERR_UNSUPPORTED;
   if (t->packed && !p.wp) return LIBCONV_ERR_UNSUPPORTED;
+  const int ks = plan.ksplit > 1 ? plan.ksplit : 1;
+  if (!split_ok(*t, p, ks)) return LIBCONV_ERR_UNSUPPORTED;
   const TileCounts c = counts(*t, p);
-  if (c.total > 0x7fffffffLL) return LIBCONV_ERR_UNSUPPORTED;
+  if (c.total * ks > 0x7fffffffLL) return LIBCONV_ERR_UNSUPPORTED;
   IgemmArgs a;
   a.x = p.x; a.w = t->packed ? p.wp : p.w; a.b = p.b; a.y = p.y;
   a.N = p.N; a.C = p.C; a.T = p.T; a.K = p.K; a.OT = p.OT;
@@ -1099,22 +1215,55 @@ libconv_status igemm_launch(const Problem& p, const Plan& plan) {
   }
   a.pt = p.pt; a.ph = p.ph; a.pw = p.pw; a.st = p.st;
   a.relu = p.act == LIBCONV_ACT_RELU;
-  const int ck = t->CG * (t->wide ? 8 : 4);
-  a.chunks = (p.C + ck - 1) / ck;
+  a.chunks = chunks_of(*t, p);
+  a.ksplit = ks;
+  a.cps = (a.chunks + ks - 1) / ks;
   a.kp = (p.K + kPackAlign - 1) / kPackAlign * kPackAlign;
   a.co_tiles = (int)c.co; a.row_tiles = (int)c.rows; a.col_tiles = (int)c.cols;
   const int eb = dtype_bytes(p.dtype);
-  // as many output-channel tiles side by side as keep their weights within
-  // about 2 MB (half an XCD's L2)
-  const long long w_tile = (long long)t->BM * p.C * p.KT * p.KH * p.KW * eb;
+  // as many output-channel tiles side by side as keep their weights (of one
+  // split) within about 2 MB (half an XCD's L2)
+  const long long w_tile = (long long)t->BM * std::min(p.C, a.cps * t->CG * (t->wide ? 8 : 4)) *
+                           p.KT * p.KH * p.KW * eb;
   a.co_group = (int)std::max(1LL, std::min<long long>(c.co, (2LL << 20) / std::max(1LL, w_tile)));
   a.x_bytes = (uint32_t)((long long)p.N * p.C * p.T * p.H * p.W * eb);
   a.w_bytes = t->packed ? (uint32_t)packed_weight_bytes(p.C, p.K, p.KT, p.KH, p.KW, p.dtype)
                         : (uint32_t)((long long)p.K * p.C * p.KT * p.KH * p.KW * eb);
   a.b_bytes = p.b ? (uint32_t)(p.K * eb) : 0u;
   a.y_bytes = (uint32_t)((long long)p.N * p.K * p.OT * p.OH * p.OW * eb);
-  const hipError_t e = fn(a, (unsigned)c.total, p.stream);
-  return e == hipSuccess ? LIBCONV_OK : LIBCONV_ERR_LAUNCH;
+  a.part = nullptr;
+  a.part_bytes = 0;
+  if (ks == 1) {
+    const hipError_t e = fn(a, (unsigned)c.total, p.stream);
+    return e == hipSuccess ? LIBCONV_OK : LIBCONV_ERR_LAUNCH;
+  }
+  // split-K: partial sums in a stream-ordered temporary, then the sum kernel
+  const long long pb = part_bytes(p, ks);
+  void* part = nullptr;
+  if (stream_alloc((size_t)pb, p.stream, &part) != LIBCONV_OK) return LIBCONV_ERR_OUT_OF_MEMORY;
+  a.part = static_cast<float*>(part);
+  a.part_bytes = (uint32_t)pb;
+  libconv_status st = LIBCONV_OK;
+  if (fn(a, (unsigned)(c.total * ks), p.stream) != hipSuccess) st = LIBCONV_ERR_LAUNCH;
+  if (st == LIBCONV_OK) {
+    ReduceArgs r;
+    r.part = a.part; r.b = p.b; r.y = p.y;
+    r.S = ks; r.K = p.K; r.plane = p.OT * p.OH * p.OW; r.relu = a.relu;
+    r.n_out = out_elems(p);
+    r.part_bytes = a.part_bytes; r.b_bytes = a.b_bytes; r.y_bytes = a.y_bytes;
+    const bool v4 = r.plane % 4 == 0;
+    const int V = v4 ? 4 : 1;
+    const unsigned grid = (unsigned)((r.n_out / V + kThreads - 1) / kThreads);
+    ReduceFn rf = nullptr;
+    switch (p.dtype) {
+      case LIBCONV_F32: rf = v4 ? &launch_reduce<DT_F32, 4> : &launch_reduce<DT_F32, 1>; break;
+      case LIBCONV_F16: rf = v4 ? &launch_reduce<DT_F16, 4> : &launch_reduce<DT_F16, 1>; break;
+      default: rf = v4 ? &launch_reduce<DT_BF16, 4> : &launch_reduce<DT_BF16, 1>; break;
+    }
+    if (rf(r, grid, p.stream) != hipSuccess) st = LIBCONV_ERR_LAUNCH;
+  }
+  if (stream_free(part, p.stream) != LIBCONV_OK && st == LIBCONV_OK) st = LIBCONV_ERR_LAUNCH;
+  return st;
 }
 
 }  // namespace libconv

@@ -32,8 +32,15 @@ struct Problem {
 struct Plan {
   int algo;         // LIBCONV_ALGO_DIRECT or LIBCONV_ALGO_IGEMM
   int tile;         // tile configuration id (see tile_name)
-  long long grid;   // workgroups
+  long long grid;   // workgroups (of the convolution kernel)
+  int ksplit = 1;   // MFMA tiles: workgroups sharing one tile's reduction (split-K)
 };
+
+// Device memory for one call's temporaries (packed weights, split-K partial
+// sums), ordered on `stream`: taken from a per-device pool that keeps freed
+// memory cached, so calls after the first do not go to the driver.
+libconv_status stream_alloc(size_t bytes, hipStream_t stream, void** out);
+libconv_status stream_free(void* p, hipStream_t stream);
 
 inline int dtype_bytes(int dt) { return dt == LIBCONV_F32 ? 4 : 2; }
 
