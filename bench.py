@@ -14,11 +14,12 @@ step); per-layer figures (µs, TFLOP/s, GB/s, binding roofline and fraction)
 are in ``layers``; ``roofline`` describes the layer whose kernel takes the most
 time; ``cpu_baseline`` is the fp64 oracle timed on the host cores.
 
-Per-layer times: ``us_mean`` comes from an event pair around each launch
-inside the timed steps, which also counts the dispatch of the launch (about
-2-3 us); ``us_b2b`` from one event pair around R back-to-back launches of the
-layer alone, divided by R, which matches the kernel durations of a rocprofv3
-kernel trace.  The roofline fractions use ``us_b2b``.
+The step is timed twice, K eager steps and K replays of the step captured
+once as a HIP graph (no host launch overhead; ``--no-graph`` skips it), and
+the faster is reported (``config.step_mode``; both times are in ``config``).
+Per-layer times: ``us_b2b``, one event pair around R back-to-back launches of
+the layer alone, divided by R, which matches the kernel durations of a
+rocprofv3 kernel trace.  The roofline fractions use ``us_b2b``.
 """
 from __future__ import annotations
 
@@ -131,6 +132,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="ocr_stack", choices=sorted(W.WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager steps instead of replays of the step captured as a HIP graph")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the workload, copy MIB MiB device-to-device --steps times "
@@ -186,35 +189,57 @@ def main():
     def sp(l):
         return (l.stride[1:], l.pad[1:]) if l.dims == 2 else (l.stride, l.pad)
 
-    def step(events=None):
+    def step():
         for i, l in enumerate(layers):
             x_in = outs[i - 1] if (chained and i > 0) else xs[i]
             s, p = sp(l)
-            if events is not None:
-                events[i][0].record()
             L.conv_nd(x_in, ws[i], bs[i], s, p, l.act, out=outs[i])
-            if events is not None:
-                events[i][1].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
+    # The step as a HIP graph (captured once through torch's graph capture, on
+    # torch's capture stream, which is the stream libconv launches on): a
+    # replay issues the layers back to back without host launch overhead.
+    # Under capture libconv plans without temporaries (no split-K, no weight
+    # packing per call), which can be slower for some layers, so both the
+    # eager step and the replayed step are timed over K steps and the faster
+    # is reported (both are in `config`).
+    graph, graph_note = None, "off"
+    if not args.no_graph:
+        try:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            graph, graph_note = g, "captured"
+        except Exception as e:  # a layer whose call cannot be captured: eager steps
+            graph, graph_note = None, f"capture failed ({type(e).__name__})"
+            torch.cuda.synchronize()
+
     K = args.steps
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in layers] for _ in range(K)]
-    torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    t_start.record()
-    for k in range(K):
-        step(ev[k])
-    t_end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / K
+
+    def timed(run_one):
+        torch.cuda.synchronize()
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        t_start.record()
+        for _ in range(K):
+            run_one()
+        t_end.record()
+        torch.cuda.synchronize()
+        return t_start.elapsed_time(t_end) / K, time.perf_counter() - w0
+
+    ms_eager, wall_eager = timed(step)
+    ms_graph, wall_graph = timed(graph.replay) if graph is not None else (None, None)
+    if ms_graph is not None and ms_graph < ms_eager:
+        ms_per_step, wall, mode = ms_graph, wall_graph, "graph replay"
+    else:
+        ms_per_step, wall, mode = ms_eager, wall_eager, "eager"
 
     # each layer alone, R launches back to back between one event pair
     R = max(10, K)
@@ -236,8 +261,6 @@ def main():
     per_layer = []
     step_flops = 0
     for i, l in enumerate(layers):
-        times = [ev[k][i][0].elapsed_time(ev[k][i][1]) for k in range(K)]
-        us_step = 1000.0 * float(np.mean(times))
         us = b2b[i]
         flops, nbytes = layer_work(l, lib)
         step_flops += flops
@@ -248,8 +271,6 @@ def main():
         per_layer.append({
             "layer": l.name, "kernel": L.libconv_tile_name(tile), "grid": grid,
             "us_b2b": round(us, 3), "b2b_reps": R,
-            "us_mean": round(us_step, 3), "us_min": round(1000.0 * float(np.min(times)), 3),
-            "us_median": round(1000.0 * float(np.median(times)), 3),
             "gflop": round(flops / 1e9, 4), "mbytes": round(nbytes / 1e6, 3),
             "tflops": round(tflops, 3), "gbs": round(gbs, 1),
             "bound": bound, "frac": round(frac, 4),
@@ -302,7 +323,10 @@ def main():
         "dtype": layers[0].dtype,
         "data": "synthetic (seeded; shapes and value distributions of the workload)",
         "config": {"workload": args.workload, "description": WORKLOAD_TEXT[args.workload],
-                   "chained": chained, "wall_s_timed": round(wall, 4)},
+                   "chained": chained, "step_mode": mode, "graph": graph_note,
+                   "ms_per_step_eager": round(ms_eager, 5),
+                   "ms_per_step_graph": None if ms_graph is None else round(ms_graph, 5),
+                   "wall_s_timed": round(wall, 4)},
         "roofline": roof,
         "cpu_baseline": cpu,
         "layers": per_layer,

@@ -207,6 +207,15 @@ libconv_status run(Problem& p, int algo) {
     return LIBCONV_ERR_NO_DEVICE;
   }
   p.cus = g_dev_cus[dev];
+  // While the stream is being captured into a graph, plan without
+  // stream-ordered temporaries: an allocation recorded into a graph is not
+  // guaranteed to be mapped when the graph's kernels run.
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(p.stream, &cap) != hipSuccess) {
+    (void)hipGetLastError();
+    cap = hipStreamCaptureStatusNone;
+  }
+  p.no_temps = p.no_temps || cap != hipStreamCaptureStatusNone;
   Plan plan;
   st = plan_for(p, algo, &plan, p.w == nullptr);
   if (st != LIBCONV_OK) return st;
@@ -220,6 +229,7 @@ libconv_status run(Problem& p, int algo) {
   }
   if (plan.algo == LIBCONV_ALGO_DIRECT) return direct_launch(p, plan);
   if (!igemm_tile_packed(plan.tile) || p.wp) return igemm_launch(p, plan);
+  if (p.no_temps) return LIBCONV_ERR_UNSUPPORTED;  // never reached: planning excludes it
   // The tile reads packed weights but the caller passed OIHW weights: pack
   // them into a stream-ordered temporary on the call's stream (no device-wide
   // synchronisation; recordable in a HIP graph), run, and release it.
@@ -352,6 +362,7 @@ libconv_status libconv_forward_packed(const void* x, const void* packed_w, const
   Problem p = make_problem(x, nullptr, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW, pad_t, pad_h,
                            pad_w, stride_t, stride_h, stride_w, dtype, act, stream);
   p.wp = packed_w;
+  p.no_temps = true;  // this entry point never allocates: no split-K either
   if (!packed_w && x && y) return LIBCONV_ERR_NULL_POINTER;
   return run(p, LIBCONV_ALGO_IGEMM);
 }

@@ -1153,9 +1153,10 @@ static bool plan_among(const Problem& p, int want_packed, Plan* plan) {
   for (const auto& t : kTiles) {
     if (want_packed >= 0 && t.packed != want_packed) continue;
     if (!tile_fits(t, p) || !t.fn[p.dtype]) continue;
+    if (p.no_temps && t.packed && !p.wp) continue;  // would pack into a temporary
     const TileCounts c = counts(t, p);
-    for (int ks = 1; ks <= 4; ++ks) {
-      if ((fk > 0 && ks != fk) || !split_ok(t, p, ks)) continue;
+    for (int ks = 1; ks <= (p.no_temps ? 1 : 4); ++ks) {
+      if ((fk > 0 && !p.no_temps && ks != fk) || !split_ok(t, p, ks)) continue;
       const double cost = estimate_us(t, p, c, ks);
       if (!best || cost < best_cost) {
         best = &t;
@@ -1180,7 +1181,8 @@ bool igemm_plan_packed(const Problem& p, Plan* plan) { return plan_among(p, 1, p
 bool igemm_plan_tile(const Problem& p, int tile_id, Plan* plan) {
   const TileDesc* t = find_tile(tile_id);
   if (!t || !tile_fits(*t, p) || !t->fn[p.dtype]) return false;
-  const int fk = forced_ksplit();
+  if (p.no_temps && t->packed && !p.wp) return false;
+  const int fk = p.no_temps ? 1 : forced_ksplit();
   plan->algo = LIBCONV_ALGO_IGEMM;
   plan->tile = t->id;
   plan->ksplit = fk > 1 && split_ok(*t, p, fk) ? fk : 1;
@@ -1202,7 +1204,7 @@ libconv_status igemm_launch(const Problem& p, const Plan& plan) {
   if (!fn) return LIBCONV_ERR_UNSUPPORTED;
   if (t->packed && !p.wp) return LIBCONV_ERR_UNSUPPORTED;
   const int ks = plan.ksplit > 1 ? plan.ksplit : 1;
-  if (!split_ok(*t, p, ks)) return LIBCONV_ERR_UNSUPPORTED;
+  if (!split_ok(*t, p, ks) || (ks > 1 && p.no_temps)) return LIBCONV_ERR_UNSUPPORTED;
   const TileCounts c = counts(*t, p);
   if (c.total * ks > 0x7fffffffLL) return LIBCONV_ERR_UNSUPPORTED;
   IgemmArgs a;

@@ -26,6 +26,7 @@ struct Problem {
   void* y;
   hipStream_t stream;
   int cus;         // compute units of the current device (filled before a launch)
+  bool no_temps;   // plan without stream-ordered temporaries (the stream is capturing)
 };
 
 // What the dispatcher decided.

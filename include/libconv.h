@@ -25,17 +25,22 @@
  *               libconv keeps no pointer after the call returns, copies
  *               nothing between host and device and never synchronises the
  *               host.
- *   Memory      libconv_forward_packed and libconv_pack_weights allocate
- *               nothing.  conv2d_forward / conv3d_forward allocate nothing
- *               either, except when the dispatcher runs the shape on packed
- *               weights (3-D layers): the packed copy then lives in a
- *               stream-ordered temporary (hipMallocAsync / hipFreeAsync on
- *               `stream`), which needs no device-wide synchronisation.
+ *   Memory      libconv_pack_weights allocates nothing.  A convolution
+ *               call may take one stream-ordered temporary: the packed copy
+ *               of OIHW weights when the dispatcher runs the shape on packed
+ *               weights, or the fp32 partial sums of a split-K plan.  It is
+ *               taken from and returned to a per-device pool on `stream`
+ *               (no device-wide synchronisation; the pool keeps freed memory
+ *               cached, so calls after the first do not reach the driver).
  *   Stream      work is enqueued on `stream` (a hipStream_t; NULL means the
  *               null stream) and the call returns as soon as it is enqueued.
  *               Inputs must stay valid until the stream reaches the kernel.
  *               The calls make no host sync, so they may be recorded into a
- *               HIP graph.
+ *               HIP graph.  While `stream` is capturing, the dispatcher
+ *               picks plans that need no temporary (no split-K, no per-call
+ *               weight packing), so a captured call may run a different
+ *               kernel than the same call made eagerly; pass packed weights
+ *               (libconv_forward_packed) to keep the packed MFMA kernels.
  *   Dtypes      x, w, bias and y share one storage dtype (libconv_dtype).
  *               Products and sums are formed in fp32 (fp16/bf16 products are
  *               exact in fp32) and y is rounded once, to nearest even.

@@ -1,0 +1,159 @@
+"""libconv calls recorded into a HIP graph (through torch's graph capture,
+whose capture stream is the stream libconv enqueues on) and replayed: every
+replay, with the program's own eager work and synchronisations between
+replays, must give exactly the eager result (the kernels are deterministic,
+so bit for bit).  Covers a chained fp32 stack without temporaries and layers
+that take a stream-ordered temporary (split-K partial sums, weights packed
+per call)."""
+import sys
+
+import pytest
+
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _needs_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def note(msg):
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _stack(specs, seed):
+    """Device inputs and outputs for a list of (layer, chained) specs."""
+    dev = "cuda:0"
+    xs, ws, bs, outs = [], [], [], []
+    for i, layer in enumerate(specs):
+        x, w, b = W.make_inputs(layer, seed + i)
+        xs.append(x.torch(dev))
+        ws.append(w.torch(dev))
+        bs.append(b.torch(dev))
+    return xs, ws, bs
+
+
+def _run(L, specs, xs, ws, bs, outs, chained):
+    for i, l in enumerate(specs):
+        x_in = outs[i - 1] if (chained and i > 0) else xs[i]
+        st, pd = (l.stride[1:], l.pad[1:]) if l.dims == 2 else (l.stride, l.pad)
+        L.conv_nd(x_in, ws[i], bs[i], st, pd, l.act, out=outs[i])
+
+
+def _check_graph(specs, chained, seed):
+    import direct_implicit_gemm_amd as L
+    xs, ws, bs = _stack(specs, seed)
+    outs = []
+    for l in specs:
+        full = tuple(L.libconv_out_size(n, k, p, s) for n, k, p, s in
+                     zip((l.T, l.H, l.W), (l.KT, l.KH, l.KW), l.pad, l.stride))
+        shape = (l.N, l.C_out) + (full[1:] if l.dims == 2 else full)
+        outs.append(torch.empty(shape, dtype=xs[len(outs)].dtype, device="cuda:0"))
+    _run(L, specs, xs, ws, bs, outs, chained)
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        _run(L, specs, xs, ws, bs, outs, chained)
+    torch.cuda.synchronize()
+    junk = torch.randn(1 << 20, device="cuda:0")
+    for r in range(4):
+        for o in outs:
+            o.fill_(float("nan") if o.dtype == torch.float32 else 0.0)  # the replay must rewrite
+        g.replay()
+        torch.cuda.synchronize()
+        for i, o in enumerate(outs):
+            assert torch.equal(o, eager[i]), f"replay {r}, layer {i}: differs from eager"
+        # the program's own eager work between replays
+        junk.mul_(1.0001).add_(0.5)
+        _run(L, specs[:1], xs, ws, bs, [torch.empty_like(outs[0])] + outs[1:], False)
+        torch.cuda.synchronize()
+        note(f"replay {r}: all {len(outs)} outputs equal the eager result")
+
+
+def test_graph_chained_fp32_stack():
+    l1 = W.Layer("g1", "f32", 1, 3, 1, 66, 96, 16, 1, 3, 3, (0, 1, 1), (1, 2, 2), "relu", 2,
+                 "U01", "U11", "U0.1")
+    l2 = W.Layer("g2", "f32", 1, 16, 1, 33, 48, 32, 1, 3, 3, (0, 1, 1), (1, 1, 1), "relu", 2,
+                 "U01", "U11", "U0.1")
+    l3 = W.Layer("g3", "f32", 1, 32, 1, 33, 48, 64, 1, 1, 1, (0, 0, 0), (1, 1, 1), "none", 2,
+                 "U01", "U11", "U0.1")
+    _check_graph([l1, l2, l3], True, 500)
+
+
+def test_graph_layers_that_take_temporaries_eagerly(monkeypatch):
+    """Eagerly these calls take a stream-ordered temporary (split-K partial
+    sums, forced here; weights packed per call on a 3-D layer).  Under
+    capture the dispatcher plans without temporaries, so the replays run
+    other kernels: each replay must equal the first bit for bit, and both the
+    eager and the replayed results must pass the oracle gates.  A forward on
+    weights packed beforehand keeps the packed kernels inside the graph."""
+    import direct_implicit_gemm_amd as L
+    import oracle
+    from convcheck import assert_gates, metrics, oracle_args, to_f64
+    monkeypatch.setenv("LIBCONV_FORCE_KSPLIT", "2")
+    specs = [
+        W.Layer("g4", "bf16", 1, 160, 1, 9, 48, 72, 1, 3, 3, (0, 1, 1), (1, 1, 1), "relu", 2,
+                "N01", "N01", "U0.05"),
+        W.Layer("g5", "f16", 1, 64, 3, 6, 40, 64, 3, 3, 3, (1, 1, 1), (1, 1, 1), "none", 3,
+                "N01", "N01", "U0.05"),
+    ]
+    ins = [W.make_inputs(l, 600 + i) for i, l in enumerate(specs)]
+    dev = "cuda:0"
+    xs = [x.torch(dev) for x, _, _ in ins]
+    ws = [w.torch(dev) for _, w, _ in ins]
+    bs = [b.torch(dev) for _, _, b in ins]
+    packed = L.pack_weights(ws[1])          # before any capture
+    torch.cuda.synchronize()
+
+    def run(outs):
+        for i, l in enumerate(specs):
+            st, pd = oracle_args(l)
+            L.conv_nd(xs[i], ws[i], bs[i], st, pd, l.act, out=outs[i])
+        st, pd = oracle_args(specs[1])
+        L.conv_nd_packed(xs[1], packed, bs[1], st, pd, specs[1].act, out=outs[2])
+
+    def fresh():
+        return [torch.empty((1, 72, 9, 48), dtype=xs[0].dtype, device=dev),
+                torch.empty((1, 64, 3, 6, 40), dtype=xs[1].dtype, device=dev),
+                torch.empty((1, 64, 3, 6, 40), dtype=xs[1].dtype, device=dev)]
+
+    def gates(outs, what):
+        for i, l in enumerate(specs + [specs[1]]):
+            x, w, b = ins[min(i, 1)]
+            ref, s = oracle.conv(x.f64(), w.f64(), b.f64(), *oracle_args(l),
+                                 relu=l.act == "relu")
+            m = metrics(to_f64(outs[i]), ref, s, l.dtype)
+            note(f"{what} output {i}: {m}")
+            assert_gates(m, l.dtype, f"{what} {i}")
+
+    eager = fresh()
+    run(eager)
+    torch.cuda.synchronize()
+    gates(eager, "eager")
+    outs = fresh()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(outs)
+    torch.cuda.synchronize()
+    first = None
+    for r in range(4):
+        for o in outs:
+            o.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        if first is None:
+            first = [o.clone() for o in outs]
+            gates(outs, "replay 0")
+        else:
+            for i, o in enumerate(outs):
+                assert torch.equal(o, first[i]), f"replay {r}, output {i} differs from replay 0"
+        run(fresh())  # the program's own eager work between replays (with temporaries)
+        torch.cuda.synchronize()
+        note(f"replay {r} ok")
