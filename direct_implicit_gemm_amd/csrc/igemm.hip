@@ -125,7 +125,10 @@ template <int DT_, int KT_, int KH_, int KW_, int SH_, int SW_, int BM_, int TH_
 struct Cfg {
   static constexpr int DT = DT_, KT = KT_, KH = KH_, KW = KW_, SH = SH_, SW = SW_;
   static constexpr int BM = BM_, TH = TH_, TW = TW_, WM = WM_, WN = WN_, CG = CG_;
-  static constexpr bool PK = PK_ != 0;
+  // PK_ bit 0: packed weights; bit 1: single-stage tile (all input channels
+  // of the layer in one stage; one LDS buffer, no overlap machinery)
+  static constexpr bool PK = (PK_ & 1) != 0;
+  static constexpr bool ONE = (PK_ & 2) != 0;
   static constexpr bool VX = VX_ != 0;
   static constexpr int EB = Elem<DT>::bytes;
   static constexpr int SE = Mma<DT>::SE;
@@ -167,8 +170,9 @@ struct Cfg {
   static constexpr int WCHUNKS = NSLOT * BM / 64;
   static constexpr int NDMA = (WCHUNKS + 3) / 4;
   static constexpr int DMA_PAD = (PK && WCHUNKS % 4 != 0) ? 1024 : 0;
-  // LDS: two weight and two input buffers
-  static constexpr int LDS = 2 * WBYTES + 2 * XBYTES + DMA_PAD;
+  // LDS: two weight and two input buffers (one of each for single-stage tiles)
+  static constexpr int NBUF = ONE ? 1 : 2;
+  static constexpr int LDS = NBUF * (WBYTES + XBYTES) + DMA_PAD;
   // input staging: one unit = one run (VX) or one halo pixel of one channel
   // group; VX units come in blocks of 8 rows x NRUN runs
   static constexpr int XUNITS = VX ? (NROWS + 7) / 8 * 8 * NRUN : CG * HR * HC;
@@ -615,7 +619,9 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
   // ---- main loop over stages (chunk, kt), chunk-major.  Stage s+1 is written
   // to LDS after stage s's MFMAs, then one barrier hands it over.
   auto wbuf = [&](int i) -> unsigned char* { return lds + i * G::WBYTES; };
-  auto xbuf = [&](int i) -> unsigned char* { return lds + 2 * G::WBYTES + i * G::XBYTES; };
+  auto xbuf = [&](int i) -> unsigned char* {
+    return lds + G::NBUF * G::WBYTES + i * G::XBYTES;
+  };
   // Stage s: packed weights are copied into LDS one stage ahead (they are
   // read from L2), everything else goes through registers two stages ahead.
   // Every step issues the same instructions, so that the compiler can track
@@ -634,6 +640,17 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
     }
   };
   auto main_loop = [&](auto ragged) __attribute__((always_inline)) {
+    if constexpr (G::ONE) {  // the one stage: read, write to LDS, multiply
+      StageRegs<G> r1;
+      const Src qw = w_src(chunk0, kt_lo), qx = x_src(chunk0, kt_lo);
+      static_for<0, NWP>([&](auto kc) { read_w(ragged, kc, qw, r1, wbuf(0)); });
+      static_for<0, NXP>([&](auto kc) { read_x(ragged, kc, qx, r1); });
+      wait_vmcnt<0>();
+      store_stage(r1, wbuf(0), xbuf(0));
+      lds_barrier();
+      compute(wbuf(0), xbuf(0), [](auto) {});
+      return;
+    }
     StageRegs<G> ra, rb;
     Cursor cw{chunk0, kt_lo, 0}, cx{chunk0, kt_lo, 0};  // next stage to read: weights, input
     // all reads of the stage at cursor cx (and, for packed weights, of the
@@ -891,6 +908,7 @@ struct TileDesc {
                   // (measured on MI355X on large grids; used to rank tiles)
   int occ;        // workgroups one CU holds at once (registers and LDS of the
                   // built kernel; checked against the runtime by a GPU test)
+  int one;        // 1: single-stage tile (the layer's input channels fit one stage)
   int lds;
   const char* name;
   LaunchFn fn[3];  // by libconv_dtype
@@ -918,7 +936,7 @@ constexpr OccFn occupier() {
 
 #define LIBCONV_TILE(ID, WIDE, KT, KH, KW, SH, SW, FLAT, BM, TH, TW, WM, WN, CG, PK, VX, EFF,   \
                      OCC, NAME)                                                                 \
-  {ID, WIDE, KT, KH, KW, SH, SW, FLAT, BM, TH, TW, CG, PK, VX, EFF, OCC,                         \
+  {ID, WIDE, KT, KH, KW, SH, SW, FLAT, BM, TH, TW, CG, (PK) & 1, VX, EFF, OCC, (PK) >> 1,        \
    Cfg<WIDE ? DT_F16 : DT_F32, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK, VX>::LDS, NAME, \
    {launcher<DT_F32, WIDE, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK, VX>(),               \
     launcher<DT_F16, WIDE, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK, VX>(),               \
@@ -941,12 +959,17 @@ const TileDesc kTiles[] = {
     LIBCONV_TILE(220, 1, 1, 1, 1, 1, 1, 1, 128, 1, 256, 2, 2, 8, 0, 1, 20, 1, "igemm16_k1_m128_n256"),
     LIBCONV_TILE(221, 1, 1, 1, 1, 1, 1, 1, 128, 1, 128, 2, 2, 8, 0, 1, 20, 2, "igemm16_k1_m128_n128"),
     LIBCONV_TILE(225, 1, 1, 1, 1, 1, 1, 1, 128, 1, 128, 2, 2, 8, 0, 0, 13, 2, "igemm16_k1_m128_n128_e"),
+    LIBCONV_TILE(226, 1, 1, 1, 1, 1, 1, 1, 128, 1, 64, 2, 2, 16, 2, 1, 15, 3, "igemm16_k1_m128_n64_one"),
+    LIBCONV_TILE(227, 1, 1, 1, 1, 1, 1, 1, 128, 1, 128, 2, 2, 16, 2, 1, 18, 2, "igemm16_k1_m128_n128_one"),
     // fp32 operands
     LIBCONV_TILE(240, 0, 1, 3, 3, 1, 1, 0, 32, 8, 32, 1, 4, 4, 0, 1, 50, 1, "igemm32_k3s1_m32_n8x32"),
     LIBCONV_TILE(241, 0, 1, 3, 3, 1, 1, 0, 64, 4, 32, 2, 2, 4, 0, 1, 40, 1, "igemm32_k3s1_m64_n4x32"),
     LIBCONV_TILE(242, 0, 1, 3, 3, 2, 2, 0, 64, 2, 32, 2, 2, 4, 0, 1, 35, 1, "igemm32_k3s2_m64_n2x32"),
     LIBCONV_TILE(243, 0, 1, 1, 1, 1, 1, 1, 64, 1, 128, 2, 2, 8, 0, 1, 15, 3, "igemm32_k1_m64_n128"),
     LIBCONV_TILE(250, 0, 1, 1, 1, 1, 1, 1, 64, 1, 128, 2, 2, 8, 0, 0, 10, 3, "igemm32_k1_m64_n128_e"),
+    // single-stage 1x1 tiles (C_in <= the stage's channels): one LDS buffer
+    LIBCONV_TILE(253, 0, 1, 1, 1, 1, 1, 1, 64, 1, 128, 2, 2, 8, 2, 1, 15, 6, "igemm32_k1_m64_n128_one"),
+    LIBCONV_TILE(254, 0, 1, 1, 1, 1, 1, 1, 64, 1, 64, 2, 2, 8, 2, 1, 12, 6, "igemm32_k1_m64_n64_one"),
     // fp32, 8 channels per stage: small LDS stages, several workgroups per CU
     LIBCONV_TILE(244, 0, 1, 3, 3, 1, 1, 0, 32, 8, 32, 1, 4, 2, 0, 1, 48, 2, "igemm32_k3s1_m32_n8x32_c8"),
     LIBCONV_TILE(245, 0, 1, 3, 3, 2, 2, 0, 64, 2, 32, 2, 2, 2, 0, 1, 44, 2, "igemm32_k3s2_m64_n2x32_c8"),
@@ -995,6 +1018,7 @@ bool tile_fits(const TileDesc& t, const Problem& p) {
     if (row % (16 / dtype_bytes(p.dtype)) != 0 || (reinterpret_cast<uintptr_t>(p.x) & 15) != 0)
       return false;
   }
+  if (t.one && (p.C > t.CG * se || p.KT != 1)) return false;
   if (t.flat) return is_flat(p);
   return p.KT == t.KT && p.KH == t.KH && p.KW == t.KW && p.sh == t.SH && p.sw == t.SW &&
          (t.KT > 1 || (p.st == 1 && p.pt == 0));

@@ -44,14 +44,17 @@ def _tiles():
 
 def _layer_for(tid: int, name: str, ragged: bool) -> W.Layer:
     """A small layer that the tile `name` fits."""
-    m = re.match(r"igemm(16|32)(p?)_k(\d+)(s(\d))?_m(\d+)_n(\d+)x?(\d+)?(_c8)?(_e)?$", name)
+    m = re.match(r"igemm(16|32)(p?)_k(\d+)(s(\d))?_m(\d+)_n(\d+)x?(\d+)?(_c8)?(_e)?(_one)?$", name)
     assert m, name
     wide, packed, kdig = m.group(1) == "16", m.group(2) == "p", m.group(3)
     stride, bm = m.group(5), int(m.group(6))
     elem = m.group(10) is not None
+    one = m.group(11) is not None
     dtype = ("bf16" if tid % 2 else "f16") if wide else "f32"
     se = 8 if wide else 4
     c = (3 * se if ragged else 4 * se) if not packed else (3 * se - 4 if ragged else 4 * se)
+    if one:  # single-stage tiles: every input channel in the one stage
+        c = 5 * se if ragged else (128 if wide else 32)  # the stage's full width
     k = bm + bm // 2 + 8                       # ragged output-channel tiles
     w_ = 72 if not elem else 67               # ragged pixel tiles; odd W for "_e" tiles
     relu = "relu" if tid % 3 else "none"
