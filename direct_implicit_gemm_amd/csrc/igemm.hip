@@ -117,6 +117,7 @@ struct IgemmArgs {
   // activation) to part[split][n][co][ot][oh][ow]; 1 = no split
   int ksplit, cps;
   float* part;
+  int vec_out;        // 1: output rows are whole 16-byte vectors and y is 16-byte aligned
   uint32_t x_bytes, w_bytes, b_bytes, y_bytes, part_bytes;
 };
 
@@ -172,7 +173,10 @@ struct Cfg {
   static constexpr int DMA_PAD = (PK && WCHUNKS % 4 != 0) ? 1024 : 0;
   // LDS: two weight and two input buffers (one of each for single-stage tiles)
   static constexpr int NBUF = ONE ? 1 : 2;
-  static constexpr int LDS = NBUF * (WBYTES + XBYTES) + DMA_PAD;
+  // the vectorised epilogue reuses LDS as four wave-private 32x32 tiles
+  static constexpr int EPI_LDS = 4 * 32 * (32 + 16 / EB) * EB;
+  static constexpr int STAGES_LDS = NBUF * (WBYTES + XBYTES) + DMA_PAD;
+  static constexpr int LDS = STAGES_LDS > EPI_LDS ? STAGES_LDS : EPI_LDS;
   // input staging: one unit = one run (VX) or one halo pixel of one channel
   // group; VX units come in blocks of 8 rows x NRUN runs
   static constexpr int XUNITS = VX ? (NROWS + 7) / 8 * 8 * NRUN : CG * HR * HC;
@@ -245,6 +249,11 @@ __device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, unsigned
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16,
                                            off, 0, 0, 0);
 }
+
+// This wave's LDS accesses so far are complete and none of the later ones
+// is moved above this point (a wave-private LDS region changes hands between
+// lanes of the same wave).
+__device__ __forceinline__ void lds_fence() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 // Slot vector of tap t from a unit's TS vectors: the unit holds
 // w[co][c0 .. c0+SE)[0 .. TS) with the tap index fastest; the slot wants the
@@ -739,6 +748,60 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
   }
   const __amdgpu_buffer_rsrc_t yr = make_rsrc(a.y, a.y_bytes);
   const __amdgpu_buffer_rsrc_t br = make_rsrc(a.b, a.b_bytes);
+  if (a.vec_out) {
+    // Rows of whole 16-byte vectors: each 32x32 block goes through a
+    // wave-private LDS tile and leaves as 16-byte row segments, VEC outputs
+    // per store instead of one.  The stage buffers are free once every wave
+    // has finished its last reads of them and its last copies into them (each
+    // wave waits for its own copies at the end of the main loop): one barrier.
+    lds_barrier();
+    constexpr int VEC = 16 / EB;                   // outputs per 16-byte store
+    constexpr int PITCH_E = 32 + VEC;              // LDS row pitch in elements (16 B aligned)
+    constexpr int SEGS = 32 / VEC;                 // 16-byte segments per row
+    constexpr int ROWS_PER_READ = 64 / SEGS;       // rows one wave-wide read covers
+    unsigned char* tile = lds + wave * (32 * PITCH_E * EB);
+#pragma unroll
+    for (int i = 0; i < G::FA; ++i) {
+      float bias[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int co = co0 + co_w0 + i * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+        bias[r] = E::load(br, guard_offset(a.b && co < a.K, co * EB));
+      }
+#pragma unroll
+      for (int j = 0; j < G::FB; ++j) {
+        // accumulator element r of this lane: row 8 (r / 4) + 4 hf + r % 4, column il
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 8 * (r >> 2) + 4 * hf + (r & 3);
+          const float v = epilogue(acc[i][j][r], bias[r], a.relu);
+          if constexpr (EB == 4)
+            *reinterpret_cast<float*>(tile + (row * PITCH_E + il) * 4) = v;
+          else
+            *reinterpret_cast<uint16_t*>(tile + (row * PITCH_E + il) * 2) = E::from_f32(v);
+        }
+        lds_fence();
+        const int b = blk0 + j;
+        const int oh = oh0 + b / G::BPR;
+        const int owb = ow0 + (b % G::BPR) * 32;
+#pragma unroll
+        for (int k = 0; k < 32 / ROWS_PER_READ; ++k) {
+          const int row = lane / SEGS + k * ROWS_PER_READ;
+          const int seg = lane % SEGS;
+          const u32x4_t v = *reinterpret_cast<const u32x4_t*>(tile + (row * PITCH_E + seg * VEC) * EB);
+          const int co = co0 + co_w0 + i * 32 + row;
+          const int ow = owb + seg * VEC;
+          const int off = (((n * a.K + co) * a.OT + ot) * ohw + oh * a.OW + ow) * EB;
+          // a.OW is a multiple of VEC, so a segment is wholly inside or
+          // wholly outside the row; outside the output the store is dropped
+          __builtin_amdgcn_raw_buffer_store_b128(
+              v, yr, guard_offset(co < a.K && oh < a.OH && ow < a.OW, off), 0, 0);
+        }
+        lds_fence();
+      }
+    }
+    return;
+  }
   // All bias loads first (one round trip); channels beyond C_out read 0 and
   // are not stored.
   float bias[G::FA][16];
@@ -958,7 +1021,7 @@ const TileDesc kTiles[] = {
     // 16-bit operands, 1x1 stride 1 pad 0 (flattened planes)
     LIBCONV_TILE(220, 1, 1, 1, 1, 1, 1, 1, 128, 1, 256, 2, 2, 8, 0, 1, 20, 1, "igemm16_k1_m128_n256"),
     LIBCONV_TILE(221, 1, 1, 1, 1, 1, 1, 1, 128, 1, 128, 2, 2, 8, 0, 1, 20, 2, "igemm16_k1_m128_n128"),
-    LIBCONV_TILE(225, 1, 1, 1, 1, 1, 1, 1, 128, 1, 128, 2, 2, 8, 0, 0, 13, 2, "igemm16_k1_m128_n128_e"),
+    LIBCONV_TILE(225, 1, 1, 1, 1, 1, 1, 1, 128, 1, 128, 2, 2, 8, 0, 0, 13, 1, "igemm16_k1_m128_n128_e"),
     LIBCONV_TILE(226, 1, 1, 1, 1, 1, 1, 1, 128, 1, 64, 2, 2, 16, 2, 1, 15, 3, "igemm16_k1_m128_n64_one"),
     LIBCONV_TILE(227, 1, 1, 1, 1, 1, 1, 1, 128, 1, 128, 2, 2, 16, 2, 1, 18, 2, "igemm16_k1_m128_n128_one"),
     // fp32 operands
@@ -969,7 +1032,7 @@ const TileDesc kTiles[] = {
     LIBCONV_TILE(250, 0, 1, 1, 1, 1, 1, 1, 64, 1, 128, 2, 2, 8, 0, 0, 10, 3, "igemm32_k1_m64_n128_e"),
     // single-stage 1x1 tiles (C_in <= the stage's channels): one LDS buffer
     LIBCONV_TILE(253, 0, 1, 1, 1, 1, 1, 1, 64, 1, 128, 2, 2, 8, 2, 1, 15, 6, "igemm32_k1_m64_n128_one"),
-    LIBCONV_TILE(254, 0, 1, 1, 1, 1, 1, 1, 64, 1, 64, 2, 2, 8, 2, 1, 12, 6, "igemm32_k1_m64_n64_one"),
+    LIBCONV_TILE(254, 0, 1, 1, 1, 1, 1, 1, 64, 1, 64, 2, 2, 8, 2, 1, 12, 7, "igemm32_k1_m64_n64_one"),
     // fp32, 8 channels per stage: small LDS stages, several workgroups per CU
     LIBCONV_TILE(244, 0, 1, 3, 3, 1, 1, 0, 32, 8, 32, 1, 4, 2, 0, 1, 48, 2, "igemm32_k3s1_m32_n8x32_c8"),
     LIBCONV_TILE(245, 0, 1, 3, 3, 2, 2, 0, 64, 2, 32, 2, 2, 2, 0, 1, 44, 2, "igemm32_k3s2_m64_n2x32_c8"),
@@ -1259,6 +1322,7 @@ libconv_status igemm_launch(const Problem& p, const Plan& plan) {
   a.y_bytes = (uint32_t)((long long)p.N * p.K * p.OT * p.OH * p.OW * eb);
   a.part = nullptr;
   a.part_bytes = 0;
+  a.vec_out = (a.OW % (16 / eb)) == 0 && (reinterpret_cast<uintptr_t>(p.y) & 15) == 0;
   if (ks == 1) {
     const hipError_t e = fn(a, (unsigned)c.total, p.stream);
     return e == hipSuccess ? LIBCONV_OK : LIBCONV_ERR_LAUNCH;
