@@ -183,6 +183,10 @@ struct Cfg {
   static constexpr int XPASS = (XUNITS + kThreads - 1) / kThreads;
   // global reads into registers each wave issues per stage
   static constexpr int REG_LOADS = XPASS * SE + WPASS * TS;
+  // slot pair before whose MFMAs the next stage's registers are written to
+  // LDS (the free buffer), so that two pairs of MFMAs still cover the write
+  // latency before the end-of-stage barrier; -1: after the last pair
+  static constexpr int SPAIR = NPAIR >= 3 ? NPAIR - 2 : -1;
 
   static_assert(WM * WN == 4, "four waves");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
@@ -588,7 +592,8 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
   auto compute = [&](const unsigned char* wl, const unsigned char* xl, auto&& hook)
       __attribute__((always_inline)) {
     u32x4_t fa[2][G::FA], fb[2][G::FB];
-    auto load_frags = [&](int p, int k) {
+    auto load_frags = [&](auto pc, int k) {
+      constexpr int p = decltype(pc)::value;
       const int s0 = 2 * p;
       const int s1 = (2 * p + 1 < G::NSLOT) ? 2 * p + 1 : 2 * p;
       const int xo = hf ? xslot(s1) : xslot(s0);
@@ -606,10 +611,10 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
         for (int j = 0; j < G::FB; ++j) fb[k][j] = u32x4_t{0u, 0u, 0u, 0u};
       }
     };
-    load_frags(0, 0);
+    load_frags(std::integral_constant<int, 0>{}, 0);
     static_for<0, G::NPAIR>([&](auto pc) {
       constexpr int p = decltype(pc)::value;
-      if constexpr (p + 1 < G::NPAIR) load_frags(p + 1, (p + 1) & 1);
+      if constexpr (p + 1 < G::NPAIR) load_frags(std::integral_constant<int, p + 1>{}, (p + 1) & 1);
       hook(pc);
       // keep the next pair's LDS reads (and the hook's global reads) ahead of
       // this pair's MFMAs: left alone, the scheduler sinks them below the
@@ -687,7 +692,12 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
     // Stage s: `mine` is free and receives the input (and OIHW weights) of
     // stage s+2, packed weights of stage s+1 go to the free LDS weight
     // buffer; `other` holds stage s+1.  The reads are spread over the slot
-    // pairs, weights first.
+    // pairs, weights first.  Stage s+1 is written from `other` to the free
+    // buffer before slot pair SPAIR: by then every read of `other` has had
+    // most of a stage to arrive, and the last pairs' MFMAs cover the LDS
+    // write latency, so the barrier that ends the stage finds the writes
+    // done.  The free buffer held stage s-1, whose reads all finished before
+    // the barrier that ended stage s-1.
     auto step = [&](int s, StageRegs<G>& mine, StageRegs<G>& other)
         __attribute__((always_inline)) {
       const Src qw = G::PK ? w_src(cw.chunk, cw.kt) : w_src(cx.chunk, cx.kt);
@@ -696,6 +706,11 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
       compute(wbuf(s & 1), xbuf(s & 1), [&](auto pc) {
         constexpr int p = decltype(pc)::value;
         constexpr int lo = p * (NWP + NXP) / G::NPAIR, hi = (p + 1) * (NWP + NXP) / G::NPAIR;
+        if constexpr (p == G::SPAIR) {
+          // `other`'s reads precede the lo reads this step has issued so far
+          wait_vmcnt<lo>();
+          store_stage(other, wbuf((s + 1) & 1), xbuf((s + 1) & 1));
+        }
         static_for<lo, hi>([&](auto kc) {
           constexpr int k = decltype(kc)::value;
           if constexpr (k < NWP)
@@ -706,8 +721,11 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
       });
       if constexpr (G::PK) advance(cw);
       advance(cx);
+      // packed weights of stage s+1 (copied straight to LDS, the first reads
+      // of this step) have landed; the REG_LOADS register reads of stage s+2
+      // issued after them may still be in flight
       wait_vmcnt<G::REG_LOADS>();
-      store_stage(other, wbuf((s + 1) & 1), xbuf((s + 1) & 1));
+      if constexpr (G::SPAIR < 0) store_stage(other, wbuf((s + 1) & 1), xbuf((s + 1) & 1));
       lds_barrier();
     };
     int s = 0;
@@ -1015,13 +1033,15 @@ const TileDesc kTiles[] = {
     LIBCONV_TILE(202, 1, 1, 3, 3, 1, 1, 0, 128, 2, 64, 2, 2, 2, 0, 1, 14, 1, "igemm16_k3s1_m128_n2x64"),
     LIBCONV_TILE(203, 1, 1, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 0, 1, 28, 1, "igemm16_k3s1_m64_n8x32"),
     LIBCONV_TILE(205, 1, 1, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 0, 0, 18, 1, "igemm16_k3s1_m64_n8x32_e"),
+    // 128 channels x 64 pixels per wave (4 x 2 MFMA blocks): 0.75 KB of LDS reads per MFMA
+    LIBCONV_TILE(206, 1, 1, 3, 3, 1, 1, 0, 128, 8, 32, 1, 4, 2, 0, 1, 20, 1, "igemm16_k3s1_m128w_n8x32"),
     // 16-bit operands, 3x3 stride 2
     LIBCONV_TILE(210, 1, 1, 3, 3, 2, 2, 0, 64, 4, 32, 2, 2, 2, 0, 1, 20, 2, "igemm16_k3s2_m64_n4x32"),
     LIBCONV_TILE(215, 1, 1, 3, 3, 2, 2, 0, 64, 4, 32, 2, 2, 2, 0, 0, 13, 1, "igemm16_k3s2_m64_n4x32_e"),
     // 16-bit operands, 1x1 stride 1 pad 0 (flattened planes)
     LIBCONV_TILE(220, 1, 1, 1, 1, 1, 1, 1, 128, 1, 256, 2, 2, 8, 0, 1, 20, 1, "igemm16_k1_m128_n256"),
     LIBCONV_TILE(221, 1, 1, 1, 1, 1, 1, 1, 128, 1, 128, 2, 2, 8, 0, 1, 20, 2, "igemm16_k1_m128_n128"),
-    LIBCONV_TILE(225, 1, 1, 1, 1, 1, 1, 1, 128, 1, 128, 2, 2, 8, 0, 0, 13, 1, "igemm16_k1_m128_n128_e"),
+    LIBCONV_TILE(225, 1, 1, 1, 1, 1, 1, 1, 128, 1, 128, 2, 2, 8, 0, 0, 13, 2, "igemm16_k1_m128_n128_e"),
     LIBCONV_TILE(226, 1, 1, 1, 1, 1, 1, 1, 128, 1, 64, 2, 2, 16, 2, 1, 15, 3, "igemm16_k1_m128_n64_one"),
     LIBCONV_TILE(227, 1, 1, 1, 1, 1, 1, 1, 128, 1, 128, 2, 2, 16, 2, 1, 18, 2, "igemm16_k1_m128_n128_one"),
     // fp32 operands
@@ -1037,7 +1057,7 @@ const TileDesc kTiles[] = {
     LIBCONV_TILE(244, 0, 1, 3, 3, 1, 1, 0, 32, 8, 32, 1, 4, 2, 0, 1, 48, 2, "igemm32_k3s1_m32_n8x32_c8"),
     LIBCONV_TILE(245, 0, 1, 3, 3, 2, 2, 0, 64, 2, 32, 2, 2, 2, 0, 1, 44, 2, "igemm32_k3s2_m64_n2x32_c8"),
     LIBCONV_TILE(246, 0, 1, 3, 3, 2, 2, 0, 64, 4, 32, 2, 2, 2, 0, 1, 44, 2, "igemm32_k3s2_m64_n4x32_c8"),
-    LIBCONV_TILE(247, 0, 1, 3, 3, 1, 1, 0, 32, 4, 32, 1, 4, 2, 0, 1, 48, 2, "igemm32_k3s1_m32_n4x32_c8"),
+    LIBCONV_TILE(247, 0, 1, 3, 3, 1, 1, 0, 32, 4, 32, 1, 4, 2, 0, 1, 48, 3, "igemm32_k3s1_m32_n4x32_c8"),
     LIBCONV_TILE(248, 0, 1, 3, 3, 1, 1, 0, 32, 8, 32, 1, 4, 2, 0, 0, 32, 2, "igemm32_k3s1_m32_n8x32_c8_e"),
     LIBCONV_TILE(249, 0, 1, 3, 3, 2, 2, 0, 64, 2, 32, 2, 2, 2, 0, 0, 29, 2, "igemm32_k3s2_m64_n2x32_c8_e"),
     // packed weights: 16-bit, 3x3x3 stride 1 (one frame tap per stage)
@@ -1047,11 +1067,14 @@ const TileDesc kTiles[] = {
     LIBCONV_TILE(263, 1, 3, 3, 3, 1, 1, 0, 64, 4, 32, 1, 4, 2, 1, 1, 30, 2, "igemm16p_k333s1_m64_n4x32"),
     LIBCONV_TILE(264, 1, 3, 3, 3, 1, 1, 0, 128, 8, 32, 2, 2, 1, 1, 1, 24, 1, "igemm16p_k333s1_m128_n8x32_c8"),
     LIBCONV_TILE(265, 1, 3, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 1, 0, 22, 2, "igemm16p_k333s1_m64_n8x32_e"),
+    // 128 channels x 64 pixels per wave (4 x 2 MFMA blocks), one workgroup per CU
+    LIBCONV_TILE(267, 1, 3, 3, 3, 1, 1, 0, 128, 8, 32, 1, 4, 2, 1, 1, 31, 1, "igemm16p_k333s1_m128w_n8x32"),
     // packed weights: 16-bit, 3x3 stride 1
     LIBCONV_TILE(270, 1, 1, 3, 3, 1, 1, 0, 128, 8, 32, 2, 2, 2, 1, 1, 30, 1, "igemm16p_k3s1_m128_n8x32"),
     LIBCONV_TILE(271, 1, 1, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 1, 1, 36, 2, "igemm16p_k3s1_m64_n8x32"),
     LIBCONV_TILE(272, 1, 1, 3, 3, 1, 1, 0, 128, 4, 32, 2, 2, 2, 1, 1, 23, 1, "igemm16p_k3s1_m128_n4x32"),
     LIBCONV_TILE(275, 1, 1, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 1, 0, 24, 2, "igemm16p_k3s1_m64_n8x32_e"),
+    LIBCONV_TILE(276, 1, 1, 3, 3, 1, 1, 0, 128, 8, 32, 1, 4, 2, 1, 1, 34, 1, "igemm16p_k3s1_m128w_n8x32"),
 };
 
 #undef LIBCONV_TILE

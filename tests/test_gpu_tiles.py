@@ -44,7 +44,7 @@ def _tiles():
 
 def _layer_for(tid: int, name: str, ragged: bool) -> W.Layer:
     """A small layer that the tile `name` fits."""
-    m = re.match(r"igemm(16|32)(p?)_k(\d+)(s(\d))?_m(\d+)_n(\d+)x?(\d+)?(_c8)?(_e)?(_one)?$", name)
+    m = re.match(r"igemm(16|32)(p?)_k(\d+)(s(\d))?_m(\d+)w?_n(\d+)x?(\d+)?(_c8)?(_e)?(_one)?$", name)
     assert m, name
     wide, packed, kdig = m.group(1) == "16", m.group(2) == "p", m.group(3)
     stride, bm = m.group(5), int(m.group(6))
