@@ -18,8 +18,12 @@ The step is timed twice, K eager steps and K replays of the step captured
 once as a HIP graph (no host launch overhead; ``--no-graph`` skips it), and
 the faster is reported (``config.step_mode``; both times are in ``config``).
 Per-layer times: ``us_b2b``, one event pair around R back-to-back launches of
-the layer alone, divided by R, which matches the kernel durations of a
-rocprofv3 kernel trace.  The roofline fractions use ``us_b2b``.
+the layer alone, divided by R (for short kernels this is bounded by the host's
+call rate); ``us_graph``, the same R launches captured once as a HIP graph and
+replayed between one event pair (no host in the timed region; only when the
+call plans the same kernel under capture).  ``us`` is the smaller, and the
+roofline fractions use it; it matches the kernel durations of a rocprofv3
+kernel trace.
 """
 from __future__ import annotations
 
@@ -241,42 +245,80 @@ def main():
     else:
         ms_per_step, wall, mode = ms_eager, wall_eager, "eager"
 
-    # each layer alone, R launches back to back between one event pair
+    # Each layer alone, R launches back to back, timed two ways on the launch
+    # stream: (1) issued eagerly between one event pair -- for short kernels
+    # this is bounded by the host's call rate (Python, ctypes, planning,
+    # launch); (2) the same R launches captured once as a HIP graph and
+    # replayed between one event pair, which removes the host from the timed
+    # region.  (2) is taken only when the call plans the same kernel under
+    # capture as eagerly (libconv_query_plan), so both time one kernel.
     R = max(10, K)
-    b2b = []
+    GRAPH_REPLAYS = 3
+
+    def plan_of(l, capturing):
+        st_, algo, tile, grid, ks = L.libconv_query_plan(
+            l.N, l.C_in, l.T, l.H, l.W, l.C_out, l.KT, l.KH, l.KW, *l.pad, *l.stride,
+            W.DTYPE_CODE[l.dtype], W.ACT_CODE[l.act], L.ALGO_AUTO, int(capturing))
+        return algo, tile, grid, ks
+
+    b2b, b2b_graph = [], []
     for i, l in enumerate(layers):
         x_in = outs[i - 1] if (chained and i > 0) else xs[i]
         s_, p_ = sp(l)
+
+        def launch_r():
+            for _ in range(R):
+                L.conv_nd(x_in, ws[i], bs[i], s_, p_, l.act, out=outs[i])
+
         L.conv_nd(x_in, ws[i], bs[i], s_, p_, l.act, out=outs[i])
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
-        for _ in range(R):
-            L.conv_nd(x_in, ws[i], bs[i], s_, p_, l.act, out=outs[i])
+        launch_r()
         e1.record()
         torch.cuda.synchronize()
         b2b.append(1000.0 * e0.elapsed_time(e1) / R)
+        ug = None
+        if not args.no_graph and plan_of(l, False) == plan_of(l, True):
+            try:
+                gl = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(gl):
+                    launch_r()
+                gl.replay()
+                torch.cuda.synchronize()
+                e0.record()
+                for _ in range(GRAPH_REPLAYS):
+                    gl.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                ug = 1000.0 * e0.elapsed_time(e1) / (R * GRAPH_REPLAYS)
+                del gl
+            except Exception:  # capture refused: keep the eager figure
+                torch.cuda.synchronize()
+                ug = None
+        b2b_graph.append(ug)
 
     per_layer = []
     step_flops = 0
     for i, l in enumerate(layers):
-        us = b2b[i]
+        ue, ug = b2b[i], b2b_graph[i]
+        us, mode = (ug, "graph") if ug is not None and ug < ue else (ue, "eager")
         flops, nbytes = layer_work(l, lib)
         step_flops += flops
         bound, tflops, gbs, frac = roofline_of(l, flops, nbytes, us * 1e-6)
-        st_, algo, tile, grid = L.libconv_query_algo(
-            l.N, l.C_in, l.T, l.H, l.W, l.C_out, l.KT, l.KH, l.KW, *l.pad, *l.stride,
-            W.DTYPE_CODE[l.dtype], W.ACT_CODE[l.act], L.ALGO_AUTO)
+        algo, tile, grid, ks = plan_of(l, False)
         per_layer.append({
-            "layer": l.name, "kernel": L.libconv_tile_name(tile), "grid": grid,
-            "us_b2b": round(us, 3), "b2b_reps": R,
+            "layer": l.name, "kernel": L.libconv_tile_name(tile), "grid": grid, "ksplit": ks,
+            "us": round(us, 3), "timing": mode,
+            "us_b2b": round(ue, 3), "us_graph": None if ug is None else round(ug, 3),
+            "b2b_reps": R,
             "gflop": round(flops / 1e9, 4), "mbytes": round(nbytes / 1e6, 3),
             "tflops": round(tflops, 3), "gbs": round(gbs, 1),
             "bound": bound, "frac": round(frac, 4),
         })
 
-    dom = max(range(len(layers)), key=lambda i: per_layer[i]["us_b2b"])
+    dom = max(range(len(layers)), key=lambda i: per_layer[i]["us"])
     dl = per_layer[dom]
     flops, nbytes = layer_work(layers[dom], lib)
     if dl["bound"] == "mfma":

@@ -62,6 +62,9 @@ def load() -> ctypes.CDLL:
     lib.libconv_query_algo.argtypes = [I] * 18 + [ctypes.POINTER(I), ctypes.POINTER(I),
                                                   ctypes.POINTER(LL)]
     lib.libconv_query_algo.restype = I
+    lib.libconv_query_plan.argtypes = [I] * 19 + [ctypes.POINTER(I), ctypes.POINTER(I),
+                                                  ctypes.POINTER(LL), ctypes.POINTER(I)]
+    lib.libconv_query_plan.restype = I
     lib.libconv_tile_name.argtypes = [I]
     lib.libconv_tile_name.restype = ctypes.c_char_p
     lib.libconv_tile_occupancy.argtypes = [I, I, I]
@@ -138,6 +141,18 @@ def libconv_query_algo(N, C_in, T, H, W, C_out, KT, KH, KW, pad_t, pad_h, pad_w,
                                    stride_t, stride_h, stride_w, dtype, act, algo,
                                    ctypes.byref(a), ctypes.byref(t), ctypes.byref(g))
     return st, a.value, t.value, g.value
+
+
+def libconv_query_plan(N, C_in, T, H, W, C_out, KT, KH, KW, pad_t, pad_h, pad_w,
+                       stride_t, stride_h, stride_w, dtype, act, algo,
+                       capturing) -> Tuple[int, int, int, int, int]:
+    """Returns (status, algo, tile_id, grid, ksplit)."""
+    a, t, g, k = ctypes.c_int(-1), ctypes.c_int(-1), ctypes.c_longlong(-1), ctypes.c_int(-1)
+    st = load().libconv_query_plan(N, C_in, T, H, W, C_out, KT, KH, KW, pad_t, pad_h, pad_w,
+                                   stride_t, stride_h, stride_w, dtype, act, algo, capturing,
+                                   ctypes.byref(a), ctypes.byref(t), ctypes.byref(g),
+                                   ctypes.byref(k))
+    return st, a.value, t.value, g.value, k.value
 
 
 def libconv_tile_name(tile_id: int) -> str:

@@ -197,6 +197,53 @@ libconv_status plan_for(const Problem& p, int algo, Plan* plan, bool packed_only
   return LIBCONV_ERR_UNSUPPORTED;
 }
 
+// Plans of recent calls, per host thread: a layer called again with the same
+// shape reuses its plan instead of re-running the cost model.  The key holds
+// everything the dispatcher reads (shape, dtype, activation, forced family,
+// capture state, which weight forms exist, 16-byte alignment of x, compute
+// units).  Not used while a LIBCONV_FORCE_* override is set.
+struct PlanKey {
+  int v[24];
+  bool operator==(const PlanKey& o) const { return std::memcmp(v, o.v, sizeof(v)) == 0; }
+};
+
+PlanKey plan_key(const Problem& p, int algo) {
+  PlanKey k;
+  const int v[24] = {p.N, p.C, p.T, p.H, p.W, p.K, p.KT, p.KH, p.KW, p.pt, p.ph, p.pw, p.st, p.sh,
+                     p.sw, p.dtype, p.act, algo, (int)p.no_temps, p.w == nullptr,
+                     (int)(reinterpret_cast<uintptr_t>(p.x) & 15), p.cus, p.wp != nullptr, 0};
+  std::memcpy(k.v, v, sizeof(v));
+  return k;
+}
+
+struct PlanCacheEntry {
+  bool used = false;
+  PlanKey key;
+  Plan plan;
+};
+constexpr int kPlanCacheSlots = 64;
+thread_local PlanCacheEntry t_plan_cache[kPlanCacheSlots];
+
+libconv_status cached_plan(const Problem& p, int algo, Plan* plan) {
+  if (std::getenv("LIBCONV_FORCE_TILE") || std::getenv("LIBCONV_FORCE_KSPLIT"))
+    return plan_for(p, algo, plan, p.w == nullptr);
+  const PlanKey k = plan_key(p, algo);
+  uint32_t h = 2166136261u;  // FNV-1a over the key words
+  for (int x : k.v) h = (h ^ (uint32_t)x) * 16777619u;
+  PlanCacheEntry& e = t_plan_cache[h % kPlanCacheSlots];
+  if (e.used && e.key == k) {
+    *plan = e.plan;
+    return LIBCONV_OK;
+  }
+  const libconv_status st = plan_for(p, algo, plan, p.w == nullptr);
+  if (st == LIBCONV_OK) {
+    e.used = true;
+    e.key = k;
+    e.plan = *plan;
+  }
+  return st;
+}
+
 libconv_status run(Problem& p, int algo) {
   libconv_status st = validate(p, algo, true);
   if (st != LIBCONV_OK) return st;
@@ -217,7 +264,7 @@ libconv_status run(Problem& p, int algo) {
   }
   p.no_temps = p.no_temps || cap != hipStreamCaptureStatusNone;
   Plan plan;
-  st = plan_for(p, algo, &plan, p.w == nullptr);
+  st = cached_plan(p, algo, &plan);
   if (st != LIBCONV_OK) return st;
   if (std::getenv("LIBCONV_LOG")) {
     const char* name = plan.algo == LIBCONV_ALGO_DIRECT ? direct_tile_name(plan.tile)
@@ -371,17 +418,30 @@ libconv_status libconv_query_algo(int N, int C_in, int T, int H, int W, int C_ou
                                   int KW, int pad_t, int pad_h, int pad_w, int stride_t,
                                   int stride_h, int stride_w, int dtype, int act, int algo,
                                   int* algo_out, int* tile_out, long long* grid_out) {
-  if (!algo_out || !tile_out || !grid_out) return LIBCONV_ERR_NULL_POINTER;
+  int ksplit = 1;
+  return libconv_query_plan(N, C_in, T, H, W, C_out, KT, KH, KW, pad_t, pad_h, pad_w, stride_t,
+                            stride_h, stride_w, dtype, act, algo, 0, algo_out, tile_out, grid_out,
+                            &ksplit);
+}
+
+libconv_status libconv_query_plan(int N, int C_in, int T, int H, int W, int C_out, int KT, int KH,
+                                  int KW, int pad_t, int pad_h, int pad_w, int stride_t,
+                                  int stride_h, int stride_w, int dtype, int act, int algo,
+                                  int capturing, int* algo_out, int* tile_out,
+                                  long long* grid_out, int* ksplit_out) {
+  if (!algo_out || !tile_out || !grid_out || !ksplit_out) return LIBCONV_ERR_NULL_POINTER;
   Problem p = make_problem(nullptr, nullptr, nullptr, nullptr, N, C_in, T, H, W, C_out, KT, KH, KW,
                            pad_t, pad_h, pad_w, stride_t, stride_h, stride_w, dtype, act, nullptr);
   libconv_status st = validate(p, algo, false);
   if (st != LIBCONV_OK) return st;
+  p.no_temps = capturing != 0;
   Plan plan;
   st = plan_for(p, algo, &plan);
   if (st != LIBCONV_OK) return st;
   *algo_out = plan.algo;
   *tile_out = plan.tile;
   *grid_out = p.N == 0 ? 0 : plan.grid;
+  *ksplit_out = plan.ksplit;
   return LIBCONV_OK;
 }
 

@@ -1045,19 +1045,19 @@ const TileDesc kTiles[] = {
     LIBCONV_TILE(226, 1, 1, 1, 1, 1, 1, 1, 128, 1, 64, 2, 2, 16, 2, 1, 15, 3, "igemm16_k1_m128_n64_one"),
     LIBCONV_TILE(227, 1, 1, 1, 1, 1, 1, 1, 128, 1, 128, 2, 2, 16, 2, 1, 18, 2, "igemm16_k1_m128_n128_one"),
     // fp32 operands
-    LIBCONV_TILE(240, 0, 1, 3, 3, 1, 1, 0, 32, 8, 32, 1, 4, 4, 0, 1, 50, 1, "igemm32_k3s1_m32_n8x32"),
+    LIBCONV_TILE(240, 0, 1, 3, 3, 1, 1, 0, 32, 8, 32, 1, 4, 4, 0, 1, 48, 1, "igemm32_k3s1_m32_n8x32"),
     LIBCONV_TILE(241, 0, 1, 3, 3, 1, 1, 0, 64, 4, 32, 2, 2, 4, 0, 1, 40, 1, "igemm32_k3s1_m64_n4x32"),
-    LIBCONV_TILE(242, 0, 1, 3, 3, 2, 2, 0, 64, 2, 32, 2, 2, 4, 0, 1, 35, 1, "igemm32_k3s2_m64_n2x32"),
+    LIBCONV_TILE(242, 0, 1, 3, 3, 2, 2, 0, 64, 2, 32, 2, 2, 4, 0, 1, 43, 1, "igemm32_k3s2_m64_n2x32"),
     LIBCONV_TILE(243, 0, 1, 1, 1, 1, 1, 1, 64, 1, 128, 2, 2, 8, 0, 1, 15, 3, "igemm32_k1_m64_n128"),
     LIBCONV_TILE(250, 0, 1, 1, 1, 1, 1, 1, 64, 1, 128, 2, 2, 8, 0, 0, 10, 3, "igemm32_k1_m64_n128_e"),
     // single-stage 1x1 tiles (C_in <= the stage's channels): one LDS buffer
     LIBCONV_TILE(253, 0, 1, 1, 1, 1, 1, 1, 64, 1, 128, 2, 2, 8, 2, 1, 15, 6, "igemm32_k1_m64_n128_one"),
     LIBCONV_TILE(254, 0, 1, 1, 1, 1, 1, 1, 64, 1, 64, 2, 2, 8, 2, 1, 12, 7, "igemm32_k1_m64_n64_one"),
     // fp32, 8 channels per stage: small LDS stages, several workgroups per CU
-    LIBCONV_TILE(244, 0, 1, 3, 3, 1, 1, 0, 32, 8, 32, 1, 4, 2, 0, 1, 48, 2, "igemm32_k3s1_m32_n8x32_c8"),
-    LIBCONV_TILE(245, 0, 1, 3, 3, 2, 2, 0, 64, 2, 32, 2, 2, 2, 0, 1, 44, 2, "igemm32_k3s2_m64_n2x32_c8"),
-    LIBCONV_TILE(246, 0, 1, 3, 3, 2, 2, 0, 64, 4, 32, 2, 2, 2, 0, 1, 44, 2, "igemm32_k3s2_m64_n4x32_c8"),
-    LIBCONV_TILE(247, 0, 1, 3, 3, 1, 1, 0, 32, 4, 32, 1, 4, 2, 0, 1, 48, 3, "igemm32_k3s1_m32_n4x32_c8"),
+    LIBCONV_TILE(244, 0, 1, 3, 3, 1, 1, 0, 32, 8, 32, 1, 4, 2, 0, 1, 57, 2, "igemm32_k3s1_m32_n8x32_c8"),
+    LIBCONV_TILE(245, 0, 1, 3, 3, 2, 2, 0, 64, 2, 32, 2, 2, 2, 0, 1, 51, 2, "igemm32_k3s2_m64_n2x32_c8"),
+    LIBCONV_TILE(246, 0, 1, 3, 3, 2, 2, 0, 64, 4, 32, 2, 2, 2, 0, 1, 54, 2, "igemm32_k3s2_m64_n4x32_c8"),
+    LIBCONV_TILE(247, 0, 1, 3, 3, 1, 1, 0, 32, 4, 32, 1, 4, 2, 0, 1, 49, 3, "igemm32_k3s1_m32_n4x32_c8"),
     LIBCONV_TILE(248, 0, 1, 3, 3, 1, 1, 0, 32, 8, 32, 1, 4, 2, 0, 0, 32, 2, "igemm32_k3s1_m32_n8x32_c8_e"),
     LIBCONV_TILE(249, 0, 1, 3, 3, 2, 2, 0, 64, 2, 32, 2, 2, 2, 0, 0, 29, 2, "igemm32_k3s2_m64_n2x32_c8_e"),
     // packed weights: 16-bit, 3x3x3 stride 1 (one frame tap per stage)
@@ -1219,27 +1219,36 @@ static bool split_ok(const TileDesc& t, const Problem& p, int ksplit) {
 
 // Estimated time of a tile and split on this shape, in microseconds.  The
 // busiest compute unit runs ceil(units / CUs) work units (tiles, times the
-// split count); occ of them at a time share its matrix cores, so their MFMA
-// work adds up at the tile's measured efficiency, while the fixed latency of
-// a workgroup (first reads, last stores: about kRoundUs) is paid once per
-// round of occ concurrent workgroups.  Packed tiles on OIHW weights add the
+// split count), occ of them at a time (one round).  A round takes the longer
+// of (a) the MFMA work of its units, which share the CU's matrix cores, at the
+// tile's measured efficiency, and (b) the latency chain of one workgroup:
+// about kFirstUs (launch, first reads, last stores) plus kStageUs per stage,
+// the time a stage's reads take to arrive when no MFMA work hides them
+// (fitted to single-round launches on MI355X: a one-stage 1x1 tile takes 5-7
+// us, a four-stage 3x3 tile 10-12 us).  Packed tiles on OIHW weights add the
 // pack step: a stream-ordered temporary (allocate, free) and the pack kernel,
-// about 8 us on MI355X, plus reading and writing the weights once.  A split
-// adds the sum kernel: a launch and its temporary, plus writing and reading
-// the fp32 partial sums once and writing the output.
-constexpr double kRoundUs = 4.0;
+// about 12 us per call on MI355X, plus reading and writing the weights once.
+// A split adds the sum kernel: a launch and its temporary, plus writing and
+// reading the fp32 partial sums once and writing the output.
+constexpr double kFirstUs = 4.5;
+constexpr double kStageUs = 1.6;
 static double estimate_us(const TileDesc& t, const Problem& p, const TileCounts& c, int ksplit) {
   const double ck = t.CG * (t.wide ? 8 : 4);
   const int chunks = chunks_of(t, p);
   const double cps = std::ceil((double)chunks / ksplit);
   const double unit_flop = 2.0 * t.BM * t.TH * t.TW * cps * ck * p.KT * p.KH * p.KW;
   const double cu_flop_per_us = (t.wide ? 4096.0 : 256.0) * 2400.0 * (t.eff / 100.0);
+  const double unit_us = unit_flop / cu_flop_per_us;
+  const double latency_us = kFirstUs + kStageUs * cps * p.KT;
   const double cus = p.cus > 0 ? p.cus : 256.0;
   const double per_cu = std::ceil(c.total * ksplit / cus);
-  double us = per_cu * unit_flop / cu_flop_per_us + std::ceil(per_cu / t.occ) * kRoundUs;
+  const double full_rounds = std::floor(per_cu / t.occ);
+  const double rest = per_cu - full_rounds * t.occ;
+  double us = full_rounds * std::max(t.occ * unit_us, latency_us);
+  if (rest > 0) us += std::max(rest * unit_us, latency_us);
   if (t.packed && !p.wp) {
     const double wbytes = (double)packed_weight_bytes(p.C, p.K, p.KT, p.KH, p.KW, p.dtype);
-    us += 8.0 + 2.0 * wbytes / 6.0e6;
+    us += 12.0 + 2.0 * wbytes / 6.0e6;
   }
   if (ksplit > 1)
     us += 10.0 + (2.0 * part_bytes(p, ksplit) + out_elems(p) * dtype_bytes(p.dtype)) / 4.0e6;

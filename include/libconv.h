@@ -197,6 +197,23 @@ libconv_status libconv_query_algo(int N, int C_in, int T, int H, int W,
                                   int dtype, int act, int algo,
                                   int* algo_out, int* tile_out, long long* grid_out);
 
+/*
+ * libconv_query_algo with two more facts about the plan: *ksplit_out, the
+ * number of workgroups that share one output tile's reduction (split-K; 1 =
+ * none), and the plan for a call made while its stream is being captured
+ * into a HIP graph when `capturing` is non-zero (such a call takes no
+ * stream-ordered temporaries: no split-K and no per-call weight packing, so
+ * it can run another kernel than the same call made eagerly).  Pure host
+ * arithmetic: works without a GPU.  Output pointers may not be NULL.
+ */
+libconv_status libconv_query_plan(int N, int C_in, int T, int H, int W,
+                                  int C_out, int KT, int KH, int KW,
+                                  int pad_t, int pad_h, int pad_w,
+                                  int stride_t, int stride_h, int stride_w,
+                                  int dtype, int act, int algo, int capturing,
+                                  int* algo_out, int* tile_out, long long* grid_out,
+                                  int* ksplit_out);
+
 /* Human-readable name of a tile configuration id; "?" if unknown. */
 const char* libconv_tile_name(int tile_id);
 
