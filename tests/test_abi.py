@@ -183,3 +183,27 @@ def test_tile_occupancy_query_without_gpu():
                 assert 1 <= occ <= 8, (name, dt, occ)
             else:
                 assert occ == -1, (name, dt, occ)
+
+
+def test_query_plan_capture_excludes_temporaries():
+    """Under graph capture the plan takes no stream-ordered temporaries: no
+    split-K and no packed tile fed from OIHW weights; eagerly the same calls
+    may use both.  The eager plan agrees with libconv_query_algo."""
+    for name in ("c4_B", "c5_A", "c2_L2", "c3_B"):
+        l = W.ALL_LAYERS[name]
+        args = (l.N, l.C_in, l.T, l.H, l.W, l.C_out, l.KT, l.KH, l.KW, *l.pad, *l.stride,
+                W.DTYPE_CODE[l.dtype], W.ACT_CODE[l.act], L.ALGO_AUTO)
+        st, algo, tile, grid, ks = L.libconv_query_plan(*args, 0)
+        assert st == 0 and ks >= 1
+        assert L.libconv_query_algo(*args)[1:] == (algo, tile, grid)
+        st, calgo, ctile, cgrid, cks = L.libconv_query_plan(*args, 1)
+        assert st == 0 and cks == 1, (name, cks)
+        name_c = L.libconv_tile_name(ctile)
+        assert "16p" not in name_c and "32p" not in name_c, (name, name_c)
+    # the UNet 1280-channel layer splits eagerly (few tiles for the CUs)
+    l = W.ALL_LAYERS["c4_B"]
+    args = (l.N, l.C_in, l.T, l.H, l.W, l.C_out, l.KT, l.KH, l.KW, *l.pad, *l.stride,
+            W.DTYPE_CODE[l.dtype], W.ACT_CODE[l.act], L.ALGO_AUTO)
+    assert L.libconv_query_plan(*args, 0)[4] > 1
+    out = L.libconv_query_plan(1, 4, 1, 8, 8, 8, 1, 3, 3, 0, 1, 1, 1, 1, 1, 5, 0, 0, 0)
+    assert out[0] == 3  # bad dtype

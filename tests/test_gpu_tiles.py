@@ -42,6 +42,19 @@ def _tiles():
     return out
 
 
+def _one_stage_width(tid: int, kdig: str, wide: bool) -> int:
+    """The most input channels a single-stage tile takes: the widest C that
+    the tile (forced through LIBCONV_FORCE_TILE) accepts for its geometry."""
+    import direct_implicit_gemm_amd as L
+    k = 1 if kdig == "1" else 3
+    for c in ((128, 64, 32) if wide else (32, 16)):
+        q = L.libconv_query_plan(1, c, 1, 12, 64, 16, 1, k, k, 0, k // 2, k // 2, 1, 1, 1,
+                                 1 if wide else 0, 0, 0, 0)
+        if q[0] == 0 and q[2] == tid:
+            return c
+    raise AssertionError(f"no channel count fits tile {tid}")
+
+
 def _layer_for(tid: int, name: str, ragged: bool) -> W.Layer:
     """A small layer that the tile `name` fits."""
     m = re.match(r"igemm(16|32)(p?)_k(\d+)(s(\d))?_m(\d+)w?_n(\d+)x?(\d+)?(_c8)?(_e)?(_one)?$", name)
@@ -54,7 +67,7 @@ def _layer_for(tid: int, name: str, ragged: bool) -> W.Layer:
     se = 8 if wide else 4
     c = (3 * se if ragged else 4 * se) if not packed else (3 * se - 4 if ragged else 4 * se)
     if one:  # single-stage tiles: every input channel in the one stage
-        c = 5 * se if ragged else (128 if wide else 32)  # the stage's full width
+        c = 5 * se if ragged else _one_stage_width(tid, kdig, wide)  # the stage's full width
     k = bm + bm // 2 + 8                       # ragged output-channel tiles
     w_ = 72 if not elem else 67               # ragged pixel tiles; odd W for "_e" tiles
     relu = "relu" if tid % 3 else "none"
@@ -77,8 +90,8 @@ def test_every_tile(ragged, monkeypatch):
     tiles = _tiles()
     assert len(tiles) >= 20
     for i, (tid, name) in enumerate(tiles):
-        layer = _layer_for(tid, name, ragged)
         monkeypatch.setenv("LIBCONV_FORCE_TILE", str(tid))
+        layer = _layer_for(tid, name, ragged)
         q = L.libconv_query_algo(layer.N, layer.C_in, layer.T, layer.H, layer.W, layer.C_out,
                                  layer.KT, layer.KH, layer.KW, *layer.pad, *layer.stride,
                                  W.DTYPE_CODE[layer.dtype], W.ACT_CODE[layer.act], 0)
