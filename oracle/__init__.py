@@ -46,6 +46,8 @@ def _load():
         lp = ctypes.POINTER(ctypes.c_long)
         lib.oracle_out_extent.argtypes = [ctypes.c_long] * 4
         lib.oracle_out_extent.restype = ctypes.c_long
+        lib.oracle_out_extent2.argtypes = [ctypes.c_long] * 5
+        lib.oracle_out_extent2.restype = ctypes.c_long
         lib.oracle_threads.argtypes = [ctypes.c_int]
         lib.oracle_threads.restype = ctypes.c_int
         lib.oracle_conv.argtypes = [dp, dp, dp, dp, dp, lp, ctypes.c_int, ctypes.c_int]
@@ -68,6 +70,11 @@ def out_extent(n_in: int, k: int, pad: int, stride: int) -> int:
     return int(_load().oracle_out_extent(n_in, k, pad, stride))
 
 
+def out_extent2(n_in: int, k: int, pad_lo: int, pad_hi: int, stride: int) -> int:
+    """Output positions with pad_lo before and pad_hi after the input."""
+    return int(_load().oracle_out_extent2(n_in, k, pad_lo, pad_hi, stride))
+
+
 def threads(requested: int = 0) -> int:
     """OpenMP threads the oracle will use (after applying ``requested`` if > 0)."""
     return int(_load().oracle_threads(requested))
@@ -82,13 +89,13 @@ def _as5d(x: np.ndarray, w: np.ndarray):
     raise ValueError("x must be NCHW or NCDHW")
 
 
-def _dims(x5, w5, stride, pad):
+def _dims(x5, w5, stride, pad, pad_t_back):
     N, C, T, H, W = x5.shape
     CO, C2, KT, KH, KW = w5.shape
     if C2 != C:
         raise ValueError("channel mismatch")
     return np.array([N, C, T, H, W, CO, KT, KH, KW, pad[0], pad[1], pad[2],
-                     stride[0], stride[1], stride[2]], dtype=np.int64)
+                     stride[0], stride[1], stride[2], pad_t_back], dtype=np.int64)
 
 
 def _norm3(v, nd) -> Tuple[int, int, int]:
@@ -102,10 +109,10 @@ def _norm3(v, nd) -> Tuple[int, int, int]:
     raise ValueError(v)
 
 
-def _spatial(x5, w5, stride3, pad3, nd):
+def _spatial(x5, w5, stride3, pad3, pad_t_back):
     _, _, T, H, W = x5.shape
     _, _, KT, KH, KW = w5.shape
-    o = (out_extent(T, KT, pad3[0], stride3[0]),
+    o = (out_extent2(T, KT, pad3[0], pad_t_back, stride3[0]),
          out_extent(H, KH, pad3[1], stride3[1]),
          out_extent(W, KW, pad3[2], stride3[2]))
     if min(o) < 0:
@@ -113,27 +120,41 @@ def _spatial(x5, w5, stride3, pad3, nd):
     return o
 
 
+def _time_pad_back(p3, nd, pad_t_back):
+    """Time padding after the last frame: the pad before it unless given
+    (the causal padding of "SeedVR2 NCNN Vulkan", section 7.2, is 0)."""
+    if pad_t_back is None:
+        return p3[0]
+    if nd == 2 or int(pad_t_back) < 0:
+        raise ValueError("pad_t_back needs 3-D operands and a non-negative value")
+    return int(pad_t_back)
+
+
 def conv(x: np.ndarray, w: np.ndarray, b: Optional[np.ndarray], stride=1, pad=0,
-         relu: bool = False, nthreads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+         relu: bool = False, nthreads: int = 0,
+         pad_t_back: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
     """fp64 forward convolution.  Returns (y, S), both float64, shaped like y.
 
     x: NCHW or NCDHW; w: OIHW or OIDHW; b: [C_out] or None.
     stride / pad: an int, or one value per spatial axis ((h, w) or (t, h, w)).
-    For 2-D operands the time stride is 1 and the time pad is 0.
+    For 2-D operands the time stride is 1 and the time pad is 0.  For 3-D
+    operands the time pad applies before the first frame and, unless
+    pad_t_back is given, after the last one.
     """
     x5, w5, nd = _as5d(np.ascontiguousarray(x, np.float64), np.ascontiguousarray(w, np.float64))
     s3 = _norm3(stride, nd)
     p3 = _norm3(pad, nd)
     if nd == 2:
         s3, p3 = (1, s3[1], s3[2]), (0, p3[1], p3[2])
+    ptb = _time_pad_back(p3, nd, pad_t_back)
     x5 = np.ascontiguousarray(x5)
     w5 = np.ascontiguousarray(w5)
     bb = None if b is None else np.ascontiguousarray(b, np.float64)
-    OT, OH, OW = _spatial(x5, w5, s3, p3, nd)
+    OT, OH, OW = _spatial(x5, w5, s3, p3, ptb)
     N, CO = x5.shape[0], w5.shape[0]
     y = np.empty((N, CO, OT, OH, OW), np.float64)
     s = np.empty_like(y)
-    dims = _dims(x5, w5, s3, p3)
+    dims = _dims(x5, w5, s3, p3, ptb)
     rc = _load().oracle_conv(_dp(x5), _dp(w5), _dp(bb), _dp(y), _dp(s),
                              dims.ctypes.data_as(ctypes.POINTER(ctypes.c_long)),
                              int(bool(relu)), int(nthreads))
@@ -146,20 +167,22 @@ def conv(x: np.ndarray, w: np.ndarray, b: Optional[np.ndarray], stride=1, pad=0,
 
 def conv_points(x: np.ndarray, w: np.ndarray, b: Optional[np.ndarray],
                 flat_idx: Sequence[int], stride=1, pad=0, relu: bool = False,
-                nthreads: int = 0) -> Tuple[np.ndarray, np.ndarray]:
+                nthreads: int = 0, pad_t_back: Optional[int] = None
+                ) -> Tuple[np.ndarray, np.ndarray]:
     """The outputs at flat indices of y (row-major over N, C_out, (OT,) OH, OW)."""
     x5, w5, nd = _as5d(np.ascontiguousarray(x, np.float64), np.ascontiguousarray(w, np.float64))
     s3 = _norm3(stride, nd)
     p3 = _norm3(pad, nd)
     if nd == 2:
         s3, p3 = (1, s3[1], s3[2]), (0, p3[1], p3[2])
+    ptb = _time_pad_back(p3, nd, pad_t_back)
     x5 = np.ascontiguousarray(x5)
     w5 = np.ascontiguousarray(w5)
     bb = None if b is None else np.ascontiguousarray(b, np.float64)
     idx = np.ascontiguousarray(np.asarray(flat_idx, dtype=np.int64))
     y = np.empty(idx.shape[0], np.float64)
     s = np.empty_like(y)
-    dims = _dims(x5, w5, s3, p3)
+    dims = _dims(x5, w5, s3, p3, ptb)
     rc = _load().oracle_conv_points(_dp(x5), _dp(w5), _dp(bb),
                                     idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
                                     idx.shape[0], _dp(y), _dp(s),

@@ -33,18 +33,24 @@
  *
  * Pins: tests/test_oracle.py (closed form for all-ones inputs, delta kernels,
  * linearity, brute-force im2col x matmul, torch's fp64 CPU convolution, the
- * stride and 3-D/2-D identities, the hand-computed fixture in tests/golden/).
+ * stride and 3-D/2-D identities, the hand-computed fixture in tests/golden/;
+ * for time padding on one side: the all-ones closed form, torch's conv3d of
+ * the explicitly zero-padded input, and causal = symmetric then cropped).
  */
 #include <math.h>
 #include <stdint.h>
 #include <omp.h>
 
-/* Geometry of one call.  Index order of dims[]: */
+/* Geometry of one call.  Index order of dims[]: D_PT is the time padding
+ * before the first frame, D_PTB the time padding after the last one (equal
+ * for the symmetric padding of the conv shader; the causal padding of the
+ * spatio-temporal VAE in "SeedVR2 NCNN Vulkan", section 7.2, pads only before
+ * the first frame). */
 enum { D_N, D_C, D_T, D_H, D_W, D_CO, D_KT, D_KH, D_KW,
-       D_PT, D_PH, D_PW, D_ST, D_SH, D_SW, D_COUNT };
+       D_PT, D_PH, D_PW, D_ST, D_SH, D_SW, D_PTB, D_COUNT };
 
 typedef struct {
-  long N, C, T, H, W, CO, KT, KH, KW, pt, ph, pw, st, sh, sw;
+  long N, C, T, H, W, CO, KT, KH, KW, pt, ph, pw, st, sh, sw, ptb;
   long OT, OH, OW;
 } geom_t;
 
@@ -62,14 +68,27 @@ long oracle_out_extent(long in, long k, long pad, long stride)
   return count;
 }
 
+/*
+ * The same count with different padding before (pad_lo) and after (pad_hi)
+ * the input: the window must end inside [-pad_lo, in - 1 + pad_hi].
+ */
+long oracle_out_extent2(long in, long k, long pad_lo, long pad_hi, long stride)
+{
+  if (in < 1 || k < 1 || pad_lo < 0 || pad_hi < 0 || stride < 1) return -1;
+  long count = 0;
+  for (long o = 0; o * stride - pad_lo + (k - 1) <= in - 1 + pad_hi; ++o) ++count;
+  return count;
+}
+
 static int make_geom(const long* d, geom_t* g)
 {
   g->N = d[D_N];  g->C = d[D_C];  g->T = d[D_T];  g->H = d[D_H];  g->W = d[D_W];
   g->CO = d[D_CO]; g->KT = d[D_KT]; g->KH = d[D_KH]; g->KW = d[D_KW];
   g->pt = d[D_PT]; g->ph = d[D_PH]; g->pw = d[D_PW];
   g->st = d[D_ST]; g->sh = d[D_SH]; g->sw = d[D_SW];
+  g->ptb = d[D_PTB];
   if (g->N < 1 || g->C < 1 || g->CO < 1) return -1;
-  g->OT = oracle_out_extent(g->T, g->KT, g->pt, g->st);
+  g->OT = oracle_out_extent2(g->T, g->KT, g->pt, g->ptb, g->st);
   g->OH = oracle_out_extent(g->H, g->KH, g->ph, g->sh);
   g->OW = oracle_out_extent(g->W, g->KW, g->pw, g->sw);
   if (g->OT < 0 || g->OH < 0 || g->OW < 0) return -1;

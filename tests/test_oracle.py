@@ -357,3 +357,100 @@ def test_thread_count_does_not_change_result():
     y4, s4 = oracle.conv(x, w, None, 1, 1, nthreads=4)
     np.testing.assert_array_equal(y1, y4)
     np.testing.assert_array_equal(s1, s4)
+
+
+# ------------------------------------------- padding only before / after in time
+# The causal 3-D convolution of the spatio-temporal VAE ("SeedVR2 NCNN Vulkan",
+# section 7.2) pads the frame axis on one side only (the page builds it from
+# Concat/Crop around a plain Convolution3D).
+
+
+def test_out_extent2_closed_form():
+    """Walked count against floor((in + lo + hi - k) / s) + 1."""
+    for n_in, k, lo, hi, s in itertools.product(range(1, 12), range(1, 6), range(0, 4),
+                                               range(0, 4), range(1, 4)):
+        span = n_in + lo + hi - k
+        want = span // s + 1 if span >= 0 else 0
+        assert oracle.out_extent2(n_in, k, lo, hi, s) == want, (n_in, k, lo, hi, s)
+        if lo == hi:
+            assert oracle.out_extent2(n_in, k, lo, hi, s) == oracle.out_extent(n_in, k, lo, s)
+
+
+@pytest.mark.parametrize("dims", [
+    # N, C, T, H, W, CO, KT, KH, KW, pf, pb, ph, pw, st, sh, sw
+    (1, 2, 5, 4, 6, 3, 3, 3, 3, 2, 0, 1, 1, 1, 1, 1),
+    (2, 3, 4, 5, 3, 2, 2, 1, 3, 1, 0, 0, 1, 1, 1, 1),
+    (1, 1, 7, 3, 3, 2, 3, 3, 3, 0, 2, 1, 1, 2, 1, 1),
+    (1, 2, 6, 4, 4, 1, 3, 2, 2, 3, 1, 1, 0, 2, 2, 1),
+])
+def test_all_ones_closed_form_time_pads(dims):
+    """x = w = 1: y = C * cnt_t(ot) * cnt_h(oh) * cnt_w(ow) + b, with cnt_t
+    counting the taps kt whose frame ot*st - pf + kt lies in [0, T)."""
+    N, C, T, H, W, CO, KT, KH, KW, pf, pb, ph, pw, st, sh, sw = dims
+    b = np.arange(CO) * 0.25 - 0.5
+    y, s = oracle.conv(np.ones((N, C, T, H, W)), np.ones((CO, C, KT, KH, KW)), b,
+                       (st, sh, sw), (pf, ph, pw), pad_t_back=pb)
+    OT = (T + pf + pb - KT) // st + 1
+    OH = (H + 2 * ph - KH) // sh + 1
+    OW = (W + 2 * pw - KW) // sw + 1
+    assert y.shape == (N, CO, OT, OH, OW)
+
+    def cnt(o, s_, p_, k, n):
+        return sum(1 for t in range(k) if 0 <= o * s_ - p_ + t < n)
+
+    for ot, oh, ow in itertools.product(range(OT), range(OH), range(OW)):
+        taps = C * cnt(ot, st, pf, KT, T) * cnt(oh, sh, ph, KH, H) * cnt(ow, sw, pw, KW, W)
+        np.testing.assert_array_equal(y[0, :, ot, oh, ow], taps + b)
+        np.testing.assert_array_equal(s[0, :, ot, oh, ow], taps + np.abs(b))
+
+
+@pytest.mark.parametrize("dims", [
+    (1, 3, 5, 6, 7, 4, 3, 3, 3, 2, 0, 1, 1, 1, 1, 1),
+    (2, 2, 6, 5, 5, 3, 3, 3, 3, 1, 2, 1, 1, 2, 1, 2),
+    (1, 4, 4, 4, 6, 2, 2, 3, 1, 0, 1, 1, 0, 1, 2, 1),
+])
+def test_time_pads_match_torch_explicit_padding(dims):
+    """Padding (pf, pb) in time = torch's fp64 conv3d of the input with pf
+    zero frames concatenated before it and pb after it (the Concat of the page)."""
+    N, C, T, H, W, CO, KT, KH, KW, pf, pb, ph, pw, st, sh, sw = dims
+    r = _rng(77)
+    x = r.standard_normal((N, C, T, H, W))
+    w = r.standard_normal((CO, C, KT, KH, KW))
+    b = r.standard_normal(CO)
+    y, _ = oracle.conv(x, w, b, (st, sh, sw), (pf, ph, pw), pad_t_back=pb)
+    xt = torch.nn.functional.pad(torch.from_numpy(x), (0, 0, 0, 0, pf, pb))
+    ref = torch.nn.functional.conv3d(xt, torch.from_numpy(w), torch.from_numpy(b),
+                                     stride=(st, sh, sw), padding=(0, ph, pw)).numpy()
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_causal_is_symmetric_cropped():
+    """Causal padding (KT-1 frames before, none after, stride 1) keeps the
+    first T frames of the symmetric KT-1 padding (the Crop of the page)."""
+    r = _rng(78)
+    N, C, T, H, W, CO, KT = 1, 3, 5, 6, 4, 2, 3
+    x = r.standard_normal((N, C, T, H, W))
+    w = r.standard_normal((CO, C, KT, 3, 3))
+    y, _ = oracle.conv(x, w, None, 1, (KT - 1, 1, 1), pad_t_back=0)
+    full = torch.nn.functional.conv3d(torch.from_numpy(x), torch.from_numpy(w),
+                                      padding=(KT - 1, 1, 1)).numpy()
+    assert y.shape[2] == T
+    np.testing.assert_allclose(y, full[:, :, :T], rtol=1e-12, atol=1e-12)
+    # output frame t sees input frames t-KT+1 .. t only: changing frame T-1
+    # changes only the last output frame
+    x2 = x.copy()
+    x2[:, :, T - 1] += 1.0
+    y2, _ = oracle.conv(x2, w, None, 1, (KT - 1, 1, 1), pad_t_back=0)
+    np.testing.assert_array_equal(y2[:, :, :T - 1], y[:, :, :T - 1])
+    assert np.abs(y2[:, :, T - 1] - y[:, :, T - 1]).max() > 0
+
+
+def test_time_pads_points_match_full():
+    r = _rng(79)
+    x = r.standard_normal((1, 2, 6, 5, 5))
+    w = r.standard_normal((3, 2, 3, 3, 3))
+    y, s = oracle.conv(x, w, None, (2, 1, 1), (2, 1, 1), pad_t_back=0)
+    idx = r.choice(y.size, 40, replace=False)
+    yp, sp = oracle.conv_points(x, w, None, idx, (2, 1, 1), (2, 1, 1), pad_t_back=0)
+    np.testing.assert_array_equal(yp, y.reshape(-1)[idx])
+    np.testing.assert_array_equal(sp, s.reshape(-1)[idx])
