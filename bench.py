@@ -56,11 +56,20 @@ WORKLOAD_TEXT = {
     "unet_bf16": "diffusion-UNet bf16 N=2: conv3x3 640->640 on 64x64; conv3x3 1280->1280 on 32x32",
     "vae3d_f16": ("video-VAE f16 conv3d N=1 T=5: 3x3x3 128->128 on 256x480; "
                   "3x3x3 512->512 on 64x120 +ReLU"),
+    "vae3d_causal_f16": ("video-VAE f16 causal conv3d N=1 T=5 (2 frames of time padding "
+                         "before the first frame, none after): 3x3x3 128->128 on 256x480; "
+                         "3x3x3 512->512 on 64x120 +ReLU"),
 }
+ALL_WORKLOADS = {**W.WORKLOADS, **W.EXTRA_WORKLOADS}
+
+
+def time_pads(layer: W.Layer):
+    """(before, after) padding of the frame axis."""
+    return layer.pad[0], layer.pad[0] if layer.pad_t_back is None else layer.pad_t_back
 
 
 def out_shape(layer: W.Layer, lib):
-    o = [lib.libconv_out_size(layer.T, layer.KT, layer.pad[0], layer.stride[0]),
+    o = [lib.libconv_out_size2(layer.T, layer.KT, *time_pads(layer), layer.stride[0]),
          lib.libconv_out_size(layer.H, layer.KH, layer.pad[1], layer.stride[1]),
          lib.libconv_out_size(layer.W, layer.KW, layer.pad[2], layer.stride[2])]
     return o
@@ -134,7 +143,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="ocr_stack", choices=sorted(W.WORKLOADS))
+    ap.add_argument("--workload", default="ocr_stack", choices=sorted(ALL_WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager steps instead of replays of the step captured as a HIP graph")
@@ -174,7 +183,7 @@ def main():
                           "GBps_read_plus_write": round(2 * n * 4 * args.steps / el / 1e9, 1)}))
         return
 
-    _, layers = W.WORKLOADS[args.workload]
+    _, layers = ALL_WORKLOADS[args.workload]
     # Inputs: the workload's seeded tensors; the stack is chained, so only the
     # first layer's x is used when layers feed each other.
     inputs = [W.make_inputs(l) for l in layers]
@@ -193,11 +202,17 @@ def main():
     def sp(l):
         return (l.stride[1:], l.pad[1:]) if l.dims == 2 else (l.stride, l.pad)
 
+    def conv(l, x_in, w, b, out):
+        if l.pad_t_back is not None:  # time padding differs before / after the frames
+            L.conv3d_tpad(x_in, w, b, time_pads(l), l.stride, l.pad[1:], l.act, out=out)
+        else:
+            s, p = sp(l)
+            L.conv_nd(x_in, w, b, s, p, l.act, out=out)
+
     def step():
         for i, l in enumerate(layers):
             x_in = outs[i - 1] if (chained and i > 0) else xs[i]
-            s, p = sp(l)
-            L.conv_nd(x_in, ws[i], bs[i], s, p, l.act, out=outs[i])
+            conv(l, x_in, ws[i], bs[i], outs[i])
 
     for _ in range(args.warmup):
         step()
@@ -256,21 +271,23 @@ def main():
     GRAPH_REPLAYS = 3
 
     def plan_of(l, capturing):
+        # the query takes one time pad: one-sided padding is asked as the
+        # symmetric padding with the same number of output frames
+        pad = (sum(time_pads(l)) // 2,) + tuple(l.pad[1:])
         st_, algo, tile, grid, ks = L.libconv_query_plan(
-            l.N, l.C_in, l.T, l.H, l.W, l.C_out, l.KT, l.KH, l.KW, *l.pad, *l.stride,
+            l.N, l.C_in, l.T, l.H, l.W, l.C_out, l.KT, l.KH, l.KW, *pad, *l.stride,
             W.DTYPE_CODE[l.dtype], W.ACT_CODE[l.act], L.ALGO_AUTO, int(capturing))
         return algo, tile, grid, ks
 
     b2b, b2b_graph = [], []
     for i, l in enumerate(layers):
         x_in = outs[i - 1] if (chained and i > 0) else xs[i]
-        s_, p_ = sp(l)
 
         def launch_r():
             for _ in range(R):
-                L.conv_nd(x_in, ws[i], bs[i], s_, p_, l.act, out=outs[i])
+                conv(l, x_in, ws[i], bs[i], outs[i])
 
-        L.conv_nd(x_in, ws[i], bs[i], s_, p_, l.act, out=outs[i])
+        conv(l, x_in, ws[i], bs[i], outs[i])
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
@@ -343,7 +360,8 @@ def main():
             t0 = time.perf_counter()
             for l, (x, w, b) in zip(layers, inputs):
                 s, p = sp(l)
-                oracle.conv(x.f64(), w.f64(), b.f64(), s, p, relu=l.act == "relu")
+                oracle.conv(x.f64(), w.f64(), b.f64(), s, p, relu=l.act == "relu",
+                            pad_t_back=l.pad_t_back)
             sec, runs = time.perf_counter() - t0, 1
         cpu = {"value": round(step_flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
                "kind": "oracle",

@@ -83,6 +83,10 @@ def load() -> ctypes.CDLL:
     lib.libconv_pack_weights.restype = I
     lib.libconv_forward_packed.argtypes = [P, P, P, P] + [I] * 17 + [P]
     lib.libconv_forward_packed.restype = I
+    lib.conv3d_forward_tpad.argtypes = [P, P, P, P, P] + [I] * 18 + [P]
+    lib.conv3d_forward_tpad.restype = I
+    lib.libconv_out_size2.argtypes = [I] * 5
+    lib.libconv_out_size2.restype = I
     _lib = lib
     return lib
 
@@ -115,6 +119,18 @@ def libconv_forward_algo(x, w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW, pad
     return load().libconv_forward_algo(x, w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW,
                                        pad_t, pad_h, pad_w, stride_t, stride_h, stride_w,
                                        dtype, act, algo, stream)
+
+
+def conv3d_forward_tpad(x, w, packed_w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW,
+                        pad_t_front, pad_t_back, pad_h, pad_w, stride_t, stride_h, stride_w,
+                        dtype, act, stream) -> int:
+    return load().conv3d_forward_tpad(x, w, packed_w, bias, y, N, C_in, T, H, W, C_out, KT, KH,
+                                      KW, pad_t_front, pad_t_back, pad_h, pad_w, stride_t,
+                                      stride_h, stride_w, dtype, act, stream)
+
+
+def libconv_out_size2(n_in, k, pad_lo, pad_hi, stride) -> int:
+    return load().libconv_out_size2(n_in, k, pad_lo, pad_hi, stride)
 
 
 def libconv_packed_weight_bytes(C_in, C_out, KT, KH, KW, dtype) -> int:
@@ -317,6 +333,48 @@ def conv_nd_packed(x, pw: PackedWeights, b=None, stride=1, padding=0, act="none"
                                      _dtype_code(x), _ACTS[act], stream)
     if st_ != 0:
         raise LibconvError(st_, "libconv_forward_packed")
+    return y
+
+
+def conv3d_tpad(x, w, b=None, pad_t=(0, 0), stride=1, padding_hw=0, act="none", out=None,
+                stream=None):
+    """3-D convolution with pad_t = (frames before, frames after); (KT-1, 0) is
+    the causal convolution.  w: OIDHW device tensor or PackedWeights."""
+    import torch
+    if x.dim() != 5:
+        raise ValueError("x must be NCDHW")
+    packed = isinstance(w, PackedWeights)
+    w_shape = w.w_shape if packed else tuple(w.shape)
+    if len(w_shape) != 5 or w_shape[1] != x.shape[1]:
+        raise ValueError("w must be OIDHW with x's channel count")
+    for t in (x,) + (() if packed else (w,)) + ((b,) if b is not None else ()):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != x.dtype:
+            raise ValueError("x, w, b must be contiguous device tensors of one dtype")
+    if packed and w.dtype != x.dtype:
+        raise ValueError("packed weights do not match x")
+    st, sh, sw = _triple(stride, 3)
+    ph, pw_ = _triple(padding_hw, 2)
+    pf, pb = (int(pad_t[0]), int(pad_t[1]))
+    N, C, T, H, W = x.shape
+    K, _, KT, KH, KW = w_shape
+    lib = load()
+    ot = lib.libconv_out_size2(T, KT, pf, pb, st)
+    oh = lib.libconv_out_size(H, KH, ph, sh)
+    ow = lib.libconv_out_size(W, KW, pw_, sw)
+    if min(ot, oh, ow) < 1:
+        raise LibconvError(2, "conv3d_tpad")
+    shape = (N, K, ot, oh, ow)
+    y = torch.empty(shape, dtype=x.dtype, device=x.device) if out is None else out
+    if tuple(y.shape) != shape or not y.is_contiguous() or y.dtype != x.dtype:
+        raise ValueError("bad output tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    st_ = lib.conv3d_forward_tpad(_ptr(x), None if packed else _ptr(w),
+                                  w.data.data_ptr() if packed else None, _ptr(b), _ptr(y),
+                                  N, C, T, H, W, K, KT, KH, KW, pf, pb, ph, pw_, st, sh, sw,
+                                  _dtype_code(x), _ACTS[act], stream)
+    if st_ != 0:
+        raise LibconvError(st_, "conv3d_forward_tpad")
     return y
 
 

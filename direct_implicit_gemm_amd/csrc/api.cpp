@@ -40,11 +40,17 @@ long long product(std::initializer_list<long long> v) {
   return r;
 }
 
-long long out_extent(long long in, long long k, long long pad, long long stride) {
-  if (in < 1 || k < 1 || pad < 0 || stride < 1) return -1;
-  const long long span = in + 2 * pad - k;
+// Output positions with pad_lo before and pad_hi after the input.
+long long out_extent2(long long in, long long k, long long pad_lo, long long pad_hi,
+                      long long stride) {
+  if (in < 1 || k < 1 || pad_lo < 0 || pad_hi < 0 || stride < 1) return -1;
+  const long long span = in + pad_lo + pad_hi - k;
   if (span < 0) return -1;
   return span / stride + 1;
+}
+
+long long out_extent(long long in, long long k, long long pad, long long stride) {
+  return out_extent2(in, k, pad, pad, stride);
 }
 
 bool overlaps(const void* a, long long abytes, const void* b, long long bbytes) {
@@ -64,7 +70,7 @@ libconv_status validate(Problem& p, int algo, bool with_pointers) {
   if (p.N < 0 || p.C < 1 || p.T < 1 || p.H < 1 || p.W < 1 || p.K < 1 || p.KT < 1 || p.KH < 1 ||
       p.KW < 1)
     return LIBCONV_ERR_BAD_SHAPE;
-  const long long ot = out_extent(p.T, p.KT, p.pt, p.st);
+  const long long ot = out_extent2(p.T, p.KT, p.pt, p.ptb, p.st);
   const long long oh = out_extent(p.H, p.KH, p.ph, p.sh);
   const long long ow = out_extent(p.W, p.KW, p.pw, p.sw);
   if (ot < 1 || oh < 1 || ow < 1) return LIBCONV_ERR_BAD_SHAPE;
@@ -211,7 +217,7 @@ PlanKey plan_key(const Problem& p, int algo) {
   PlanKey k;
   const int v[24] = {p.N, p.C, p.T, p.H, p.W, p.K, p.KT, p.KH, p.KW, p.pt, p.ph, p.pw, p.st, p.sh,
                      p.sw, p.dtype, p.act, algo, (int)p.no_temps, p.w == nullptr,
-                     (int)(reinterpret_cast<uintptr_t>(p.x) & 15), p.cus, p.wp != nullptr, 0};
+                     (int)(reinterpret_cast<uintptr_t>(p.x) & 15), p.cus, p.wp != nullptr, p.ptb};
   std::memcpy(k.v, v, sizeof(v));
   return k;
 }
@@ -301,6 +307,7 @@ Problem make_problem(const void* x, const void* w, const void* bias, void* y, in
   p.N = N; p.C = C_in; p.T = T; p.H = H; p.W = W;
   p.K = C_out; p.KT = KT; p.KH = KH; p.KW = KW;
   p.pt = pad_t; p.ph = pad_h; p.pw = pad_w;
+  p.ptb = pad_t;
   p.st = stride_t; p.sh = stride_h; p.sw = stride_w;
   p.dtype = dtype; p.act = act;
   p.x = x; p.w = w; p.b = bias; p.y = y;
@@ -401,6 +408,23 @@ libconv_status libconv_pack_weights(const void* w, void* packed, long long packe
                      reinterpret_cast<hipStream_t>(stream));
 }
 
+libconv_status conv3d_forward_tpad(const void* x, const void* w, const void* packed_w,
+                                   const void* bias, void* y, int N, int C_in, int T, int H, int W,
+                                   int C_out, int KT, int KH, int KW, int pad_t_front,
+                                   int pad_t_back, int pad_h, int pad_w, int stride_t,
+                                   int stride_h, int stride_w, int dtype, int act, void* stream) {
+  if ((w == nullptr) == (packed_w == nullptr)) return LIBCONV_ERR_NULL_POINTER;
+  Problem p = make_problem(x, w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW, pad_t_front,
+                           pad_h, pad_w, stride_t, stride_h, stride_w, dtype, act, stream);
+  p.ptb = pad_t_back;
+  if (packed_w) {
+    p.wp = packed_w;
+    p.no_temps = true;  // as libconv_forward_packed: never allocates
+    return run(p, LIBCONV_ALGO_IGEMM);
+  }
+  return run(p, LIBCONV_ALGO_AUTO);
+}
+
 libconv_status libconv_forward_packed(const void* x, const void* packed_w, const void* bias,
                                       void* y, int N, int C_in, int T, int H, int W, int C_out,
                                       int KT, int KH, int KW, int pad_t, int pad_h, int pad_w,
@@ -463,7 +487,11 @@ int libconv_tile_occupancy(int tile_id, int dtype, int measured) {
 }
 
 int libconv_out_size(int in, int k, int pad, int stride) {
-  const long long o = out_extent(in, k, pad, stride);
+  return libconv_out_size2(in, k, pad, pad, stride);
+}
+
+int libconv_out_size2(int in, int k, int pad_lo, int pad_hi, int stride) {
+  const long long o = out_extent2(in, k, pad_lo, pad_hi, stride);
   return (o < 1 || o > 0x7fffffff) ? -1 : (int)o;
 }
 

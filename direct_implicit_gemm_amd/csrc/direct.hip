@@ -544,7 +544,7 @@ long tap_floats_per_channel(const TapTile& t, int dtype) {
 }
 
 bool tap_fits(const TapTile& t, const Problem& p) {
-  if (p.KT != 1 || p.st != 1 || p.pt != 0) return false;
+  if (p.KT != 1 || p.st != 1 || p.pt != 0 || p.ptb != 0) return false;
   if (p.KH != t.KH || p.KW != t.KW || p.sh != t.SH || p.sw != t.SW) return false;
   if (t.vx) {
     const int run = 16 / dtype_bytes(p.dtype);

@@ -1087,7 +1087,7 @@ const TileDesc* find_tile(int id) {
 
 bool is_flat(const Problem& p) {
   return p.KT == 1 && p.KH == 1 && p.KW == 1 && p.st == 1 && p.sh == 1 && p.sw == 1 &&
-         p.pt == 0 && p.ph == 0 && p.pw == 0;
+         p.pt == 0 && p.ptb == 0 && p.ph == 0 && p.pw == 0;
 }
 
 bool tile_fits(const TileDesc& t, const Problem& p) {
@@ -1107,7 +1107,7 @@ bool tile_fits(const TileDesc& t, const Problem& p) {
   if (t.one && (p.C > t.CG * se || p.KT != 1)) return false;
   if (t.flat) return is_flat(p);
   return p.KT == t.KT && p.KH == t.KH && p.KW == t.KW && p.sh == t.SH && p.sw == t.SW &&
-         (t.KT > 1 || (p.st == 1 && p.pt == 0));
+         (t.KT > 1 || (p.st == 1 && p.pt == 0 && p.ptb == 0));
 }
 
 struct TileCounts {

@@ -10,11 +10,14 @@
 namespace libconv {
 
 // One convolution call, normalised to the 3-D form (2-D: T = KT = 1,
-// pt = 0, st = 1).  K is C_out.  Output extents are filled by validation.
+// pt = 0, st = 1).  K is C_out.  pt pads the frame axis before the first
+// frame and ptb after the last (equal unless the caller asked otherwise).
+// Output extents are filled by validation.
 struct Problem {
   int N, C, T, H, W;
   int K, KT, KH, KW;
   int pt, ph, pw;
+  int ptb;
   int st, sh, sw;
   int OT, OH, OW;
   int dtype;  // libconv_dtype

@@ -183,6 +183,27 @@ libconv_status libconv_forward_packed(const void* x, const void* packed_w, const
                                       int dtype, int act, void* stream);
 
 /*
+ * conv3d_forward with the frame axis padded by pad_t_front zero frames
+ * before the first frame and pad_t_back after the last; they may differ.
+ * The causal 3-D convolution of the spatio-temporal VAE in "SeedVR2 NCNN
+ * Vulkan", section 7.2 (built there from Concat/Crop around a plain
+ * Convolution3D) is pad_t_front = KT - 1, pad_t_back = 0: output frame t then
+ * reads input frames t-KT+1 .. t only (stride 1).  Output frames:
+ * floor((T + pad_t_front + pad_t_back - KT) / stride_t) + 1.
+ * Weights: exactly one of w (OIDHW, as conv3d_forward; the dispatcher picks
+ * the kernel) and packed_w (from libconv_pack_weights, as
+ * libconv_forward_packed: MFMA kernels only, never allocates); the other is
+ * NULL, else LIBCONV_ERR_NULL_POINTER.  Pads must be >= 0.
+ */
+libconv_status conv3d_forward_tpad(const void* x, const void* w, const void* packed_w,
+                                   const void* bias, void* y,
+                                   int N, int C_in, int T, int H, int W,
+                                   int C_out, int KT, int KH, int KW,
+                                   int pad_t_front, int pad_t_back, int pad_h, int pad_w,
+                                   int stride_t, int stride_h, int stride_w,
+                                   int dtype, int act, void* stream);
+
+/*
  * Which kernel the dispatcher would launch for this shape, without launching.
  * Arguments as for libconv_forward_algo (algo may force a family).  On
  * LIBCONV_OK: *algo_out is LIBCONV_ALGO_DIRECT or LIBCONV_ALGO_IGEMM,
@@ -228,6 +249,10 @@ int libconv_tile_occupancy(int tile_id, int dtype, int measured);
 /* floor((in + 2*pad - k) / stride) + 1, or -1 if an argument is out of range
  * (in < 1, k < 1, pad < 0, stride < 1) or the window does not fit. */
 int libconv_out_size(int in, int k, int pad, int stride);
+
+/* The same with pad_lo before and pad_hi after the input (the frame axis of
+ * conv3d_forward_tpad): floor((in + pad_lo + pad_hi - k) / stride) + 1, or -1. */
+int libconv_out_size2(int in, int k, int pad_lo, int pad_hi, int stride);
 
 /* Static description of a status code; never NULL. */
 const char* libconv_status_string(int status);

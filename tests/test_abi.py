@@ -207,3 +207,30 @@ def test_query_plan_capture_excludes_temporaries():
     assert L.libconv_query_plan(*args, 0)[4] > 1
     out = L.libconv_query_plan(1, 4, 1, 8, 8, 8, 1, 3, 3, 0, 1, 1, 1, 1, 1, 5, 0, 0, 0)
     assert out[0] == 3  # bad dtype
+
+
+def test_out_size2_matches_oracle():
+    for n_in, k, lo, hi, s in itertools.product(range(1, 10), range(1, 5), range(0, 3),
+                                               range(0, 3), range(1, 4)):
+        want = oracle.out_extent2(n_in, k, lo, hi, s)
+        assert L.libconv_out_size2(n_in, k, lo, hi, s) == (want if want >= 1 else -1)
+    assert L.libconv_out_size2(5, 3, -1, 0, 1) == -1
+
+
+def test_tpad_argument_errors_without_gpu():
+    """Weights: exactly one of w and packed_w; negative pads are a bad shape.
+    Both are rejected before any device access."""
+    args = (4, 1, 5, 8, 8, 8, 3, 3, 3)
+    fake = 1 << 40
+    st = L.conv3d_forward_tpad(fake, fake, fake, None, fake + (1 << 30), *args, 2, 0, 1, 1,
+                               1, 1, 1, 1, 0, None)
+    assert st == 1  # both weight forms
+    st = L.conv3d_forward_tpad(fake, None, None, None, fake + (1 << 30), *args, 2, 0, 1, 1,
+                               1, 1, 1, 1, 0, None)
+    assert st == 1  # neither
+    st = L.conv3d_forward_tpad(fake, fake, None, None, fake + (1 << 30), *args, -1, 0, 1, 1,
+                               1, 1, 1, 1, 0, None)
+    assert st == 2
+    st = L.conv3d_forward_tpad(fake, fake, None, None, fake + (1 << 30), *args, 0, -2, 1, 1,
+                               1, 1, 1, 1, 0, None)
+    assert st == 2

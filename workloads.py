@@ -54,6 +54,9 @@ class Layer:
     x_dist: str                    # "U01", "U11", "N01"
     w_dist: str                    # "U11" or "N01", scaled by 1/sqrt(fan_in)
     b_dist: Optional[str]          # "U0.1", "U0.05", "zero"
+    # time padding after the last frame when it differs from pad[0] (the
+    # causal 3-D convolution pads only before the first frame); None: pad[0]
+    pad_t_back: Optional[int] = None
 
     @property
     def taps(self) -> int:
@@ -119,9 +122,22 @@ WORKLOADS: Dict[str, Tuple[int, List[Layer]]] = {
 
 ALL_LAYERS: Dict[str, Layer] = {l.name: l for _, ls in WORKLOADS.values() for l in ls}
 
+# Beyond the five: the video-VAE layers made causal in time (KT-1 = 2 frames of
+# padding before the first frame, none after), the Convolution3D of the
+# spatio-temporal VAE in "SeedVR2 NCNN Vulkan", section 7.2.  Same shapes and
+# value distributions as the video-VAE workload, own seed.
+EXTRA_WORKLOADS: Dict[str, Tuple[int, List[Layer]]] = {
+    "vae3d_causal_f16": (5, [
+        _l3("c5c_A", "f16", 1, 128, 5, 256, 480, 128, 3, 1, 1, "none", "N01", "N01",
+            "U0.05").with_(pad=(2, 1, 1), pad_t_back=0),
+        _l3("c5c_B", "f16", 1, 512, 5, 64, 120, 512, 3, 1, 1, "relu", "N01", "N01",
+            "U0.05").with_(pad=(2, 1, 1), pad_t_back=0),
+    ]),
+}
+
 
 def workload_of(layer_name: str) -> str:
-    for wname, (_, ls) in WORKLOADS.items():
+    for wname, (_, ls) in list(WORKLOADS.items()) + list(EXTRA_WORKLOADS.items()):
         if any(l.name == layer_name for l in ls):
             return wname
     raise KeyError(layer_name)
@@ -209,7 +225,7 @@ def make_inputs(layer: Layer, seed: Optional[int] = None):
     """
     if seed is None:
         wname = workload_of(layer.name)
-        wseed, layers = WORKLOADS[wname]
+        wseed, layers = {**WORKLOADS, **EXTRA_WORKLOADS}[wname]
         rng = np.random.default_rng(wseed)
         for l in layers:
             if l.name == layer.name:
