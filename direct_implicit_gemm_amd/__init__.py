@@ -87,6 +87,9 @@ def load() -> ctypes.CDLL:
     lib.conv3d_forward_tpad.restype = I
     lib.libconv_out_size2.argtypes = [I] * 5
     lib.libconv_out_size2.restype = I
+    FP = ctypes.POINTER(ctypes.c_float)
+    lib.libconv_fold_batchnorm.argtypes = [FP] * 6 + [ctypes.c_float, I, I, FP, FP]
+    lib.libconv_fold_batchnorm.restype = I
     _lib = lib
     return lib
 
@@ -131,6 +134,26 @@ def conv3d_forward_tpad(x, w, packed_w, bias, y, N, C_in, T, H, W, C_out, KT, KH
 
 def libconv_out_size2(n_in, k, pad_lo, pad_hi, stride) -> int:
     return load().libconv_out_size2(n_in, k, pad_lo, pad_hi, stride)
+
+
+def fold_batchnorm(w, b, gamma, beta, mean, var, eps: float):
+    """libconv_fold_batchnorm on host numpy arrays: returns (w_folded, b_folded)
+    as float32 arrays shaped like w and [C_out].  b may be None."""
+    import numpy as np
+    f32 = lambda a: np.ascontiguousarray(a, dtype=np.float32)
+    w32 = f32(w)
+    C_out = w32.shape[0]
+    k = int(w32.size // C_out)
+    gamma, beta, mean, var = (f32(a).reshape(C_out) for a in (gamma, beta, mean, var))
+    b32 = None if b is None else f32(b).reshape(C_out)
+    wo = np.empty_like(w32)
+    bo = np.empty(C_out, np.float32)
+    fp = lambda a: None if a is None else a.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+    st = load().libconv_fold_batchnorm(fp(w32), fp(b32), fp(gamma), fp(beta), fp(mean), fp(var),
+                                       float(eps), C_out, k, fp(wo), fp(bo))
+    if st != 0:
+        raise LibconvError(st, "libconv_fold_batchnorm")
+    return wo, bo
 
 
 def libconv_packed_weight_bytes(C_in, C_out, KT, KH, KW, dtype) -> int:

@@ -9,6 +9,7 @@
 // Vulkan", section 3.6, on a Convolution3D that fell back to the CPU).
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
@@ -466,6 +467,24 @@ libconv_status libconv_query_plan(int N, int C_in, int T, int H, int W, int C_ou
   *tile_out = plan.tile;
   *grid_out = p.N == 0 ? 0 : plan.grid;
   *ksplit_out = plan.ksplit;
+  return LIBCONV_OK;
+}
+
+libconv_status libconv_fold_batchnorm(const float* w, const float* b, const float* gamma,
+                                      const float* beta, const float* mean, const float* var,
+                                      float eps, int C_out, int k_per_out, float* w_out,
+                                      float* b_out) {
+  if (!w || !gamma || !beta || !mean || !var || !w_out || !b_out) return LIBCONV_ERR_NULL_POINTER;
+  if (C_out < 1 || k_per_out < 1) return LIBCONV_ERR_BAD_SHAPE;
+  for (int co = 0; co < C_out; ++co)
+    if (!((double)var[co] + (double)eps > 0.0)) return LIBCONV_ERR_BAD_SHAPE;
+  for (int co = 0; co < C_out; ++co) {
+    const double s = (double)gamma[co] / std::sqrt((double)var[co] + (double)eps);
+    const double bias = b ? (double)b[co] : 0.0;
+    b_out[co] = (float)((bias - (double)mean[co]) * s + (double)beta[co]);
+    const long long base = (long long)co * k_per_out;
+    for (int k = 0; k < k_per_out; ++k) w_out[base + k] = (float)((double)w[base + k] * s);
+  }
   return LIBCONV_OK;
 }
 

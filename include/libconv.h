@@ -235,6 +235,26 @@ libconv_status libconv_query_plan(int N, int C_in, int T, int H, int W,
                                   int* algo_out, int* tile_out, long long* grid_out,
                                   int* ksplit_out);
 
+/*
+ * Batch normalisation folded into the convolution before it, once, on the
+ * host, at model load (the detector of "PP-OCR on Vulkan compute shaders"
+ * folds each BN layer into the preceding conv's weights and bias on the CPU,
+ * so that the GPU runs the fused conv only):
+ *   s[co]       = gamma[co] / sqrt(var[co] + eps)
+ *   w_out[co][k] = w[co][k] * s[co]                (k < k_per_out = C_in*KT*KH*KW)
+ *   b_out[co]   = (b[co] - mean[co]) * s[co] + beta[co]      (b NULL: b = 0)
+ * HOST pointers, fp32 in and out, each value computed in fp64 and rounded
+ * once.  w_out / b_out may be w / b (in place).  The caller converts the
+ * folded weights to the layer's storage dtype and copies them to the device.
+ * LIBCONV_ERR_NULL_POINTER for a NULL argument other than b;
+ * LIBCONV_ERR_BAD_SHAPE for C_out < 1, k_per_out < 1, or var[co] + eps <= 0
+ * (nothing written then).
+ */
+libconv_status libconv_fold_batchnorm(const float* w, const float* b, const float* gamma,
+                                      const float* beta, const float* mean, const float* var,
+                                      float eps, int C_out, int k_per_out,
+                                      float* w_out, float* b_out);
+
 /* Human-readable name of a tile configuration id; "?" if unknown. */
 const char* libconv_tile_name(int tile_id);
 

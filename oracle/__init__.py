@@ -206,3 +206,18 @@ def output_shape(x_shape, w_shape, stride=1, pad=0):
              out_extent(x_shape[3], w_shape[3], p3[1], s3[1]),
              out_extent(x_shape[4], w_shape[4], p3[2], s3[2]))
     return (x_shape[0], w_shape[0]) + o
+
+
+def fold_batchnorm(w: np.ndarray, b: Optional[np.ndarray], gamma: np.ndarray, beta: np.ndarray,
+                   mean: np.ndarray, var: np.ndarray, eps: float) -> Tuple[np.ndarray, np.ndarray]:
+    """Batch normalisation folded into the convolution before it, in fp64 (the
+    folding formula of the page "PP-OCR on Vulkan compute shaders": the weights
+    scaled by gamma / sqrt(var + eps) per output channel, the bias shifted by
+    the mean, scaled likewise, plus beta).  Returns (w_folded, b_folded)."""
+    w = np.asarray(w, np.float64)
+    co = w.shape[0]
+    scale = np.asarray(gamma, np.float64) / np.sqrt(np.asarray(var, np.float64) + float(eps))
+    bias = np.zeros(co) if b is None else np.asarray(b, np.float64)
+    w_f = w * scale.reshape((co,) + (1,) * (w.ndim - 1))
+    b_f = (bias - np.asarray(mean, np.float64)) * scale + np.asarray(beta, np.float64)
+    return w_f, b_f

@@ -4,6 +4,7 @@ status strings, argument validation (which returns before any launch), and
 the dispatcher's choices."""
 import itertools
 
+import numpy as np
 import pytest
 
 import direct_implicit_gemm_amd as L
@@ -234,3 +235,48 @@ def test_tpad_argument_errors_without_gpu():
     st = L.conv3d_forward_tpad(fake, fake, None, None, fake + (1 << 30), *args, 0, -2, 1, 1,
                                1, 1, 1, 1, 0, None)
     assert st == 2
+
+
+def test_fold_batchnorm_host_function():
+    """libconv's host fold against the oracle's fp64 fold: each value is the
+    fp64 result rounded once to fp32 (within one fp32 ulp), in place too."""
+    r = np.random.default_rng(92)
+    w = r.standard_normal((8, 3, 3, 3)).astype(np.float32)
+    b = r.standard_normal(8).astype(np.float32)
+    g, be = r.uniform(0.5, 2, 8).astype(np.float32), r.standard_normal(8).astype(np.float32)
+    mu, var = r.standard_normal(8).astype(np.float32), r.uniform(0.1, 2, 8).astype(np.float32)
+    wf, bf = L.fold_batchnorm(w, b, g, be, mu, var, 1e-5)
+    rw, rb = oracle.fold_batchnorm(w, b, g, be, mu, var, np.float32(1e-5))
+    np.testing.assert_allclose(wf, rw, rtol=2 ** -23, atol=0)
+    np.testing.assert_allclose(bf, rb, rtol=2 ** -23, atol=1e-7)
+    wn, bn = L.fold_batchnorm(w, None, g, be, mu, var, 1e-5)
+    np.testing.assert_array_equal(wn, wf)
+    _, rb0 = oracle.fold_batchnorm(w, None, g, be, mu, var, np.float32(1e-5))
+    np.testing.assert_allclose(bn, rb0, rtol=2 ** -23, atol=1e-7)
+    # in place: output pointers equal to the inputs
+    import ctypes
+    w2, b2 = w.copy(), b.copy()
+    fp = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+    st = L.load().libconv_fold_batchnorm(fp(w2), fp(b2), fp(g), fp(be), fp(mu), fp(var),
+                                         1e-5, 8, 27, fp(w2), fp(b2))
+    assert st == 0
+    np.testing.assert_array_equal(w2, wf)
+    np.testing.assert_array_equal(b2, bf)
+
+
+def test_fold_batchnorm_errors():
+    import ctypes
+    w = np.ones((2, 4), np.float32)
+    v = np.ones(2, np.float32)
+    fp = lambda a: None if a is None else a.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+    lib = L.load()
+    wo, bo = np.empty_like(w), np.empty(2, np.float32)
+    assert lib.libconv_fold_batchnorm(fp(w), None, None, fp(v), fp(v), fp(v), 1e-5, 2, 4,
+                                      fp(wo), fp(bo)) == 1
+    assert lib.libconv_fold_batchnorm(fp(w), None, fp(v), fp(v), fp(v), fp(v), 1e-5, 0, 4,
+                                      fp(wo), fp(bo)) == 2
+    neg = np.array([1.0, -1.0], np.float32)
+    wo[:] = 7
+    assert lib.libconv_fold_batchnorm(fp(w), None, fp(v), fp(v), fp(v), fp(neg), 1e-5, 2, 4,
+                                      fp(wo), fp(bo)) == 2
+    assert np.all(wo == 7)  # nothing written

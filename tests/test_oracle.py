@@ -454,3 +454,41 @@ def test_time_pads_points_match_full():
     yp, sp = oracle.conv_points(x, w, None, idx, (2, 1, 1), (2, 1, 1), pad_t_back=0)
     np.testing.assert_array_equal(yp, y.reshape(-1)[idx])
     np.testing.assert_array_equal(sp, s.reshape(-1)[idx])
+
+
+# ----------------------------------------- batch normalisation folded into the conv
+def test_fold_batchnorm_matches_torch_batch_norm_after_conv():
+    """conv(x, w_f) + b_f = BN(conv(x, w) + b) with BN in inference form,
+    evaluated by torch's fp64 batch_norm (not the folding formula)."""
+    r = _rng(90)
+    x = r.standard_normal((2, 5, 9, 11))
+    w = r.standard_normal((6, 5, 3, 3))
+    b = r.standard_normal(6)
+    gamma, beta = r.uniform(0.5, 2.0, 6), r.standard_normal(6)
+    mean, var, eps = r.standard_normal(6), r.uniform(0.1, 3.0, 6), 1e-5
+    wf, bf = oracle.fold_batchnorm(w, b, gamma, beta, mean, var, eps)
+    y_fold, _ = oracle.conv(x, wf, bf, 1, 1)
+    conv = torch.nn.functional.conv2d(torch.from_numpy(x), torch.from_numpy(w),
+                                      torch.from_numpy(b), padding=1)
+    ref = torch.nn.functional.batch_norm(conv, torch.from_numpy(mean), torch.from_numpy(var),
+                                         torch.from_numpy(gamma), torch.from_numpy(beta),
+                                         training=False, eps=eps).numpy()
+    np.testing.assert_allclose(y_fold, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_fold_batchnorm_identity_and_no_bias():
+    """gamma = sqrt(var + eps), beta = mean: the fold leaves w and b unchanged;
+    a missing conv bias is a zero bias."""
+    r = _rng(91)
+    w = r.standard_normal((4, 3, 1, 3, 3))
+    b = r.standard_normal(4)
+    var, eps = r.uniform(0.5, 2.0, 4), 1e-3
+    mean = r.standard_normal(4)
+    wf, bf = oracle.fold_batchnorm(w, b, np.sqrt(var + eps), mean, mean, var, eps)
+    np.testing.assert_allclose(wf, w, rtol=1e-15)
+    np.testing.assert_allclose(bf, b, rtol=1e-14, atol=1e-14)
+    g, be = r.uniform(0.5, 2, 4), r.standard_normal(4)
+    w0, b0 = oracle.fold_batchnorm(w, None, g, be, mean, var, eps)
+    w1, b1 = oracle.fold_batchnorm(w, np.zeros(4), g, be, mean, var, eps)
+    np.testing.assert_array_equal(w0, w1)
+    np.testing.assert_array_equal(b0, b1)
