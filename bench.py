@@ -56,6 +56,8 @@ WORKLOAD_TEXT = {
     "unet_bf16": "diffusion-UNet bf16 N=2: conv3x3 640->640 on 64x64; conv3x3 1280->1280 on 32x32",
     "vae3d_f16": ("video-VAE f16 conv3d N=1 T=5: 3x3x3 128->128 on 256x480; "
                   "3x3x3 512->512 on 64x120 +ReLU"),
+    "ocr_pool_f32": ("OCR-detector conv3x3 s1 p1 32->32 +ReLU +2x2 max pool (fused) on 1x32x320x320 "
+                     "-> 1x32x160x160, fp32"),
     "vae3d_causal_f16": ("video-VAE f16 causal conv3d N=1 T=5 (2 frames of time padding "
                          "before the first frame, none after): 3x3x3 128->128 on 256x480; "
                          "3x3x3 512->512 on 64x120 +ReLU"),
@@ -79,9 +81,10 @@ def layer_work(layer: W.Layer, lib):
     ot, oh, ow = out_shape(layer, lib)
     out_spatial = ot * oh * ow
     flops = 2 * layer.N * layer.C_out * out_spatial * layer.C_in * layer.taps
+    stored = ot * (oh // 2) * (ow // 2) if layer.pool else out_spatial  # fused pooling
     e = W.DTYPE_BYTES[layer.dtype]
     nbytes = e * (int(np.prod(layer.x_shape)) + int(np.prod(layer.w_shape)) + layer.C_out
-                  + layer.N * layer.C_out * out_spatial)
+                  + layer.N * layer.C_out * stored)
     return flops, nbytes
 
 
@@ -196,6 +199,8 @@ def main():
     outs = []
     for i, l in enumerate(layers):
         ot, oh, ow = out_shape(l, lib)
+        if l.pool:
+            oh, ow = oh // 2, ow // 2
         shape = (l.N, l.C_out, oh, ow) if l.dims == 2 else (l.N, l.C_out, ot, oh, ow)
         outs.append(torch.empty(shape, dtype=xs[i].dtype, device=dev))
 
@@ -203,7 +208,9 @@ def main():
         return (l.stride[1:], l.pad[1:]) if l.dims == 2 else (l.stride, l.pad)
 
     def conv(l, x_in, w, b, out):
-        if l.pad_t_back is not None:  # time padding differs before / after the frames
+        if l.pool:  # conv + activation + 2x2 max pool in one call
+            L.conv2d_pool(x_in, w, b, l.stride[1:], l.pad[1:], l.act, out=out)
+        elif l.pad_t_back is not None:  # time padding differs before / after the frames
             L.conv3d_tpad(x_in, w, b, time_pads(l), l.stride, l.pad[1:], l.act, out=out)
         else:
             s, p = sp(l)
@@ -276,7 +283,8 @@ def main():
         pad = (sum(time_pads(l)) // 2,) + tuple(l.pad[1:])
         st_, algo, tile, grid, ks = L.libconv_query_plan(
             l.N, l.C_in, l.T, l.H, l.W, l.C_out, l.KT, l.KH, l.KW, *pad, *l.stride,
-            W.DTYPE_CODE[l.dtype], W.ACT_CODE[l.act], L.ALGO_AUTO, int(capturing))
+            W.DTYPE_CODE[l.dtype], W.ACT_CODE[l.act], L.ALGO_AUTO,
+            (L.PLAN_CAPTURING if capturing else 0) | (L.PLAN_POOL2 if l.pool else 0))
         return algo, tile, grid, ks
 
     b2b, b2b_graph = [], []
@@ -358,11 +366,18 @@ def main():
             import oracle
             threads = oracle.threads(len(os.sched_getaffinity(0)))
             t0 = time.perf_counter()
-            for l, (x, w, b) in zip(layers, inputs):
-                s, p = sp(l)
-                oracle.conv(x.f64(), w.f64(), b.f64(), s, p, relu=l.act == "relu",
-                            pad_t_back=l.pad_t_back)
-            sec, runs = time.perf_counter() - t0, 1
+            runs = 0
+            while True:  # whole steps, repeated to about the CPU budget
+                for l, (x, w, b) in zip(layers, inputs):
+                    s, p = sp(l)
+                    y, _ = oracle.conv(x.f64(), w.f64(), b.f64(), s, p, relu=l.act == "relu",
+                                       pad_t_back=l.pad_t_back)
+                    if l.pool:
+                        oracle.max_pool2x2(y)
+                runs += 1
+                if time.perf_counter() - t0 >= args.cpu_budget:
+                    break
+            sec = (time.perf_counter() - t0) / runs
         cpu = {"value": round(step_flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
                "kind": "oracle",
                "sample": f"the whole step ({len(layers)} layers, fp64, incl. the |x*w| sum), "

@@ -83,6 +83,8 @@ def load() -> ctypes.CDLL:
     lib.libconv_pack_weights.restype = I
     lib.libconv_forward_packed.argtypes = [P, P, P, P] + [I] * 17 + [P]
     lib.libconv_forward_packed.restype = I
+    lib.conv2d_forward_pool.argtypes = [P, P, P, P] + [I] * 13 + [P]
+    lib.conv2d_forward_pool.restype = I
     lib.conv3d_forward_tpad.argtypes = [P, P, P, P, P] + [I] * 18 + [P]
     lib.conv3d_forward_tpad.restype = I
     lib.libconv_out_size2.argtypes = [I] * 5
@@ -122,6 +124,15 @@ def libconv_forward_algo(x, w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW, pad
     return load().libconv_forward_algo(x, w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW,
                                        pad_t, pad_h, pad_w, stride_t, stride_h, stride_w,
                                        dtype, act, algo, stream)
+
+
+PLAN_CAPTURING, PLAN_POOL2 = 1, 2
+
+
+def conv2d_forward_pool(x, w, bias, y, N, C_in, H, W, C_out, KH, KW, pad_h, pad_w, stride_h,
+                        stride_w, dtype, act, stream) -> int:
+    return load().conv2d_forward_pool(x, w, bias, y, N, C_in, H, W, C_out, KH, KW, pad_h, pad_w,
+                                      stride_h, stride_w, dtype, act, stream)
 
 
 def conv3d_forward_tpad(x, w, packed_w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW,
@@ -356,6 +367,37 @@ def conv_nd_packed(x, pw: PackedWeights, b=None, stride=1, padding=0, act="none"
                                      _dtype_code(x), _ACTS[act], stream)
     if st_ != 0:
         raise LibconvError(st_, "libconv_forward_packed")
+    return y
+
+
+def conv2d_pool(x, w, b=None, stride=1, padding=0, act="none", out=None, stream=None):
+    """2-D convolution, activation and 2x2 stride-2 max pooling in one call
+    (conv2d_forward_pool); returns y [N][C_out][OH/2][OW/2]."""
+    import torch
+    if x.dim() != 4 or w.dim() != 4 or w.shape[1] != x.shape[1]:
+        raise ValueError("x must be NCHW and w OIHW with x's channel count")
+    for t in (x, w) + ((b,) if b is not None else ()):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != x.dtype:
+            raise ValueError("x, w, b must be contiguous device tensors of one dtype")
+    sh, sw = _triple(stride, 2)
+    ph, pw_ = _triple(padding, 2)
+    N, C, H, W = x.shape
+    K, _, KH, KW = w.shape
+    lib = load()
+    oh = lib.libconv_out_size(H, KH, ph, sh)
+    ow = lib.libconv_out_size(W, KW, pw_, sw)
+    if min(oh, ow) < 2:
+        raise LibconvError(2, "conv2d_pool")
+    shape = (N, K, oh // 2, ow // 2)
+    y = torch.empty(shape, dtype=x.dtype, device=x.device) if out is None else out
+    if tuple(y.shape) != shape or not y.is_contiguous() or y.dtype != x.dtype:
+        raise ValueError("bad output tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    st_ = lib.conv2d_forward_pool(_ptr(x), _ptr(w), _ptr(b), _ptr(y), N, C, H, W, K, KH, KW, ph,
+                                  pw_, sh, sw, _dtype_code(x), _ACTS[act], stream)
+    if st_ != 0:
+        raise LibconvError(st_, "conv2d_forward_pool")
     return y
 
 

@@ -79,10 +79,12 @@ libconv_status validate(Problem& p, int algo, bool with_pointers) {
   p.OT = (int)ot;
   p.OH = (int)oh;
   p.OW = (int)ow;
+  if (p.pool && (p.T != 1 || p.KT != 1 || oh < 2 || ow < 2)) return LIBCONV_ERR_BAD_SHAPE;
   const long long eb = dtype_bytes(p.dtype);
   const long long xb = product({p.N, p.C, p.T, p.H, p.W, eb});
   const long long wb = product({p.K, p.C, p.KT, p.KH, p.KW, eb});
-  const long long yb = product({p.N, p.K, ot, oh, ow, eb});
+  const long long yb = p.pool ? product({p.N, p.K, oh / 2, ow / 2, eb})
+                              : product({p.N, p.K, ot, oh, ow, eb});
   if (xb > kMaxBytes || wb > kMaxBytes || yb > kMaxBytes) return LIBCONV_ERR_TOO_LARGE;
   const long long pb = packed_weight_bytes(p.C, p.K, p.KT, p.KH, p.KW, p.dtype);
   if (pb > kMaxBytes) return LIBCONV_ERR_TOO_LARGE;
@@ -208,17 +210,18 @@ libconv_status plan_for(const Problem& p, int algo, Plan* plan, bool packed_only
 // shape reuses its plan instead of re-running the cost model.  The key holds
 // everything the dispatcher reads (shape, dtype, activation, forced family,
 // capture state, which weight forms exist, 16-byte alignment of x, compute
-// units).  Not used while a LIBCONV_FORCE_* override is set.
+// units, fused pooling).  Not used while a LIBCONV_FORCE_* override is set.
 struct PlanKey {
-  int v[24];
+  int v[25];
   bool operator==(const PlanKey& o) const { return std::memcmp(v, o.v, sizeof(v)) == 0; }
 };
 
 PlanKey plan_key(const Problem& p, int algo) {
   PlanKey k;
-  const int v[24] = {p.N, p.C, p.T, p.H, p.W, p.K, p.KT, p.KH, p.KW, p.pt, p.ph, p.pw, p.st, p.sh,
+  const int v[25] = {p.N, p.C, p.T, p.H, p.W, p.K, p.KT, p.KH, p.KW, p.pt, p.ph, p.pw, p.st, p.sh,
                      p.sw, p.dtype, p.act, algo, (int)p.no_temps, p.w == nullptr,
-                     (int)(reinterpret_cast<uintptr_t>(p.x) & 15), p.cus, p.wp != nullptr, p.ptb};
+                     (int)(reinterpret_cast<uintptr_t>(p.x) & 15), p.cus, p.wp != nullptr, p.ptb,
+                     (int)p.pool};
   std::memcpy(k.v, v, sizeof(v));
   return k;
 }
@@ -409,6 +412,16 @@ libconv_status libconv_pack_weights(const void* w, void* packed, long long packe
                      reinterpret_cast<hipStream_t>(stream));
 }
 
+libconv_status conv2d_forward_pool(const void* x, const void* w, const void* bias, void* y, int N,
+                                   int C_in, int H, int W, int C_out, int KH, int KW, int pad_h,
+                                   int pad_w, int stride_h, int stride_w, int dtype, int act,
+                                   void* stream) {
+  Problem p = make_problem(x, w, bias, y, N, C_in, 1, H, W, C_out, 1, KH, KW, 0, pad_h, pad_w, 1,
+                           stride_h, stride_w, dtype, act, stream);
+  p.pool = true;
+  return run(p, LIBCONV_ALGO_AUTO);
+}
+
 libconv_status conv3d_forward_tpad(const void* x, const void* w, const void* packed_w,
                                    const void* bias, void* y, int N, int C_in, int T, int H, int W,
                                    int C_out, int KT, int KH, int KW, int pad_t_front,
@@ -459,7 +472,8 @@ libconv_status libconv_query_plan(int N, int C_in, int T, int H, int W, int C_ou
                            pad_t, pad_h, pad_w, stride_t, stride_h, stride_w, dtype, act, nullptr);
   libconv_status st = validate(p, algo, false);
   if (st != LIBCONV_OK) return st;
-  p.no_temps = capturing != 0;
+  p.no_temps = (capturing & LIBCONV_PLAN_CAPTURING) != 0;
+  p.pool = (capturing & LIBCONV_PLAN_POOL2) != 0;
   Plan plan;
   st = plan_for(p, algo, &plan);
   if (st != LIBCONV_OK) return st;

@@ -603,6 +603,7 @@ const char* direct_tile_name(int id) {
 }
 
 bool direct_plan_tile(const Problem& p, int tile_id, Plan* plan) {
+  if (p.pool) return false;
   const TapTile* t = find_tap(tile_id);
   if (!t || !tap_fits(*t, p)) return false;
   plan->algo = LIBCONV_ALGO_DIRECT;
@@ -612,6 +613,7 @@ bool direct_plan_tile(const Problem& p, int tile_id, Plan* plan) {
 }
 
 bool direct_plan(const Problem& p, Plan* plan) {
+  if (p.pool) return false;  // the fused max pooling lives in the MFMA epilogue only
   if (const TapTile* t = tap_choose(p)) {
     plan->algo = LIBCONV_ALGO_DIRECT;
     plan->tile = t->id;

@@ -118,6 +118,9 @@ struct IgemmArgs {
   int ksplit, cps;
   float* part;
   int vec_out;        // 1: output rows are whole 16-byte vectors and y is 16-byte aligned
+  // 1: y is the 2x2 stride-2 max pool of act(conv + bias), [N][K][OH/2][OW/2]
+  // (floor), computed in the epilogue; vec_out then refers to the pooled rows
+  int pool;
   uint32_t x_bytes, w_bytes, b_bytes, y_bytes, part_bytes;
 };
 
@@ -175,8 +178,14 @@ struct Cfg {
   static constexpr int NBUF = ONE ? 1 : 2;
   // the vectorised epilogue reuses LDS as four wave-private 32x32 tiles
   static constexpr int EPI_LDS = 4 * 32 * (32 + 16 / EB) * EB;
+  // 2x2 max pooling in the epilogue: a wave's consecutive blocks are
+  // consecutive output rows (one 32-pixel block per tile row) in even-odd
+  // pairs; two fp32 32x36 LDS tiles per wave
+  static constexpr bool POOLABLE = BPR == 1 && FB % 2 == 0 && TH % 2 == 0 && KT == 1;
+  static constexpr int EPI_POOL_LDS = POOLABLE ? 4 * 2 * 32 * 36 * 4 : 0;
   static constexpr int STAGES_LDS = NBUF * (WBYTES + XBYTES) + DMA_PAD;
-  static constexpr int LDS = STAGES_LDS > EPI_LDS ? STAGES_LDS : EPI_LDS;
+  static constexpr int LDS0 = STAGES_LDS > EPI_LDS ? STAGES_LDS : EPI_LDS;
+  static constexpr int LDS = LDS0 > EPI_POOL_LDS ? LDS0 : EPI_POOL_LDS;
   // input staging: one unit = one run (VX) or one halo pixel of one channel
   // group; VX units come in blocks of 8 rows x NRUN runs
   static constexpr int XUNITS = VX ? (NROWS + 7) / 8 * 8 * NRUN : CG * HR * HC;
@@ -766,6 +775,76 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
   }
   const __amdgpu_buffer_rsrc_t yr = make_rsrc(a.y, a.y_bytes);
   const __amdgpu_buffer_rsrc_t br = make_rsrc(a.b, a.b_bytes);
+  if constexpr (G::POOLABLE) {
+    if (a.pool) {
+      // Fused 2x2 stride-2 max pooling: blocks j and j+1 of the wave are output
+      // rows oh (even) and oh+1; both go, after bias and activation, into two
+      // wave-private fp32 LDS tiles, and lane (row = channel, half h) takes the
+      // max over each 2x2 window of 8 pooled columns.  max commutes with the
+      // monotonic rounding to the storage dtype, so pooling the fp32 values
+      // and rounding once equals rounding every conv output, then pooling.
+      lds_barrier();  // the stage buffers are free (as for the vectorised epilogue)
+      constexpr int PE = 36;                         // LDS row pitch in floats
+      float* ta = reinterpret_cast<float*>(lds) + wave * 2 * 32 * PE;
+      float* tb = ta + 32 * PE;
+      const int ohp_n = a.OH / 2, owp_n = a.OW / 2;  // pooled extents
+      const int prow = lane & 31, ph = lane >> 5;
+      constexpr int VP = 16 / EB;                    // pooled outputs per 16-byte store
+#pragma unroll
+      for (int i = 0; i < G::FA; ++i) {
+        float bias[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int co = co0 + co_w0 + i * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+          bias[r] = E::load(br, guard_offset(a.b && co < a.K, co * EB));
+        }
+#pragma unroll
+        for (int jp = 0; jp < G::FB / 2; ++jp) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = 8 * (r >> 2) + 4 * hf + (r & 3);
+            ta[row * PE + il] = epilogue(acc[i][2 * jp][r], bias[r], a.relu);
+            tb[row * PE + il] = epilogue(acc[i][2 * jp + 1][r], bias[r], a.relu);
+          }
+          lds_fence();
+          float m[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const int c = 16 * ph + 2 * q;
+            m[q] = fmaxf(fmaxf(ta[prow * PE + c], ta[prow * PE + c + 1]),
+                         fmaxf(tb[prow * PE + c], tb[prow * PE + c + 1]));
+          }
+          lds_fence();
+          const int co = co0 + co_w0 + i * 32 + prow;
+          const int ohp = (oh0 + blk0 + 2 * jp) / 2;
+          const int owp = ow0 / 2 + 8 * ph;
+          const bool ok = co < a.K && ohp < ohp_n;
+          const int off = ((n * a.K + co) * ohp_n + ohp) * owp_n + owp;
+          if (a.vec_out) {  // pooled rows of whole 16-byte vectors: owp .. owp+7 in or out together
+#pragma unroll
+            for (int v = 0; v < 8 / VP; ++v) {
+              u32x4_t word;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                if constexpr (EB == 4)
+                  word[e] = __builtin_bit_cast(uint32_t, m[v * VP + e]);
+                else
+                  word[e] = (uint32_t)E::from_f32(m[v * VP + 2 * e]) |
+                            ((uint32_t)E::from_f32(m[v * VP + 2 * e + 1]) << 16);
+              }
+              __builtin_amdgcn_raw_buffer_store_b128(
+                  word, yr, guard_offset(ok && owp + v * VP < owp_n, (off + v * VP) * EB), 0, 0);
+            }
+          } else {
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+              if (ok && owp + q < owp_n) E::store(m[q], yr, (off + q) * EB);
+          }
+        }
+      }
+      return;
+    }
+  }
   if (a.vec_out) {
     // Rows of whole 16-byte vectors: each 32x32 block goes through a
     // wave-private LDS tile and leaves as 16-byte row segments, VEC outputs
@@ -990,6 +1069,7 @@ struct TileDesc {
   int occ;        // workgroups one CU holds at once (registers and LDS of the
                   // built kernel; checked against the runtime by a GPU test)
   int one;        // 1: single-stage tile (the layer's input channels fit one stage)
+  int pool;       // 1: can fuse the 2x2 max pooling into its epilogue
   int lds;
   const char* name;
   LaunchFn fn[3];  // by libconv_dtype
@@ -1018,6 +1098,8 @@ constexpr OccFn occupier() {
 #define LIBCONV_TILE(ID, WIDE, KT, KH, KW, SH, SW, FLAT, BM, TH, TW, WM, WN, CG, PK, VX, EFF,   \
                      OCC, NAME)                                                                 \
   {ID, WIDE, KT, KH, KW, SH, SW, FLAT, BM, TH, TW, CG, (PK) & 1, VX, EFF, OCC, (PK) >> 1,        \
+   !(FLAT) && Cfg<WIDE ? DT_F16 : DT_F32, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK,       \
+                  VX>::POOLABLE,                                                                \
    Cfg<WIDE ? DT_F16 : DT_F32, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK, VX>::LDS, NAME, \
    {launcher<DT_F32, WIDE, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK, VX>(),               \
     launcher<DT_F16, WIDE, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK, VX>(),               \
@@ -1105,6 +1187,7 @@ bool tile_fits(const TileDesc& t, const Problem& p) {
       return false;
   }
   if (t.one && (p.C > t.CG * se || p.KT != 1)) return false;
+  if (p.pool && !t.pool) return false;
   if (t.flat) return is_flat(p);
   return p.KT == t.KT && p.KH == t.KH && p.KW == t.KW && p.sh == t.SH && p.sw == t.SW &&
          (t.KT > 1 || (p.st == 1 && p.pt == 0 && p.ptb == 0));
@@ -1274,7 +1357,7 @@ static bool plan_among(const Problem& p, int want_packed, Plan* plan) {
     if (!tile_fits(t, p) || !t.fn[p.dtype]) continue;
     if (p.no_temps && t.packed && !p.wp) continue;  // would pack into a temporary
     const TileCounts c = counts(t, p);
-    for (int ks = 1; ks <= (p.no_temps ? 1 : 4); ++ks) {
+    for (int ks = 1; ks <= (p.no_temps || p.pool ? 1 : 4); ++ks) {
       if ((fk > 0 && !p.no_temps && ks != fk) || !split_ok(t, p, ks)) continue;
       const double cost = estimate_us(t, p, c, ks);
       if (!best || cost < best_cost) {
@@ -1301,7 +1384,7 @@ bool igemm_plan_tile(const Problem& p, int tile_id, Plan* plan) {
   const TileDesc* t = find_tile(tile_id);
   if (!t || !tile_fits(*t, p) || !t->fn[p.dtype]) return false;
   if (p.no_temps && t->packed && !p.wp) return false;
-  const int fk = p.no_temps ? 1 : forced_ksplit();
+  const int fk = p.no_temps || p.pool ? 1 : forced_ksplit();
   plan->algo = LIBCONV_ALGO_IGEMM;
   plan->tile = t->id;
   plan->ksplit = fk > 1 && split_ok(*t, p, fk) ? fk : 1;
@@ -1323,7 +1406,8 @@ libconv_status igemm_launch(const Problem& p, const Plan& plan) {
   if (!fn) return LIBCONV_ERR_UNSUPPORTED;
   if (t->packed && !p.wp) return LIBCONV_ERR_UNSUPPORTED;
   const int ks = plan.ksplit > 1 ? plan.ksplit : 1;
-  if (!split_ok(*t, p, ks) || (ks > 1 && p.no_temps)) return LIBCONV_ERR_UNSUPPORTED;
+  if (!split_ok(*t, p, ks) || (ks > 1 && (p.no_temps || p.pool))) return LIBCONV_ERR_UNSUPPORTED;
+  if (p.pool && !t->pool) return LIBCONV_ERR_UNSUPPORTED;
   const TileCounts c = counts(*t, p);
   if (c.total * ks > 0x7fffffffLL) return LIBCONV_ERR_UNSUPPORTED;
   IgemmArgs a;
@@ -1355,6 +1439,11 @@ libconv_status igemm_launch(const Problem& p, const Plan& plan) {
   a.part = nullptr;
   a.part_bytes = 0;
   a.vec_out = (a.OW % (16 / eb)) == 0 && (reinterpret_cast<uintptr_t>(p.y) & 15) == 0;
+  a.pool = p.pool ? 1 : 0;
+  if (p.pool) {  // y holds the pooled output
+    a.y_bytes = (uint32_t)((long long)p.N * p.K * (p.OH / 2) * (p.OW / 2) * eb);
+    a.vec_out = ((p.OW / 2) % (16 / eb)) == 0 && (reinterpret_cast<uintptr_t>(p.y) & 15) == 0;
+  }
   if (ks == 1) {
     const hipError_t e = fn(a, (unsigned)c.total, p.stream);
     return e == hipSuccess ? LIBCONV_OK : LIBCONV_ERR_LAUNCH;

@@ -30,6 +30,7 @@ struct Problem {
   hipStream_t stream;
   int cus;         // compute units of the current device (filled before a launch)
   bool no_temps;   // plan without stream-ordered temporaries (the stream is capturing)
+  bool pool;       // y is the 2x2 stride-2 max pool of the activated conv output (2-D only)
 };
 
 // What the dispatcher decided.

@@ -183,6 +183,24 @@ libconv_status libconv_forward_packed(const void* x, const void* packed_w, const
                                       int dtype, int act, void* stream);
 
 /*
+ * conv2d_forward followed by 2x2 max pooling with stride 2, fused into the
+ * convolution's epilogue (the conv + activation + pool fusion of the
+ * detector in "PP-OCR on Vulkan compute shaders", section 4.4, which halves
+ * the dispatches):  y[n][co][i][j] = max over a, b in {0, 1} of
+ * act(conv(x, w) + bias)[n][co][2i+a][2j+b], y [N][C_out][OH/2][OW/2]
+ * (floor: an odd last row or column of the conv output is dropped).  The
+ * max is taken before the one rounding to the storage dtype, which gives
+ * the same value as rounding every conv output and pooling them.  Runs on
+ * the MFMA kernels only: LIBCONV_ERR_UNSUPPORTED for shapes they do not take
+ * (e.g. C_in * KH * KW below one MFMA k-step's channels, 1x1 layers);
+ * LIBCONV_ERR_BAD_SHAPE when OH or OW is below 2.
+ */
+libconv_status conv2d_forward_pool(const void* x, const void* w, const void* bias, void* y,
+                                   int N, int C_in, int H, int W, int C_out, int KH, int KW,
+                                   int pad_h, int pad_w, int stride_h, int stride_w,
+                                   int dtype, int act, void* stream);
+
+/*
  * conv3d_forward with the frame axis padded by pad_t_front zero frames
  * before the first frame and pad_t_back after the last; they may differ.
  * The causal 3-D convolution of the spatio-temporal VAE in "SeedVR2 NCNN
@@ -218,13 +236,20 @@ libconv_status libconv_query_algo(int N, int C_in, int T, int H, int W,
                                   int dtype, int act, int algo,
                                   int* algo_out, int* tile_out, long long* grid_out);
 
+/* Flags of libconv_query_plan. */
+enum {
+  LIBCONV_PLAN_CAPTURING = 1,  /* the call is made while its stream is captured into a graph */
+  LIBCONV_PLAN_POOL2 = 2       /* the call is conv2d_forward_pool */
+};
+
 /*
  * libconv_query_algo with two more facts about the plan: *ksplit_out, the
  * number of workgroups that share one output tile's reduction (split-K; 1 =
- * none), and the plan for a call made while its stream is being captured
- * into a HIP graph when `capturing` is non-zero (such a call takes no
- * stream-ordered temporaries: no split-K and no per-call weight packing, so
- * it can run another kernel than the same call made eagerly).  Pure host
+ * none), and, with LIBCONV_PLAN_CAPTURING in `capturing`, the plan for a call
+ * made while its stream is being captured into a HIP graph (such a call takes
+ * no stream-ordered temporaries: no split-K and no per-call weight packing,
+ * so it can run another kernel than the same call made eagerly); with
+ * LIBCONV_PLAN_POOL2, the plan of conv2d_forward_pool.  Pure host
  * arithmetic: works without a GPU.  Output pointers may not be NULL.
  */
 libconv_status libconv_query_plan(int N, int C_in, int T, int H, int W,

@@ -221,3 +221,14 @@ def fold_batchnorm(w: np.ndarray, b: Optional[np.ndarray], gamma: np.ndarray, be
     w_f = w * scale.reshape((co,) + (1,) * (w.ndim - 1))
     b_f = (bias - np.asarray(mean, np.float64)) * scale + np.asarray(beta, np.float64)
     return w_f, b_f
+
+
+def max_pool2x2(y: np.ndarray) -> np.ndarray:
+    """2x2 max pooling with stride 2 over the last two axes, dropping an odd
+    last row or column (the pooling the PP-OCR detector fuses after its conv
+    and activation, page "PP-OCR on Vulkan compute shaders", section 4.4)."""
+    y = np.asarray(y)
+    oh, ow = y.shape[-2] // 2, y.shape[-1] // 2
+    t = y[..., :2 * oh, :2 * ow]
+    return np.maximum(np.maximum(t[..., 0::2, 0::2], t[..., 0::2, 1::2]),
+                      np.maximum(t[..., 1::2, 0::2], t[..., 1::2, 1::2]))

@@ -492,3 +492,13 @@ def test_fold_batchnorm_identity_and_no_bias():
     w1, b1 = oracle.fold_batchnorm(w, np.zeros(4), g, be, mean, var, eps)
     np.testing.assert_array_equal(w0, w1)
     np.testing.assert_array_equal(b0, b1)
+
+
+def test_max_pool2x2_matches_torch():
+    """The pooling after conv + activation against torch's max_pool2d (2x2,
+    stride 2, floor), on even and odd extents."""
+    r = _rng(95)
+    for shape in [(2, 3, 8, 10), (1, 4, 7, 9), (1, 1, 2, 3)]:
+        y = r.standard_normal(shape)
+        ref = torch.nn.functional.max_pool2d(torch.from_numpy(y), 2, 2).numpy()
+        np.testing.assert_array_equal(oracle.max_pool2x2(y), ref)

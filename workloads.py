@@ -57,6 +57,8 @@ class Layer:
     # time padding after the last frame when it differs from pad[0] (the
     # causal 3-D convolution pads only before the first frame); None: pad[0]
     pad_t_back: Optional[int] = None
+    # 2x2 stride-2 max pooling after the activation, fused into the conv
+    pool: bool = False
 
     @property
     def taps(self) -> int:
@@ -122,11 +124,19 @@ WORKLOADS: Dict[str, Tuple[int, List[Layer]]] = {
 
 ALL_LAYERS: Dict[str, Layer] = {l.name: l for _, ls in WORKLOADS.values() for l in ls}
 
-# Beyond the five: the video-VAE layers made causal in time (KT-1 = 2 frames of
-# padding before the first frame, none after), the Convolution3D of the
-# spatio-temporal VAE in "SeedVR2 NCNN Vulkan", section 7.2.  Same shapes and
-# value distributions as the video-VAE workload, own seed.
+# Beyond the five: the OCR conv + pool block, and the video-VAE layers made
+# causal in time (KT-1 = 2 frames of padding before the first frame, none
+# after), the Convolution3D of the spatio-temporal VAE in "SeedVR2 NCNN
+# Vulkan", section 7.2.  Shapes and value distributions of the workloads they
+# extend, own seeds.
 EXTRA_WORKLOADS: Dict[str, Tuple[int, List[Layer]]] = {
+    # the OCR detector's conv + ReLU + 2x2 max-pool block, fused into one call
+    # ("PP-OCR on Vulkan compute shaders", section 4.4): the OCR stack's
+    # second layer followed by the pooling, 320x320 -> 160x160
+    "ocr_pool_f32": (6, [
+        _l2("c2p_L2", "f32", 1, 32, 320, 320, 32, 3, 1, 1, "relu", "U01", "U11",
+            "U0.1").with_(pool=True),
+    ]),
     "vae3d_causal_f16": (5, [
         _l3("c5c_A", "f16", 1, 128, 5, 256, 480, 128, 3, 1, 1, "none", "N01", "N01",
             "U0.05").with_(pad=(2, 1, 1), pad_t_back=0),
