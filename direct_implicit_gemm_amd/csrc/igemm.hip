@@ -22,11 +22,12 @@
 //       - from OIHW weights (2-D tiles): each thread reads one channel's
 //         KH*KW contiguous 16-byte vectors and transposes them in registers
 //         (16-byte LDS stores, lanes on consecutive channels);
-//       - from packed weights ([C/SE][taps][C_out padded][SE], made by the
-//         pack kernel below -- the per-layer weight packing of the
+//       - from packed weights ([C_out padded / 64][C/SE][taps][64][SE], made
+//         by the pack kernel below -- the per-layer weight packing of the
 //         Convolution3D work in "SeedVR2 NCNN Vulkan", section 3.2): a stage
-//         is NSLOT contiguous runs copied straight into LDS by direct-to-LDS
-//         loads (no registers, no arithmetic);
+//         is NSLOT 1 KB runs copied straight into LDS by direct-to-LDS loads
+//         (no registers, no arithmetic), and all the weights one 64-channel
+//         block of a tile reads are one contiguous range of memory;
 //   * the input halo (HR rows x HC cols of one frame) is read
 //     row-contiguously -- as aligned 16-byte runs of one channel where the
 //     row length allows, else element by element -- and written
@@ -109,7 +110,7 @@ struct IgemmArgs {
   int st;             // time stride (the spatial strides are template parameters)
   int relu;
   int chunks;         // ceil(C / CK)
-  int kp;             // packed weights: output-channel stride (C_out rounded up)
+  int wblk;           // packed weights: entries per 64-output-channel block
   int co_tiles, row_tiles, col_tiles;
   int co_group;       // output-channel tiles per group of the launch order
   // split-K: `ksplit` workgroups share a tile, each summing a contiguous range
@@ -121,6 +122,8 @@ struct IgemmArgs {
   // 1: y is the 2x2 stride-2 max pool of act(conv + bias), [N][K][OH/2][OW/2]
   // (floor), computed in the epilogue; vec_out then refers to the pooled rows
   int pool;
+  // 1: the output frame is the fastest-varying part of the pixel tile index
+  int frame_fast;
   uint32_t x_bytes, w_bytes, b_bytes, y_bytes, part_bytes;
 };
 
@@ -346,12 +349,27 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
     cot = full_groups * a.co_group + rem % last;
     bid = rem / last;
   }
-  const int ctile = bid % a.col_tiles;
-  bid /= a.col_tiles;
-  const int rtile = bid % a.row_tiles;
-  bid /= a.row_tiles;
-  const int ot = bid % a.OT;
-  const int n = bid / a.OT;
+  // A frame kernel (KT > 1) reads each input frame for KT output frames:
+  // with the output frame varying fastest (frame_fast) those tiles run
+  // together and the frame is fetched into L2 once instead of once per
+  // output frame.
+  int ctile, rtile, ot;
+  if (G::KT > 1 && a.frame_fast) {
+    ot = bid % a.OT;
+    bid /= a.OT;
+    ctile = bid % a.col_tiles;
+    bid /= a.col_tiles;
+    rtile = bid % a.row_tiles;
+    bid /= a.row_tiles;
+  } else {
+    ctile = bid % a.col_tiles;
+    bid /= a.col_tiles;
+    rtile = bid % a.row_tiles;
+    bid /= a.row_tiles;
+    ot = bid % a.OT;
+    bid /= a.OT;
+  }
+  const int n = bid;
   const int co0 = cot * G::BM;
   const int oh0 = rtile * G::TH;
   const int ow0 = ctile * G::TW;
@@ -444,7 +462,7 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
     q.ci0 = chunk * G::CK;
     if constexpr (G::PK) {
       q.rs = wr;
-      q.wrun = (chunk * G::CG * G::TS + kt * G::TS2) * a.kp + co0;
+      q.wrun = (chunk * G::CG * G::TS + kt * G::TS2) * 64 + (co0 >> 6) * a.wblk;
     } else {
       const int sb = q.ci0 * G::TS * EB;
       q.rs = make_rsrc((const char*)a.w + sb, a.w_bytes - sb);
@@ -468,7 +486,7 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
       const int c = wave + k * (kThreads / 64);
       const int slot = c / (G::BM / 64), part = c % (G::BM / 64);
       const int t2 = slot / G::CG, g = slot % G::CG;
-      const int run = q.wrun + (g * G::TS + t2) * a.kp + part * 64;
+      const int run = q.wrun + (g * G::TS + t2) * 64 + part * a.wblk;
       const bool real = c < G::WCHUNKS;  // wave-uniform
       unsigned char* dst = real ? wdst + (slot * G::BM + part * 64) * 16 : lds + G::LDS - 1024;
       copy16_to_lds(q.rs, dst, guard_offset(true, real ? (run + lane) * 16 : kFar));
@@ -929,8 +947,11 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
 }
 
 // ------------------------------------------------------------ weight packing
-// w [K][C][TS] -> wp [G = ceil(C/SE)][TS][Kp][SE] (16 bytes per entry), zero
-// for channels >= C and output channels >= K.  One thread per (output
+// w [K][C][TS] -> wp [Kp/64][G = ceil(C/SE)][TS][64][SE] (16 bytes per
+// entry), zero for channels >= C and output channels >= K.  A block of 64
+// output channels is contiguous: an MFMA tile streams its weights from one
+// range instead of 1 KB pieces at a stride of Kp entries, which spread a
+// tile's weights over a fraction of the L2 sets.  One thread per (output
 // channel, channel group): the group's SE*TS elements are contiguous in w;
 // when C is a multiple of SE they are TS aligned 16-byte vectors, otherwise
 // they are read element by element.  The thread transposes them in registers
@@ -989,7 +1010,7 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackArgs a) {
       }
     }
   }
-  store_packed<SE, TS, 0>(pr, (g * TS * a.Kp + co) * 16, a.Kp * 16, v);
+  store_packed<SE, TS, 0>(pr, (((co >> 6) * a.G + g) * TS * 64 + (co & 63)) * 16, 64 * 16, v);
 }
 
 // ------------------------------------------------------------ split-K sum
@@ -1423,7 +1444,7 @@ libconv_status igemm_launch(const Problem& p, const Plan& plan) {
   a.chunks = chunks_of(*t, p);
   a.ksplit = ks;
   a.cps = (a.chunks + ks - 1) / ks;
-  a.kp = (p.K + kPackAlign - 1) / kPackAlign * kPackAlign;
+  a.wblk = (p.C + (t->wide ? 8 : 4) - 1) / (t->wide ? 8 : 4) * p.KT * p.KH * p.KW * 64;
   a.co_tiles = (int)c.co; a.row_tiles = (int)c.rows; a.col_tiles = (int)c.cols;
   const int eb = dtype_bytes(p.dtype);
   // as many output-channel tiles side by side as keep their weights (of one
@@ -1440,6 +1461,12 @@ libconv_status igemm_launch(const Problem& p, const Plan& plan) {
   a.part_bytes = 0;
   a.vec_out = (a.OW % (16 / eb)) == 0 && (reinterpret_cast<uintptr_t>(p.y) & 15) == 0;
   a.pool = p.pool ? 1 : 0;
+  // Output frames that share input frames side by side only pay while the
+  // tile's weights stay in L2 as well: the edge frames have fewer frame taps
+  // (time padding), so the tiles of one wave drift apart in the channel loop
+  // and stop sharing each weight read.  Measured on the 3x3x3 video-VAE
+  // layers: 442 KB of weights per tile, 8-10% faster; 1.8 MB, 3-6% slower.
+  a.frame_fast = (p.KT > 1 && p.OT > 1 && w_tile <= (1LL << 20)) ? 1 : 0;
   if (p.pool) {  // y holds the pooled output
     a.y_bytes = (uint32_t)((long long)p.N * p.K * (p.OH / 2) * (p.OW / 2) * eb);
     a.vec_out = ((p.OW / 2) % (16 / eb)) == 0 && (reinterpret_cast<uintptr_t>(p.y) & 15) == 0;

@@ -70,7 +70,7 @@ int igemm_tile_occupancy(int id, int dtype, bool measured);
 bool igemm_tile_packed(int tile_id);
 libconv_status igemm_launch(const Problem& p, const Plan& plan);
 
-// Packed weights: [ceil(C/g)][KT*KH*KW][round_up(K, 128)][g] 16-byte entries,
+// Packed weights: [round_up(K, 128) / 64][ceil(C/g)][KT*KH*KW][64][g] 16-byte entries,
 // g = 8 channels (16-bit dtypes) or 4 (fp32).
 long long packed_weight_bytes(int C, int K, int KT, int KH, int KW, int dtype);
 bool pack_supported(int KT, int KH, int KW, int dtype);

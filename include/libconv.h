@@ -150,9 +150,10 @@ libconv_status libconv_forward_algo(const void* x, const void* w, const void* bi
  * kernels stage from, so that a call copies them into on-chip memory without
  * rearranging them (the per-layer weight packing of the Convolution3D backend
  * in "SeedVR2 NCNN Vulkan", section 3.2, does the same at model load).
- * Layout: [ceil(C_in/g)][KT*KH*KW][round_up(C_out, 128)][g] entries of g
- * consecutive input channels (16 bytes), g = 8 for 16-bit dtypes and 4 for
- * fp32; channels beyond C_in / C_out are zero.
+ * Layout: [round_up(C_out, 128) / 64][ceil(C_in/g)][KT*KH*KW][64][g] entries
+ * of g consecutive input channels (16 bytes), g = 8 for 16-bit dtypes and 4
+ * for fp32: blocks of 64 output channels, each contiguous; channels beyond
+ * C_in / C_out are zero.
  *
  * libconv_packed_weight_bytes: size of that buffer, or -1 if the arguments are
  * out of range, the kernel size has no packed kernels (supported: 1x1x1,

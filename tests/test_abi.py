@@ -130,7 +130,7 @@ def test_forced_algorithms():
 
 
 def test_packed_weight_bytes():
-    # [ceil(C/g)][taps][round_up(K,128)][g] x 16 bytes
+    # [round_up(K,128)/64][ceil(C/g)][taps][64][g] x 16 bytes
     assert L.libconv_packed_weight_bytes(128, 128, 3, 3, 3, L.F16) == 16 * 27 * 128 * 16
     assert L.libconv_packed_weight_bytes(12, 200, 1, 3, 3, L.BF16) == 2 * 9 * 256 * 16
     assert L.libconv_packed_weight_bytes(6, 5, 1, 1, 1, L.F32) == 2 * 1 * 128 * 16

@@ -23,14 +23,16 @@ def note(msg):
 
 
 def _expected_packed(w: np.ndarray, se: int, kp_align: int = 128) -> np.ndarray:
-    """The layout definition: [ceil(C/se)][taps][round_up(K,128)][se], zero-filled."""
+    """The layout definition: [round_up(K,128)/64][ceil(C/se)][taps][64][se],
+    zero-filled."""
     K, C = w.shape[:2]
     ts = int(np.prod(w.shape[2:]))
     g = -(-C // se)
     kp = -(-K // kp_align) * kp_align
     wf = np.zeros((kp, g * se, ts), dtype=w.dtype)
     wf[:K, :C] = w.reshape(K, C, ts)
-    return wf.reshape(kp, g, se, ts).transpose(1, 3, 0, 2).copy()   # [g][t][co][j]
+    # [co // 64][g][t][co % 64][j]
+    return wf.reshape(kp // 64, 64, g, se, ts).transpose(0, 2, 4, 1, 3).copy()
 
 
 @pytest.mark.parametrize("dt,C,K,ks", [
