@@ -141,6 +141,59 @@ def cpu_baseline(layers, inputs, budget_s: float):
     return el / runs, threads, runs
 
 
+def long_video(args, torch, L, dev):
+    """A long causal clip through one video-VAE layer (128 -> 128 channels,
+    3x3x3, 256x480, f16): the whole clip on the device against the chunked
+    driver, from device memory and from pinned host memory (two copy
+    streams), with the plain whole-tensor host copies for scale.  Times are
+    means over --steps calls after --warmup, by events on the current stream
+    (which the chunked driver makes wait for its copies)."""
+    T = args.long_video
+    layer = W.ALL_LAYERS["c5_A"].with_(T=T, pad=(2, 1, 1))
+    x, w, b = W.make_inputs(layer, 17)
+    wq = L.pack_weights(w.torch(dev))
+    bt = b.torch(dev)
+    xd = x.torch(dev)
+    shape = (1, 128, T, 256, 480)
+    yd = torch.empty(shape, dtype=torch.float16, device=dev)
+    xh = torch.empty(x.shape, dtype=torch.float16, pin_memory=True)
+    xh.copy_(x.torch("cpu"))
+    yh = torch.empty(shape, dtype=torch.float16, pin_memory=True)
+    # effective work: taps on frames inside the clip only
+    frame_taps = sum(1 for o in range(T) for kt in range(3) if 0 <= o - 2 + kt < T)
+    flop = 2.0 * 128 * 128 * 9 * 256 * 480 * frame_taps
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(args.steps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / args.steps
+
+    c = args.chunk
+    ms = {
+        "whole_device": timed(lambda: L.conv3d_tpad(xd, wq, bt, (2, 0), 1, 1, out=yd)),
+        "chunked_device": timed(lambda: L.conv3d_chunked(xd, wq, bt, c, (2, 0), 1, 1, out=yd)),
+        "chunked_host_pinned": timed(lambda: L.conv3d_chunked(xh, wq, bt, c, (2, 0), 1, 1,
+                                                              out=yh)),
+        "copy_x_host_to_device": timed(lambda: xd.copy_(xh, non_blocking=True)),
+        "copy_y_device_to_host": timed(lambda: yh.copy_(yd, non_blocking=True)),
+    }
+    print(json.dumps({
+        "long_video": {"frames": T, "chunk_out_frames": c, "layer": "128->128 3x3x3 256x480 f16, "
+                       "time pads (2, 0)", "effective_gflop": round(flop / 1e9, 1),
+                       "tensor_mb": round(x.storage.nbytes / 1e6, 1)},
+        "ms": {k: round(v, 3) for k, v in ms.items()},
+        "tflops_effective": {k: round(flop / v / 1e9, 1) for k, v in ms.items()
+                             if not k.startswith("copy")},
+        "note": "host-pinned rates include both PCIe directions; not the bench value"}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -154,6 +207,11 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the workload, copy MIB MiB device-to-device --steps times "
                          "(a plain copy of known size, to scale HBM byte counters)")
+    ap.add_argument("--long-video", type=int, default=0, metavar="FRAMES",
+                    help="instead of the workload, the video-VAE 128-channel causal layer over "
+                         "FRAMES frames: whole on the device, and streamed in chunks of "
+                         "--chunk output frames from device and from pinned host memory")
+    ap.add_argument("--chunk", type=int, default=5)
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -184,6 +242,10 @@ def main():
         print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4,
                           "copies": args.steps,
                           "GBps_read_plus_write": round(2 * n * 4 * args.steps / el / 1e9, 1)}))
+        return
+
+    if args.long_video:
+        long_video(args, torch, L, dev)
         return
 
     _, layers = ALL_WORKLOADS[args.workload]

@@ -89,6 +89,15 @@ def load() -> ctypes.CDLL:
     lib.conv3d_forward_tpad.restype = I
     lib.libconv_out_size2.argtypes = [I] * 5
     lib.libconv_out_size2.restype = I
+    IP = ctypes.POINTER(ctypes.c_int)
+    lib.libconv_frame_window.argtypes = [I] * 7 + [IP, IP]
+    lib.libconv_frame_window.restype = I
+    lib.conv3d_forward_frames.argtypes = [P, P, P, P, P] + [I] * 20 + [P]
+    lib.conv3d_forward_frames.restype = I
+    lib.libconv_chunked_workspace_bytes.argtypes = [I] * 18
+    lib.libconv_chunked_workspace_bytes.restype = LL
+    lib.conv3d_forward_chunked.argtypes = [P, P, P, P, P] + [I] * 17 + [P, LL, I, I, P, P, P]
+    lib.conv3d_forward_chunked.restype = I
     FP = ctypes.POINTER(ctypes.c_float)
     lib.libconv_fold_batchnorm.argtypes = [FP] * 6 + [ctypes.c_float, I, I, FP, FP]
     lib.libconv_fold_batchnorm.restype = I
@@ -145,6 +154,44 @@ def conv3d_forward_tpad(x, w, packed_w, bias, y, N, C_in, T, H, W, C_out, KT, KH
 
 def libconv_out_size2(n_in, k, pad_lo, pad_hi, stride) -> int:
     return load().libconv_out_size2(n_in, k, pad_lo, pad_hi, stride)
+
+
+def libconv_frame_window(T, KT, pad_t_front, pad_t_back, stride_t, out_frame0,
+                         out_frames) -> Tuple[int, int, int]:
+    """Returns (status, in_frame0, in_frames)."""
+    f0, tw = ctypes.c_int(-1), ctypes.c_int(-1)
+    st = load().libconv_frame_window(T, KT, pad_t_front, pad_t_back, stride_t, out_frame0,
+                                     out_frames, ctypes.byref(f0), ctypes.byref(tw))
+    return st, f0.value, tw.value
+
+
+def conv3d_forward_frames(x, w, packed_w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW,
+                          pad_t_front, pad_t_back, pad_h, pad_w, stride_t, stride_h, stride_w,
+                          out_frame0, out_frames, dtype, act, stream) -> int:
+    return load().conv3d_forward_frames(x, w, packed_w, bias, y, N, C_in, T, H, W, C_out, KT,
+                                        KH, KW, pad_t_front, pad_t_back, pad_h, pad_w, stride_t,
+                                        stride_h, stride_w, out_frame0, out_frames, dtype, act,
+                                        stream)
+
+
+def libconv_chunked_workspace_bytes(N, C_in, T, H, W, C_out, KT, KH, KW, pad_t_front,
+                                    pad_t_back, pad_h, pad_w, stride_t, stride_h, stride_w,
+                                    chunk_frames, dtype) -> int:
+    return load().libconv_chunked_workspace_bytes(N, C_in, T, H, W, C_out, KT, KH, KW,
+                                                  pad_t_front, pad_t_back, pad_h, pad_w,
+                                                  stride_t, stride_h, stride_w, chunk_frames,
+                                                  dtype)
+
+
+def conv3d_forward_chunked(x, w, packed_w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW,
+                           pad_t_front, pad_t_back, pad_h, pad_w, stride_t, stride_h, stride_w,
+                           chunk_frames, workspace, workspace_bytes, dtype, act, stream,
+                           copy_in_stream, copy_out_stream) -> int:
+    return load().conv3d_forward_chunked(x, w, packed_w, bias, y, N, C_in, T, H, W, C_out, KT,
+                                         KH, KW, pad_t_front, pad_t_back, pad_h, pad_w,
+                                         stride_t, stride_h, stride_w, chunk_frames, workspace,
+                                         workspace_bytes, dtype, act, stream, copy_in_stream,
+                                         copy_out_stream)
 
 
 def fold_batchnorm(w, b, gamma, beta, mean, var, eps: float):
@@ -441,6 +488,116 @@ def conv3d_tpad(x, w, b=None, pad_t=(0, 0), stride=1, padding_hw=0, act="none", 
     if st_ != 0:
         raise LibconvError(st_, "conv3d_forward_tpad")
     return y
+
+
+def _video_args(x, w, b, stride, padding_hw, pad_t, what, x_on_host_ok):
+    if x.dim() != 5:
+        raise ValueError("x must be NCDHW")
+    packed = isinstance(w, PackedWeights)
+    w_shape = w.w_shape if packed else tuple(w.shape)
+    if len(w_shape) != 5 or w_shape[1] != x.shape[1]:
+        raise ValueError("w must be OIDHW with x's channel count")
+    if not x.is_contiguous() or (not x.is_cuda and not x_on_host_ok):
+        raise ValueError(f"{what}: x must be a contiguous device tensor")
+    for t in (() if packed else (w,)) + ((b,) if b is not None else ()):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != x.dtype:
+            raise ValueError(f"{what}: w, b must be contiguous device tensors of x's dtype")
+    if packed and w.dtype != x.dtype:
+        raise ValueError("packed weights do not match x")
+    st, sh, sw = _triple(stride, 3)
+    ph, pw_ = _triple(padding_hw, 2)
+    return packed, w_shape, (st, sh, sw), (ph, pw_), (int(pad_t[0]), int(pad_t[1]))
+
+
+def conv3d_frames(x, w, b=None, T=None, out_frames=(0, 1), pad_t=(0, 0), stride=1,
+                  padding_hw=0, act="none", out=None, stream=None):
+    """Output frames [o0, o0 + n) (out_frames = (o0, n)) of the convolution
+    over a T-frame video, from x holding only the input frames
+    libconv_frame_window names for them (x [N, C, in_frames, H, W])."""
+    import torch
+    packed, w_shape, (st, sh, sw), (ph, pw_), (pf, pb) = _video_args(
+        x, w, b, stride, padding_hw, pad_t, "conv3d_frames", False)
+    N, C, _, H, W = x.shape
+    K, _, KT, KH, KW = w_shape
+    o0, on = int(out_frames[0]), int(out_frames[1])
+    lib = load()
+    oh = lib.libconv_out_size(H, KH, ph, sh)
+    ow = lib.libconv_out_size(W, KW, pw_, sw)
+    if min(oh, ow) < 1 or on < 1:
+        raise LibconvError(2, "conv3d_frames")
+    shape = (N, K, on, oh, ow)
+    y = torch.empty(shape, dtype=x.dtype, device=x.device) if out is None else out
+    if tuple(y.shape) != shape or not y.is_contiguous() or y.dtype != x.dtype or not y.is_cuda:
+        raise ValueError("bad output tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    st_ = lib.conv3d_forward_frames(_ptr(x), None if packed else _ptr(w),
+                                    w.data.data_ptr() if packed else None, _ptr(b), _ptr(y),
+                                    N, C, int(T), H, W, K, KT, KH, KW, pf, pb, ph, pw_, st, sh, sw,
+                                    o0, on, _dtype_code(x), _ACTS[act], stream)
+    if st_ != 0:
+        raise LibconvError(st_, "conv3d_forward_frames")
+    return y
+
+
+_copy_streams = {}
+
+
+def conv3d_chunked(x, w, b=None, chunk_frames=17, pad_t=(0, 0), stride=1, padding_hw=0,
+                   act="none", out=None, stream=None, copy_streams=None):
+    """The whole-video convolution streamed through the device in chunks of
+    chunk_frames output frames.  x (and the output) may live in host memory
+    (pinned for asynchronous copies) or on the device; weights and bias are
+    device tensors.  copy_streams: (in, out) stream handles for the copies
+    (default: two streams of this module's own; (s, s) with s the compute
+    stream runs everything in order).  A host output is complete when this
+    returns; a device output is ordered on `stream` as usual."""
+    import torch
+    packed, w_shape, (st, sh, sw), (ph, pw_), (pf, pb) = _video_args(
+        x, w, b, stride, padding_hw, pad_t, "conv3d_chunked", True)
+    dev = (w.data if packed else w).device
+    N, C, T, H, W = x.shape
+    K, _, KT, KH, KW = w_shape
+    lib = load()
+    ot = lib.libconv_out_size2(T, KT, pf, pb, st)
+    oh = lib.libconv_out_size(H, KH, ph, sh)
+    ow = lib.libconv_out_size(W, KW, pw_, sw)
+    if min(ot, oh, ow) < 1:
+        raise LibconvError(2, "conv3d_chunked")
+    shape = (N, K, ot, oh, ow)
+    if out is None:
+        out = (torch.empty(shape, dtype=x.dtype, device=dev) if x.is_cuda else
+               torch.empty(shape, dtype=x.dtype, pin_memory=True))
+    if tuple(out.shape) != shape or not out.is_contiguous() or out.dtype != x.dtype:
+        raise ValueError("bad output tensor")
+    dt = _dtype_code(x)
+    ws_bytes = lib.libconv_chunked_workspace_bytes(N, C, T, H, W, K, KT, KH, KW, pf, pb, ph, pw_,
+                                                   st, sh, sw, int(chunk_frames), dt)
+    if ws_bytes < 0:
+        raise LibconvError(2, "conv3d_chunked")
+    cur = torch.cuda.current_stream(dev)
+    if stream is None:
+        stream = cur.cuda_stream
+    if copy_streams is None:
+        pair = _copy_streams.get(dev.index)
+        if pair is None:
+            pair = _copy_streams[dev.index] = (torch.cuda.Stream(dev), torch.cuda.Stream(dev))
+        copy_streams = (pair[0].cuda_stream, pair[1].cuda_stream)
+    # allocated on torch's current stream: later work there is ordered after
+    # `stream` has waited for the last copy, when `stream` is that stream
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    st_ = lib.conv3d_forward_chunked(_ptr(x), None if packed else _ptr(w),
+                                     w.data.data_ptr() if packed else None, _ptr(b), _ptr(out),
+                                     N, C, T, H, W, K, KT, KH, KW, pf, pb, ph, pw_, st, sh, sw,
+                                     int(chunk_frames), ws.data_ptr(), ws_bytes, dt, _ACTS[act],
+                                     stream, copy_streams[0], copy_streams[1])
+    if st_ != 0:
+        raise LibconvError(st_, "conv3d_forward_chunked")
+    if not out.is_cuda or stream != cur.cuda_stream:
+        # host memory is read by the caller next; a foreign stream does not
+        # order the workspace's release
+        torch.cuda.synchronize(dev)
+    return out
 
 
 def conv2d(x, w, b=None, stride=1, padding=0, act="none", algo="auto", out=None, stream=None):

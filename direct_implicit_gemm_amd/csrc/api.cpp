@@ -9,6 +9,7 @@
 // Vulkan", section 3.6, on a Convolution3D that fell back to the CPU).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -320,6 +321,79 @@ Problem make_problem(const void* x, const void* w, const void* bias, void* y, in
   return p;
 }
 
+// The call that computes output frames [o0, o0 + On) of a video convolution
+// from a buffer holding exactly the input frames libconv_frame_window names:
+// the same convolution on that window, with the time padding that makes its
+// first and last taps land where they land in the whole video.
+libconv_status window_problem(Problem* out, const void* x, const void* w, const void* packed_w,
+                              const void* bias, void* y, int N, int C_in, int T, int H, int W,
+                              int C_out, int KT, int KH, int KW, int pad_t_front, int pad_t_back,
+                              int pad_h, int pad_w, int stride_t, int stride_h, int stride_w,
+                              int o0, int On, int dtype, int act, void* stream) {
+  int f0 = 0, tw = 0;
+  const libconv_status st = libconv_frame_window(T, KT, pad_t_front, pad_t_back, stride_t, o0, On,
+                                                 &f0, &tw);
+  if (st != LIBCONV_OK) return st;
+  const long long lo = (long long)o0 * stride_t - pad_t_front;
+  const long long hi = (long long)(o0 + On - 1) * stride_t - pad_t_front + KT;
+  Problem p = make_problem(x, w, bias, y, N, C_in, tw, H, W, C_out, KT, KH, KW,
+                           (int)(f0 - lo), pad_h, pad_w, stride_t, stride_h, stride_w, dtype, act,
+                           stream);
+  p.ptb = (int)(hi - (f0 + tw));
+  p.wp = packed_w;
+  p.no_temps = packed_w != nullptr;  // as libconv_forward_packed: never allocates
+  *out = p;
+  return LIBCONV_OK;
+}
+
+// Geometry of a chunked call: output frames in chunks of `chunk`, each
+// computed from its own input window (consecutive windows overlap by the
+// frames two chunks share).
+struct ChunkPlan {
+  int OT, OH, OW;
+  int chunks;
+  int max_window;        // frames of the largest input window
+  long long x_buf;       // bytes of one input-window buffer (256-byte multiple)
+  long long y_buf;       // bytes of one output-chunk buffer (256-byte multiple)
+};
+
+libconv_status chunk_plan(int N, int C_in, int T, int H, int W, int C_out, int KT, int KH, int KW,
+                          int pad_t_front, int pad_t_back, int pad_h, int pad_w, int stride_t,
+                          int stride_h, int stride_w, int chunk, int dtype, ChunkPlan* cp) {
+  if (dtype != LIBCONV_F32 && dtype != LIBCONV_F16 && dtype != LIBCONV_BF16)
+    return LIBCONV_ERR_BAD_DTYPE;
+  if (N < 0 || C_in < 1 || T < 1 || H < 1 || W < 1 || C_out < 1 || KT < 1 || KH < 1 || KW < 1 ||
+      chunk < 1)
+    return LIBCONV_ERR_BAD_SHAPE;
+  // every output frame must read at least one input frame
+  if (pad_t_front < 0 || pad_t_back < 0 || pad_t_front >= KT || pad_t_back >= KT)
+    return LIBCONV_ERR_BAD_SHAPE;
+  const long long ot = out_extent2(T, KT, pad_t_front, pad_t_back, stride_t);
+  const long long oh = out_extent(H, KH, pad_h, stride_h);
+  const long long ow = out_extent(W, KW, pad_w, stride_w);
+  if (ot < 1 || oh < 1 || ow < 1) return LIBCONV_ERR_BAD_SHAPE;
+  if (ot > 0x7fffffff || oh > 0x7fffffff || ow > 0x7fffffff) return LIBCONV_ERR_TOO_LARGE;
+  cp->OT = (int)ot; cp->OH = (int)oh; cp->OW = (int)ow;
+  chunk = (int)std::min<long long>(chunk, ot);
+  cp->chunks = (int)((ot + chunk - 1) / chunk);
+  cp->max_window = 0;
+  for (int c = 0; c < cp->chunks; ++c) {
+    int f0 = 0, tw = 0;
+    const int o0 = c * chunk;
+    const libconv_status st = libconv_frame_window(
+        T, KT, pad_t_front, pad_t_back, stride_t, o0, std::min(chunk, cp->OT - o0), &f0, &tw);
+    if (st != LIBCONV_OK) return st;
+    cp->max_window = std::max(cp->max_window, tw);
+  }
+  const long long eb = dtype_bytes(dtype);
+  const long long xb = product({N, C_in, cp->max_window, H, W, eb});
+  const long long yb = product({N, C_out, chunk, oh, ow, eb});
+  if (xb > kMaxBytes || yb > kMaxBytes) return LIBCONV_ERR_TOO_LARGE;
+  cp->x_buf = (xb + 255) / 256 * 256;
+  cp->y_buf = (yb + 255) / 256 * 256;
+  return LIBCONV_OK;
+}
+
 }  // namespace
 
 libconv_status stream_alloc(size_t bytes, hipStream_t stream, void** out) {
@@ -437,6 +511,187 @@ libconv_status conv3d_forward_tpad(const void* x, const void* w, const void* pac
     return run(p, LIBCONV_ALGO_IGEMM);
   }
   return run(p, LIBCONV_ALGO_AUTO);
+}
+
+libconv_status libconv_frame_window(int T, int KT, int pad_t_front, int pad_t_back, int stride_t,
+                                    int out_frame0, int out_frames, int* in_frame0,
+                                    int* in_frames) {
+  if (!in_frame0 || !in_frames) return LIBCONV_ERR_NULL_POINTER;
+  const long long ot = out_extent2(T, KT, pad_t_front, pad_t_back, stride_t);
+  if (ot < 1 || out_frame0 < 0 || out_frames < 1 || (long long)out_frame0 + out_frames > ot)
+    return LIBCONV_ERR_BAD_SHAPE;
+  // Output frame o reads frames o*stride_t - pad_t_front + kt, 0 <= kt < KT,
+  // of which those in [0, T) exist: at least one exactly when
+  // o*stride_t > pad_t_front - KT and o*stride_t < T + pad_t_front, which
+  // holds for a contiguous run of output frames.
+  auto floordiv = [](long long a, long long b) { return a >= 0 ? a / b : -((-a + b - 1) / b); };
+  const long long s = stride_t;
+  const long long o_lo = std::max<long long>(out_frame0, floordiv(pad_t_front - KT, s) + 1);
+  const long long o_hi = std::min<long long>(out_frame0 + out_frames - 1,
+                                             floordiv((long long)T + pad_t_front - 1, s));
+  if (o_lo > o_hi) return LIBCONV_ERR_BAD_SHAPE;  // those output frames read padding only
+  const long long f0 = std::max(0LL, o_lo * s - pad_t_front);
+  const long long f1 = std::min<long long>(T, o_hi * s - pad_t_front + KT);
+  *in_frame0 = (int)f0;
+  *in_frames = (int)(f1 - f0);
+  return LIBCONV_OK;
+}
+
+libconv_status conv3d_forward_frames(const void* x, const void* w, const void* packed_w,
+                                     const void* bias, void* y, int N, int C_in, int T, int H,
+                                     int W, int C_out, int KT, int KH, int KW, int pad_t_front,
+                                     int pad_t_back, int pad_h, int pad_w, int stride_t,
+                                     int stride_h, int stride_w, int out_frame0, int out_frames,
+                                     int dtype, int act, void* stream) {
+  if ((w == nullptr) == (packed_w == nullptr)) return LIBCONV_ERR_NULL_POINTER;
+  Problem p;
+  const libconv_status st =
+      window_problem(&p, x, w, packed_w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW,
+                     pad_t_front, pad_t_back, pad_h, pad_w, stride_t, stride_h, stride_w,
+                     out_frame0, out_frames, dtype, act, stream);
+  if (st != LIBCONV_OK) return st;
+  return run(p, packed_w ? LIBCONV_ALGO_IGEMM : LIBCONV_ALGO_AUTO);
+}
+
+long long libconv_chunked_workspace_bytes(int N, int C_in, int T, int H, int W, int C_out, int KT,
+                                          int KH, int KW, int pad_t_front, int pad_t_back,
+                                          int pad_h, int pad_w, int stride_t, int stride_h,
+                                          int stride_w, int chunk_frames, int dtype) {
+  ChunkPlan cp;
+  if (chunk_plan(N, C_in, T, H, W, C_out, KT, KH, KW, pad_t_front, pad_t_back, pad_h, pad_w,
+                 stride_t, stride_h, stride_w, chunk_frames, dtype, &cp) != LIBCONV_OK)
+    return -1;
+  return 2 * (cp.x_buf + cp.y_buf);
+}
+
+libconv_status conv3d_forward_chunked(const void* x, const void* w, const void* packed_w,
+                                      const void* bias, void* y, int N, int C_in, int T, int H,
+                                      int W, int C_out, int KT, int KH, int KW, int pad_t_front,
+                                      int pad_t_back, int pad_h, int pad_w, int stride_t,
+                                      int stride_h, int stride_w, int chunk_frames,
+                                      void* workspace, long long workspace_bytes, int dtype,
+                                      int act, void* stream, void* copy_in_stream,
+                                      void* copy_out_stream) {
+  if ((w == nullptr) == (packed_w == nullptr)) return LIBCONV_ERR_NULL_POINTER;
+  if (act != LIBCONV_ACT_NONE && act != LIBCONV_ACT_RELU) return LIBCONV_ERR_BAD_ACTIVATION;
+  ChunkPlan cp;
+  libconv_status st = chunk_plan(N, C_in, T, H, W, C_out, KT, KH, KW, pad_t_front, pad_t_back,
+                                 pad_h, pad_w, stride_t, stride_h, stride_w, chunk_frames, dtype,
+                                 &cp);
+  if (st != LIBCONV_OK) return st;
+  if (!x || !y || !workspace) return LIBCONV_ERR_NULL_POINTER;
+  if (workspace_bytes < 2 * (cp.x_buf + cp.y_buf)) return LIBCONV_ERR_BAD_SHAPE;
+  const size_t eb = (size_t)dtype_bytes(dtype);
+  const size_t x_frame = (size_t)H * W * eb, y_frame = (size_t)cp.OH * cp.OW * eb;
+  const size_t x_all = (size_t)N * C_in * T * x_frame, y_all = (size_t)N * C_out * cp.OT * y_frame;
+  if (overlaps(y, (long long)y_all, x, (long long)x_all) ||
+      overlaps(workspace, workspace_bytes, x, (long long)x_all) ||
+      overlaps(workspace, workspace_bytes, y, (long long)y_all))
+    return LIBCONV_ERR_ALIAS;
+  if (N == 0) return LIBCONV_OK;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || !device_ok(dev)) {
+    (void)hipGetLastError();
+    return LIBCONV_ERR_NO_DEVICE;
+  }
+  const hipStream_t cs = reinterpret_cast<hipStream_t>(stream);
+  const hipStream_t ki = copy_in_stream ? reinterpret_cast<hipStream_t>(copy_in_stream) : cs;
+  const hipStream_t ko = copy_out_stream ? reinterpret_cast<hipStream_t>(copy_out_stream) : ki;
+  for (hipStream_t s : {cs, ki, ko}) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cap) != hipSuccess) {
+      (void)hipGetLastError();
+      return LIBCONV_ERR_LAUNCH;
+    }
+    if (cap != hipStreamCaptureStatusNone) return LIBCONV_ERR_UNSUPPORTED;
+  }
+  const bool sync = ki != cs || ko != cs;  // more than one stream: order them with events
+  const int chunk = std::min(chunk_frames, cp.OT);
+  char* ws = static_cast<char*>(workspace);
+  void* xb[2] = {ws, ws + cp.x_buf};
+  void* yb[2] = {ws + 2 * cp.x_buf, ws + 2 * cp.x_buf + cp.y_buf};
+  // ev_in[b] / ev_conv[b] / ev_out[b]: the latest copy into xb[b], convolution
+  // into yb[b], copy out of yb[b]; ev_edge: the start and the end of the call.
+  hipEvent_t ev[7] = {};
+  hipEvent_t *ev_in = ev, *ev_conv = ev + 2, *ev_out = ev + 4, &ev_edge = ev[6];
+  auto ok = [](hipError_t e) {
+    if (e == hipSuccess) return true;
+    (void)hipGetLastError();
+    return false;
+  };
+  if (sync) {
+    for (hipEvent_t& e : ev) {
+      if (!ok(hipEventCreateWithFlags(&e, hipEventDisableTiming))) {
+        for (hipEvent_t d : ev)
+          if (d) (void)hipEventDestroy(d);
+        return LIBCONV_ERR_LAUNCH;
+      }
+    }
+  }
+  auto record = [&](hipEvent_t e, hipStream_t s) { return !sync || ok(hipEventRecord(e, s)); };
+  auto wait = [&](hipStream_t s, hipEvent_t e) {
+    return !sync || ok(hipStreamWaitEvent(s, e, 0));
+  };
+  // Input window of chunk c into xb[c & 1]: N*C_in rows of tw frames, taken
+  // at frame f0 of rows T frames apart.  Its buffer was last read by
+  // conv(c - 2).
+  auto copy_in = [&](int c) -> libconv_status {
+    const int o0 = c * chunk, on = std::min(chunk, cp.OT - o0);
+    int f0 = 0, tw = 0;
+    const libconv_status s = libconv_frame_window(T, KT, pad_t_front, pad_t_back, stride_t, o0,
+                                                  on, &f0, &tw);
+    if (s != LIBCONV_OK) return s;
+    if (c >= 2 && !wait(ki, ev_conv[c & 1])) return LIBCONV_ERR_LAUNCH;
+    const char* src = static_cast<const char*>(x) + (size_t)f0 * x_frame;
+    if (!ok(hipMemcpy2DAsync(xb[c & 1], tw * x_frame, src, (size_t)T * x_frame, tw * x_frame,
+                             (size_t)N * C_in, hipMemcpyDefault, ki)))
+      return LIBCONV_ERR_LAUNCH;
+    return record(ev_in[c & 1], ki) ? LIBCONV_OK : LIBCONV_ERR_LAUNCH;
+  };
+  // Output chunk c from yb[c & 1] into frames [o0, o0 + on) of y, once
+  // conv(c) is done.
+  auto copy_out = [&](int c) -> libconv_status {
+    const int o0 = c * chunk, on = std::min(chunk, cp.OT - o0);
+    if (!wait(ko, ev_conv[c & 1])) return LIBCONV_ERR_LAUNCH;
+    char* dst = static_cast<char*>(y) + (size_t)o0 * y_frame;
+    if (!ok(hipMemcpy2DAsync(dst, (size_t)cp.OT * y_frame, yb[c & 1], on * y_frame, on * y_frame,
+                             (size_t)N * C_out, hipMemcpyDefault, ko)))
+      return LIBCONV_ERR_LAUNCH;
+    return record(ev_out[c & 1], ko) ? LIBCONV_OK : LIBCONV_ERR_LAUNCH;
+  };
+  // The copies start after the work already on `stream` (which may produce
+  // x or still use y).  The window of chunk c + 1 is copied in before chunk
+  // c's output is copied out, so that with one copy stream the next input
+  // does not queue behind an output that waits for the convolution.
+  if (!record(ev_edge, cs) || !wait(ki, ev_edge) || !wait(ko, ev_edge)) st = LIBCONV_ERR_LAUNCH;
+  if (st == LIBCONV_OK) st = copy_in(0);
+  for (int c = 0; c < cp.chunks && st == LIBCONV_OK; ++c) {
+    if (c + 1 < cp.chunks && (st = copy_in(c + 1)) != LIBCONV_OK) break;
+    if (!wait(cs, ev_in[c & 1]) || (c >= 2 && !wait(cs, ev_out[c & 1]))) {
+      st = LIBCONV_ERR_LAUNCH;
+      break;
+    }
+    const int o0 = c * chunk, on = std::min(chunk, cp.OT - o0);
+    Problem p;
+    st = window_problem(&p, xb[c & 1], w, packed_w, bias, yb[c & 1], N, C_in, T, H, W, C_out, KT,
+                        KH, KW, pad_t_front, pad_t_back, pad_h, pad_w, stride_t, stride_h,
+                        stride_w, o0, on, dtype, act, stream);
+    if (st == LIBCONV_OK) st = run(p, packed_w ? LIBCONV_ALGO_IGEMM : LIBCONV_ALGO_AUTO);
+    if (st != LIBCONV_OK) break;
+    if (!record(ev_conv[c & 1], cs)) {
+      st = LIBCONV_ERR_LAUNCH;
+      break;
+    }
+    st = copy_out(c);
+  }
+  if (sync) {
+    // `stream` continues after every copy (also after a failure part-way,
+    // so that nothing the caller frees next is still in use)
+    for (hipStream_t s : {ki, ko})
+      if (s != cs && ok(hipEventRecord(ev_edge, s))) (void)ok(hipStreamWaitEvent(cs, ev_edge, 0));
+    for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+  }
+  return st;
 }
 
 libconv_status libconv_forward_packed(const void* x, const void* packed_w, const void* bias,

@@ -223,6 +223,92 @@ libconv_status conv3d_forward_tpad(const void* x, const void* w, const void* pac
                                    int dtype, int act, void* stream);
 
 /*
+ * Frame windows of a long video.  A 3-D convolution can be computed a few
+ * output frames at a time, each piece from only the input frames it reads;
+ * consecutive pieces share the frames their taps overlap on (KT - stride_t
+ * frames).  This is how a video too long to hold whole goes through the
+ * network: the long-video plan of "SeedVR2 NCNN Vulkan", section 9, cuts it
+ * into chunks of 17 frames that overlap by 5.  Per convolution the pieces
+ * compute the whole-video result: each output element is the same sum,
+ * rounded once (the kernel chosen for a piece may differ from the
+ * whole-video one, and with it the order of the fp32 sums).
+ *
+ * libconv_frame_window: the input frames [*in_frame0, *in_frame0 +
+ * *in_frames) that output frames [out_frame0, out_frame0 + out_frames) of a
+ * convolution over T frames read (time padding as conv3d_forward_tpad).
+ * Pure host arithmetic.  LIBCONV_ERR_BAD_SHAPE when the output range is
+ * empty or beyond the output frames, or reads padding only;
+ * LIBCONV_ERR_NULL_POINTER for NULL outputs.
+ */
+libconv_status libconv_frame_window(int T, int KT, int pad_t_front, int pad_t_back,
+                                    int stride_t, int out_frame0, int out_frames,
+                                    int* in_frame0, int* in_frames);
+
+/*
+ * Output frames [out_frame0, out_frame0 + out_frames) of the convolution
+ * conv3d_forward_tpad computes over a T-frame video, from a buffer holding
+ * only the input frames libconv_frame_window names for that range.
+ * x [N][C_in][in_frames][H][W] (device), y [N][C_out][out_frames][OH][OW]
+ * (device), both contiguous; the other arguments describe the whole video
+ * and are those of conv3d_forward_tpad (exactly one of w and packed_w).
+ * Same errors as conv3d_forward_tpad, and LIBCONV_ERR_BAD_SHAPE for an
+ * output range libconv_frame_window rejects.
+ */
+libconv_status conv3d_forward_frames(const void* x, const void* w, const void* packed_w,
+                                     const void* bias, void* y,
+                                     int N, int C_in, int T, int H, int W,
+                                     int C_out, int KT, int KH, int KW,
+                                     int pad_t_front, int pad_t_back, int pad_h, int pad_w,
+                                     int stride_t, int stride_h, int stride_w,
+                                     int out_frame0, int out_frames,
+                                     int dtype, int act, void* stream);
+
+/*
+ * Device workspace conv3d_forward_chunked needs: two input-window and two
+ * output-chunk buffers.  -1 if the arguments are invalid for it.
+ */
+long long libconv_chunked_workspace_bytes(int N, int C_in, int T, int H, int W,
+                                          int C_out, int KT, int KH, int KW,
+                                          int pad_t_front, int pad_t_back,
+                                          int pad_h, int pad_w,
+                                          int stride_t, int stride_h, int stride_w,
+                                          int chunk_frames, int dtype);
+
+/*
+ * The whole-video convolution of conv3d_forward_tpad, streamed in chunks of
+ * chunk_frames output frames: x [N][C_in][T][H][W] and y
+ * [N][C_out][OT][OH][OW] may be host memory (pinned memory lets the copies
+ * run asynchronously; pageable memory works, with copies that block the
+ * host) or device memory, and may be larger than the 2^31-byte limit of the
+ * other calls; only one chunk's window and output are on the device at a
+ * time, in `workspace` (device, caller-owned, at least
+ * libconv_chunked_workspace_bytes).  Chunk c + 1's window is copied in on
+ * copy_in_stream and chunk c - 1's output copied out on copy_out_stream
+ * while chunk c computes on `stream` (the two copy streams let the two
+ * directions of the host link run at once).  The copies start after the
+ * work already on `stream`, and `stream` waits for the last of them.
+ * copy_out_stream NULL: outputs are copied on copy_in_stream; both NULL:
+ * everything runs in order on `stream`.  Weights and bias are on the device;
+ * exactly one of w and packed_w (with OIDHW weights a packed kernel packs
+ * them per chunk: pass packed weights for long videos).  Requires
+ * pad_t_front < KT and pad_t_back < KT (every output frame reads an input
+ * frame).  LIBCONV_ERR_UNSUPPORTED while either stream is being captured
+ * into a graph; a too-small workspace is LIBCONV_ERR_BAD_SHAPE.  The call
+ * returns once everything is enqueued: the caller synchronises `stream`
+ * before reading y or reusing x or the workspace.
+ */
+libconv_status conv3d_forward_chunked(const void* x, const void* w, const void* packed_w,
+                                      const void* bias, void* y,
+                                      int N, int C_in, int T, int H, int W,
+                                      int C_out, int KT, int KH, int KW,
+                                      int pad_t_front, int pad_t_back, int pad_h, int pad_w,
+                                      int stride_t, int stride_h, int stride_w,
+                                      int chunk_frames, void* workspace,
+                                      long long workspace_bytes, int dtype, int act,
+                                      void* stream, void* copy_in_stream,
+                                      void* copy_out_stream);
+
+/*
  * Which kernel the dispatcher would launch for this shape, without launching.
  * Arguments as for libconv_forward_algo (algo may force a family).  On
  * LIBCONV_OK: *algo_out is LIBCONV_ALGO_DIRECT or LIBCONV_ALGO_IGEMM,
