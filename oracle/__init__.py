@@ -232,3 +232,31 @@ def max_pool2x2(y: np.ndarray) -> np.ndarray:
     t = y[..., :2 * oh, :2 * ow]
     return np.maximum(np.maximum(t[..., 0::2, 0::2], t[..., 0::2, 1::2]),
                       np.maximum(t[..., 1::2, 0::2], t[..., 1::2, 1::2]))
+
+
+def pack_channels(x: np.ndarray, group: int) -> np.ndarray:
+    """Channel-packed activations: x [N][C][...spatial] as
+    [N][ceil(C/group)][...spatial][group], element [n][c // group][...][c % group]
+    = x[n][c][...], and zero in the channels past C of the last group.  The
+    channel packing the page "SeedVR2 NCNN Vulkan" plans to keep through the
+    whole network (section 9: pack4 kept across layers; groups of 4 channels
+    there, one 16-byte vector of channels here).  Written as a loop over
+    channels so that the definition is read off directly."""
+    x = np.asarray(x)
+    n, c = x.shape[:2]
+    groups = -(-c // group)
+    out = np.zeros((n, groups) + x.shape[2:] + (group,), dtype=x.dtype)
+    for ch in range(c):
+        out[:, ch // group, ..., ch % group] = x[:, ch]
+    return out
+
+
+def unpack_channels(xp: np.ndarray, channels: int) -> np.ndarray:
+    """The inverse of pack_channels: the first `channels` channels of a
+    channel-packed tensor, back as [N][C][...spatial]."""
+    xp = np.asarray(xp)
+    n, group = xp.shape[0], xp.shape[-1]
+    out = np.empty((n, channels) + xp.shape[2:-1], dtype=xp.dtype)
+    for ch in range(channels):
+        out[:, ch] = xp[:, ch // group, ..., ch % group]
+    return out

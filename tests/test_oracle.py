@@ -502,3 +502,30 @@ def test_max_pool2x2_matches_torch():
         y = r.standard_normal(shape)
         ref = torch.nn.functional.max_pool2d(torch.from_numpy(y), 2, 2).numpy()
         np.testing.assert_array_equal(oracle.max_pool2x2(y), ref)
+
+
+def test_pack_channels_matches_torch_reshape():
+    """Channel packing against torch's route (zero-pad the channel axis, split
+    it into groups, move the in-group index last), 2-D and 3-D, with and
+    without a partial last group."""
+    r = _rng(96)
+    for shape, g in [((2, 8, 3, 5), 8), ((1, 13, 4, 6), 8), ((1, 6, 2, 3, 4), 4), ((2, 3, 5, 7), 4)]:
+        x = r.standard_normal(shape)
+        c = shape[1]
+        gs = -(-c // g)
+        t = torch.nn.functional.pad(torch.from_numpy(x).movedim(1, -1), (0, gs * g - c))
+        t = t.reshape(t.shape[:-1] + (gs, g)).movedim(-2, 1)
+        np.testing.assert_array_equal(oracle.pack_channels(x, g), t.numpy())
+
+
+def test_pack_channels_index_rule_and_roundtrip():
+    """Element [n][c // g][h][w][c % g] holds x[n][c][h][w]: an iota tensor
+    shows every element in its place; the pad channels are zero; unpacking
+    returns x."""
+    x = np.arange(2 * 11 * 3 * 4, dtype=np.float64).reshape(2, 11, 3, 4)
+    p = oracle.pack_channels(x, 8)
+    assert p.shape == (2, 2, 3, 4, 8)
+    for n, c, h, w in itertools.product(range(2), range(11), range(3), range(4)):
+        assert p[n, c // 8, h, w, c % 8] == x[n, c, h, w]
+    assert not p[:, 1, :, :, 3:].any()
+    np.testing.assert_array_equal(oracle.unpack_channels(p, 11), x)
