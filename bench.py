@@ -61,6 +61,10 @@ WORKLOAD_TEXT = {
     "vae3d_causal_f16": ("video-VAE f16 causal conv3d N=1 T=5 (2 frames of time padding "
                          "before the first frame, none after): 3x3x3 128->128 on 256x480; "
                          "3x3x3 512->512 on 64x120 +ReLU"),
+    "vae3d_cpack_f16": ("the video-VAE f16 conv3d layers on channel-packed activations "
+                        "([N][C/8][T][H][W][8], packed once before timing)"),
+    "unet_cpack_bf16": ("the diffusion-UNet bf16 layers on channel-packed activations "
+                        "([N][C/8][H][W][8], packed once before timing)"),
 }
 ALL_WORKLOADS = {**W.WORKLOADS, **W.EXTRA_WORKLOADS}
 
@@ -254,8 +258,9 @@ def main():
     inputs = [W.make_inputs(l) for l in layers]
     chained = args.workload in ("ocr_stack",)
     xs, ws, bs = [], [], []
-    for (x, w, b) in inputs:
-        xs.append(x.torch(dev))
+    for l, (x, w, b) in zip(layers, inputs):
+        # channel-packed layers: the input is packed once, at the network's edge
+        xs.append(L.pack_activations(x.torch(dev)) if l.cpack else x.torch(dev))
         ws.append(w.torch(dev))
         bs.append(b.torch(dev))
     outs = []
@@ -264,13 +269,21 @@ def main():
         if l.pool:
             oh, ow = oh // 2, ow // 2
         shape = (l.N, l.C_out, oh, ow) if l.dims == 2 else (l.N, l.C_out, ot, oh, ow)
-        outs.append(torch.empty(shape, dtype=xs[i].dtype, device=dev))
+        if l.cpack:
+            nb = lib.libconv_cpack_bytes(l.N, l.C_out, ot, oh, ow, W.DTYPE_CODE[l.dtype])
+            outs.append(L.PackedActivations(torch.empty(nb, dtype=torch.uint8, device=dev),
+                                            shape, xs[i].dtype))
+        else:
+            outs.append(torch.empty(shape, dtype=xs[i].dtype, device=dev))
 
     def sp(l):
         return (l.stride[1:], l.pad[1:]) if l.dims == 2 else (l.stride, l.pad)
 
     def conv(l, x_in, w, b, out):
-        if l.pool:  # conv + activation + 2x2 max pool in one call
+        if l.cpack:  # channel-packed activations in and out
+            s, p = sp(l)
+            L.conv_cpack(x_in, w, b, s, p, time_pads(l) if l.dims == 3 else None, l.act, out=out)
+        elif l.pool:  # conv + activation + 2x2 max pool in one call
             L.conv2d_pool(x_in, w, b, l.stride[1:], l.pad[1:], l.act, out=out)
         elif l.pad_t_back is not None:  # time padding differs before / after the frames
             L.conv3d_tpad(x_in, w, b, time_pads(l), l.stride, l.pad[1:], l.act, out=out)
@@ -346,7 +359,8 @@ def main():
         st_, algo, tile, grid, ks = L.libconv_query_plan(
             l.N, l.C_in, l.T, l.H, l.W, l.C_out, l.KT, l.KH, l.KW, *pad, *l.stride,
             W.DTYPE_CODE[l.dtype], W.ACT_CODE[l.act], L.ALGO_AUTO,
-            (L.PLAN_CAPTURING if capturing else 0) | (L.PLAN_POOL2 if l.pool else 0))
+            (L.PLAN_CAPTURING if capturing else 0) | (L.PLAN_POOL2 if l.pool else 0)
+            | (L.PLAN_CPACK if l.cpack else 0))
         return algo, tile, grid, ks
 
     b2b, b2b_graph = [], []

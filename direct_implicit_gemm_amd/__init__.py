@@ -98,6 +98,14 @@ def load() -> ctypes.CDLL:
     lib.libconv_chunked_workspace_bytes.restype = LL
     lib.conv3d_forward_chunked.argtypes = [P, P, P, P, P] + [I] * 17 + [P, LL, I, I, P, P, P]
     lib.conv3d_forward_chunked.restype = I
+    lib.libconv_cpack_bytes.argtypes = [I] * 6
+    lib.libconv_cpack_bytes.restype = LL
+    lib.libconv_pack_activations.argtypes = [P, P] + [I] * 6 + [P]
+    lib.libconv_pack_activations.restype = I
+    lib.libconv_unpack_activations.argtypes = [P, P] + [I] * 6 + [P]
+    lib.libconv_unpack_activations.restype = I
+    lib.conv3d_forward_cpack.argtypes = [P, P, P, P, P] + [I] * 18 + [P]
+    lib.conv3d_forward_cpack.restype = I
     FP = ctypes.POINTER(ctypes.c_float)
     lib.libconv_fold_batchnorm.argtypes = [FP] * 6 + [ctypes.c_float, I, I, FP, FP]
     lib.libconv_fold_batchnorm.restype = I
@@ -135,7 +143,7 @@ def libconv_forward_algo(x, w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW, pad
                                        dtype, act, algo, stream)
 
 
-PLAN_CAPTURING, PLAN_POOL2 = 1, 2
+PLAN_CAPTURING, PLAN_POOL2, PLAN_CPACK = 1, 2, 4
 
 
 def conv2d_forward_pool(x, w, bias, y, N, C_in, H, W, C_out, KH, KW, pad_h, pad_w, stride_h,
@@ -154,6 +162,26 @@ def conv3d_forward_tpad(x, w, packed_w, bias, y, N, C_in, T, H, W, C_out, KT, KH
 
 def libconv_out_size2(n_in, k, pad_lo, pad_hi, stride) -> int:
     return load().libconv_out_size2(n_in, k, pad_lo, pad_hi, stride)
+
+
+def libconv_cpack_bytes(N, C, T, H, W, dtype) -> int:
+    return load().libconv_cpack_bytes(N, C, T, H, W, dtype)
+
+
+def libconv_pack_activations(x, x_packed, N, C, T, H, W, dtype, stream) -> int:
+    return load().libconv_pack_activations(x, x_packed, N, C, T, H, W, dtype, stream)
+
+
+def libconv_unpack_activations(x_packed, x, N, C, T, H, W, dtype, stream) -> int:
+    return load().libconv_unpack_activations(x_packed, x, N, C, T, H, W, dtype, stream)
+
+
+def conv3d_forward_cpack(x, w, packed_w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW,
+                         pad_t_front, pad_t_back, pad_h, pad_w, stride_t, stride_h, stride_w,
+                         dtype, act, stream) -> int:
+    return load().conv3d_forward_cpack(x, w, packed_w, bias, y, N, C_in, T, H, W, C_out, KT, KH,
+                                       KW, pad_t_front, pad_t_back, pad_h, pad_w, stride_t,
+                                       stride_h, stride_w, dtype, act, stream)
 
 
 def libconv_frame_window(T, KT, pad_t_front, pad_t_back, stride_t, out_frame0,
@@ -538,6 +566,118 @@ def conv3d_frames(x, w, b=None, T=None, out_frames=(0, 1), pad_t=(0, 0), stride=
     if st_ != 0:
         raise LibconvError(st_, "conv3d_forward_frames")
     return y
+
+
+class PackedActivations:
+    """A channel-packed activation tensor on the device: ``data`` holds
+    [N][ceil(C/g)][T][H][W][g] (g = 16 bytes of channels) as raw bytes;
+    ``shape`` is the plain (N, C, [T,] H, W) shape it stands for."""
+
+    def __init__(self, data, shape, dtype):
+        self.data = data
+        self.shape = tuple(shape)
+        self.dtype = dtype
+
+    @property
+    def group(self) -> int:
+        import torch
+        return 4 if self.dtype == torch.float32 else 8
+
+    def _dims(self):
+        if len(self.shape) == 4:
+            n, c, h, w = self.shape
+            return n, c, 1, h, w
+        return self.shape
+
+
+def pack_activations(x, stream=None) -> PackedActivations:
+    """Plain NC(T)HW device tensor -> channel-packed copy."""
+    import torch
+    if x.dim() not in (4, 5) or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous NCHW or NCDHW device tensor")
+    dims = (x.shape[0], x.shape[1], 1, x.shape[2], x.shape[3]) if x.dim() == 4 else tuple(x.shape)
+    dt = _dtype_code(x)
+    lib = load()
+    nb = lib.libconv_cpack_bytes(*dims, dt)
+    if nb < 0:
+        raise LibconvError(2, "pack_activations")
+    data = torch.empty(max(nb, 1), dtype=torch.uint8, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    st = lib.libconv_pack_activations(_ptr(x), data.data_ptr(), *dims, dt, stream)
+    if st != 0:
+        raise LibconvError(st, "libconv_pack_activations")
+    return PackedActivations(data, x.shape, x.dtype)
+
+
+def unpack_activations(xp: PackedActivations, out=None, stream=None):
+    """Channel-packed -> plain NC(T)HW device tensor."""
+    import torch
+    y = torch.empty(xp.shape, dtype=xp.dtype, device=xp.data.device) if out is None else out
+    if tuple(y.shape) != xp.shape or y.dtype != xp.dtype or not y.is_contiguous():
+        raise ValueError("bad output tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(y.device).cuda_stream
+    st = load().libconv_unpack_activations(xp.data.data_ptr(), _ptr(y), *xp._dims(),
+                                           _dtype_code(y), stream)
+    if st != 0:
+        raise LibconvError(st, "libconv_unpack_activations")
+    return y
+
+
+def conv_cpack(xp: PackedActivations, w, b=None, stride=1, padding=0, pad_t=None, act="none",
+               out=None, stream=None) -> PackedActivations:
+    """Convolution on channel-packed activations; returns the packed output.
+    w: OI(D)HW device tensor or PackedWeights.  2-D when xp stands for NCHW.
+    padding: (h, w) or (t, h, w); pad_t = (front, back) overrides the time
+    padding."""
+    import torch
+    packed = isinstance(w, PackedWeights)
+    w_shape = w.w_shape if packed else tuple(w.shape)
+    N, C, T, H, W = xp._dims()
+    nd = len(xp.shape) - 2
+    if len(w_shape) != nd + 2 or w_shape[1] != C:
+        raise ValueError("w does not match the activations")
+    if not packed and (not w.is_cuda or not w.is_contiguous() or w.dtype != xp.dtype):
+        raise ValueError("w must be a contiguous device tensor of the activations' dtype")
+    if b is not None and (not b.is_cuda or not b.is_contiguous() or b.dtype != xp.dtype):
+        raise ValueError("b must be a contiguous device tensor of the activations' dtype")
+    K = w_shape[0]
+    if nd == 2:
+        KT, (KH, KW) = 1, w_shape[2:]
+        st, (sh, sw) = 1, _triple(stride, 2)
+        pf = pb = 0
+        ph, pw_ = _triple(padding, 2)
+    else:
+        KT, KH, KW = w_shape[2:]
+        st, sh, sw = _triple(stride, 3)
+        pt_, ph, pw_ = _triple(padding, 3)
+        pf, pb = (pt_, pt_) if pad_t is None else (int(pad_t[0]), int(pad_t[1]))
+    lib = load()
+    ot = lib.libconv_out_size2(T, KT, pf, pb, st)
+    oh = lib.libconv_out_size(H, KH, ph, sh)
+    ow = lib.libconv_out_size(W, KW, pw_, sw)
+    if min(ot, oh, ow) < 1:
+        raise LibconvError(2, "conv_cpack")
+    dt = _dtype_code(torch.empty(0, dtype=xp.dtype))
+    nb = lib.libconv_cpack_bytes(N, K, ot, oh, ow, dt)
+    if nb < 0:
+        raise LibconvError(10, "conv_cpack")
+    shape = (N, K, oh, ow) if nd == 2 else (N, K, ot, oh, ow)
+    if out is None:
+        out = PackedActivations(torch.empty(max(nb, 1), dtype=torch.uint8, device=xp.data.device),
+                                shape, xp.dtype)
+    elif out.shape != shape or out.dtype != xp.dtype or out.data.numel() < nb:
+        raise ValueError("bad output tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(xp.data.device).cuda_stream
+    st_ = lib.conv3d_forward_cpack(xp.data.data_ptr(), None if packed else _ptr(w),
+                                   w.data.data_ptr() if packed else None, _ptr(b),
+                                   out.data.data_ptr(), N, C, T, H, W, K, KT, KH, KW, pf, pb, ph,
+                                   pw_, st, sh, sw, dt, _ACTS[act], stream)
+    if st_ != 0:
+        raise LibconvError(st_, "conv3d_forward_cpack")
+    return out
 
 
 _copy_streams = {}

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libconv.so")
-SOURCES = ["api.cpp", "direct.hip", "igemm.hip"]
+SOURCES = ["api.cpp", "direct.hip", "igemm.hip", "layout.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -81,11 +81,16 @@ libconv_status validate(Problem& p, int algo, bool with_pointers) {
   p.OH = (int)oh;
   p.OW = (int)ow;
   if (p.pool && (p.T != 1 || p.KT != 1 || oh < 2 || ow < 2)) return LIBCONV_ERR_BAD_SHAPE;
+  if (p.cpack && p.pool) return LIBCONV_ERR_UNSUPPORTED;
   const long long eb = dtype_bytes(p.dtype);
-  const long long xb = product({p.N, p.C, p.T, p.H, p.W, eb});
+  // channel-packed tensors hold whole 16-byte groups of channels
+  const long long se = 16 / eb;
+  const long long cx = p.cpack ? (p.C + se - 1) / se * se : p.C;
+  const long long cy = p.cpack ? (p.K + se - 1) / se * se : p.K;
+  const long long xb = product({p.N, cx, p.T, p.H, p.W, eb});
   const long long wb = product({p.K, p.C, p.KT, p.KH, p.KW, eb});
   const long long yb = p.pool ? product({p.N, p.K, oh / 2, ow / 2, eb})
-                              : product({p.N, p.K, ot, oh, ow, eb});
+                              : product({p.N, cy, ot, oh, ow, eb});
   if (xb > kMaxBytes || wb > kMaxBytes || yb > kMaxBytes) return LIBCONV_ERR_TOO_LARGE;
   const long long pb = packed_weight_bytes(p.C, p.K, p.KT, p.KH, p.KW, p.dtype);
   if (pb > kMaxBytes) return LIBCONV_ERR_TOO_LARGE;
@@ -213,16 +218,16 @@ libconv_status plan_for(const Problem& p, int algo, Plan* plan, bool packed_only
 // capture state, which weight forms exist, 16-byte alignment of x, compute
 // units, fused pooling).  Not used while a LIBCONV_FORCE_* override is set.
 struct PlanKey {
-  int v[25];
+  int v[27];
   bool operator==(const PlanKey& o) const { return std::memcmp(v, o.v, sizeof(v)) == 0; }
 };
 
 PlanKey plan_key(const Problem& p, int algo) {
   PlanKey k;
-  const int v[25] = {p.N, p.C, p.T, p.H, p.W, p.K, p.KT, p.KH, p.KW, p.pt, p.ph, p.pw, p.st, p.sh,
+  const int v[27] = {p.N, p.C, p.T, p.H, p.W, p.K, p.KT, p.KH, p.KW, p.pt, p.ph, p.pw, p.st, p.sh,
                      p.sw, p.dtype, p.act, algo, (int)p.no_temps, p.w == nullptr,
                      (int)(reinterpret_cast<uintptr_t>(p.x) & 15), p.cus, p.wp != nullptr, p.ptb,
-                     (int)p.pool};
+                     (int)p.pool, (int)p.cpack, (int)(reinterpret_cast<uintptr_t>(p.y) & 15)};
   std::memcpy(k.v, v, sizeof(v));
   return k;
 }
@@ -394,6 +399,28 @@ libconv_status chunk_plan(int N, int C_in, int T, int H, int W, int C_out, int K
   return LIBCONV_OK;
 }
 
+libconv_status layout_call(const void* src, void* dst, int N, int C, int T, int H, int W,
+                           int dtype, bool to_packed, void* stream) {
+  if (dtype != LIBCONV_F32 && dtype != LIBCONV_F16 && dtype != LIBCONV_BF16)
+    return LIBCONV_ERR_BAD_DTYPE;
+  if (N < 0 || C < 1 || T < 1 || H < 1 || W < 1) return LIBCONV_ERR_BAD_SHAPE;
+  const long long spatial = (long long)T * H * W;
+  const long long plain = product({N, C, spatial, dtype_bytes(dtype)});
+  const long long packed = cpack_bytes(N, C, spatial, dtype);
+  if (plain > kMaxBytes || packed > kMaxBytes) return LIBCONV_ERR_TOO_LARGE;
+  if (!src || !dst) return LIBCONV_ERR_NULL_POINTER;
+  if (overlaps(src, to_packed ? plain : packed, dst, to_packed ? packed : plain))
+    return LIBCONV_ERR_ALIAS;
+  if (N == 0) return LIBCONV_OK;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || !device_ok(dev)) {
+    (void)hipGetLastError();
+    return LIBCONV_ERR_NO_DEVICE;
+  }
+  return layout_launch(src, dst, N, C, spatial, dtype, to_packed,
+                       reinterpret_cast<hipStream_t>(stream));
+}
+
 }  // namespace
 
 libconv_status stream_alloc(size_t bytes, hipStream_t stream, void** out) {
@@ -511,6 +538,42 @@ libconv_status conv3d_forward_tpad(const void* x, const void* w, const void* pac
     return run(p, LIBCONV_ALGO_IGEMM);
   }
   return run(p, LIBCONV_ALGO_AUTO);
+}
+
+libconv_status conv3d_forward_cpack(const void* x, const void* w, const void* packed_w,
+                                    const void* bias, void* y, int N, int C_in, int T, int H,
+                                    int W, int C_out, int KT, int KH, int KW, int pad_t_front,
+                                    int pad_t_back, int pad_h, int pad_w, int stride_t,
+                                    int stride_h, int stride_w, int dtype, int act,
+                                    void* stream) {
+  if ((w == nullptr) == (packed_w == nullptr)) return LIBCONV_ERR_NULL_POINTER;
+  Problem p = make_problem(x, w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW, pad_t_front,
+                           pad_h, pad_w, stride_t, stride_h, stride_w, dtype, act, stream);
+  p.ptb = pad_t_back;
+  p.cpack = true;
+  if (packed_w) {
+    p.wp = packed_w;
+    p.no_temps = true;  // as libconv_forward_packed: never allocates
+    return run(p, LIBCONV_ALGO_IGEMM);
+  }
+  return run(p, LIBCONV_ALGO_AUTO);
+}
+
+long long libconv_cpack_bytes(int N, int C, int T, int H, int W, int dtype) {
+  if (dtype != LIBCONV_F32 && dtype != LIBCONV_F16 && dtype != LIBCONV_BF16) return -1;
+  if (N < 0 || C < 1 || T < 1 || H < 1 || W < 1) return -1;
+  const long long b = cpack_bytes(N, C, (long long)T * H * W, dtype);
+  return b > kMaxBytes ? -1 : b;
+}
+
+libconv_status libconv_pack_activations(const void* x, void* x_packed, int N, int C, int T, int H,
+                                        int W, int dtype, void* stream) {
+  return layout_call(x, x_packed, N, C, T, H, W, dtype, true, stream);
+}
+
+libconv_status libconv_unpack_activations(const void* x_packed, void* x, int N, int C, int T,
+                                          int H, int W, int dtype, void* stream) {
+  return layout_call(x_packed, x, N, C, T, H, W, dtype, false, stream);
 }
 
 libconv_status libconv_frame_window(int T, int KT, int pad_t_front, int pad_t_back, int stride_t,
@@ -725,10 +788,11 @@ libconv_status libconv_query_plan(int N, int C_in, int T, int H, int W, int C_ou
   if (!algo_out || !tile_out || !grid_out || !ksplit_out) return LIBCONV_ERR_NULL_POINTER;
   Problem p = make_problem(nullptr, nullptr, nullptr, nullptr, N, C_in, T, H, W, C_out, KT, KH, KW,
                            pad_t, pad_h, pad_w, stride_t, stride_h, stride_w, dtype, act, nullptr);
-  libconv_status st = validate(p, algo, false);
-  if (st != LIBCONV_OK) return st;
   p.no_temps = (capturing & LIBCONV_PLAN_CAPTURING) != 0;
   p.pool = (capturing & LIBCONV_PLAN_POOL2) != 0;
+  p.cpack = (capturing & LIBCONV_PLAN_CPACK) != 0;
+  libconv_status st = validate(p, algo, false);
+  if (st != LIBCONV_OK) return st;
   Plan plan;
   st = plan_for(p, algo, &plan);
   if (st != LIBCONV_OK) return st;

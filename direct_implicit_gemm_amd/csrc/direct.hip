@@ -48,11 +48,26 @@ struct DirectArgs {
   int OT, OH, OW;
   int relu;
   int col_tiles, row_tiles;
+  int cpack;     // 1: x and y channel-packed ([N][C/g][T][H][W][g], g = 16 bytes of channels)
   int cc;        // input channels per LDS stage
   int hr, hc;    // halo rows / columns
   int ws_off;    // float offset of the weight area (multiple of 4: 16-byte aligned)
   uint32_t x_bytes, w_bytes, b_bytes, y_bytes;
 };
+
+// Byte offset of element (n, c, t, h, w) of an activation tensor with C
+// channels: plain [N][C][T][H][W], or channel-packed
+// [N][ceil(C/g)][T][H][W][g] with g = 16 / EB.
+template <int EB>
+__device__ __forceinline__ int act_offset(int cpack, int n, int C, int c, int T, int t, int H,
+                                          int h, int W, int w) {
+  if (cpack) {
+    constexpr int g = 16 / EB;
+    const int cg = (C + g - 1) / g;
+    return (((((n * cg + c / g) * T + t) * H + h) * W + w) * g + c % g) * EB;
+  }
+  return ((((n * C + c) * T + t) * H + h) * W + w) * EB;
+}
 
 template <int DT, int COT, int P>
 __global__ __launch_bounds__(kThreads) void direct_kernel(DirectArgs a) {
@@ -113,7 +128,7 @@ __global__ __launch_bounds__(kThreads) void direct_kernel(DirectArgs a) {
             const int ih = ih0 + r, iw = iw0 + col;
             const bool live = q0 + u < items && col < a.hc;
             const bool ok = live && (unsigned)ih < (unsigned)a.H && (unsigned)iw < (unsigned)a.W;
-            const int off = ((((n * a.C + ci0 + c) * a.T + it) * a.H + ih) * a.W + iw) * eb;
+            const int off = act_offset<eb>(a.cpack, n, a.C, ci0 + c, a.T, it, a.H, ih, a.W, iw);
             v[u] = E::load(xr, guard_offset(ok, off));
             dst[u] = live ? (c * a.hr + r) * a.hc + col : -1;
             if (++m == nseg) {  // next row of this wave: 4 halo rows further
@@ -190,14 +205,18 @@ __global__ __launch_bounds__(kThreads) void direct_kernel(DirectArgs a) {
 #pragma unroll
   for (int j = 0; j < COT; ++j)
     bias[j] = E::load(br, guard_offset(a.b && co0 + j < a.K, (co0 + j) * eb));
+  // channel-packed output: the channels past C_out in the last group are
+  // written too (as 0: their weights and bias read 0)
+  const int k_store = a.cpack ? (a.K + 16 / eb - 1) / (16 / eb) * (16 / eb) : a.K;
 #pragma unroll
   for (int j = 0; j < COT; ++j) {
     const int co = co0 + j;
-    const int row = (((n * a.K + co) * a.OT + ot) * a.OH + oh) * a.OW;
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       const int ow = ow0 + p * 64 + lane;
-      if (co < a.K && ow < a.OW) E::store(epilogue(acc[j][p], bias[j], a.relu), yr, (row + ow) * eb);
+      if (co < k_store && ow < a.OW)
+        E::store(epilogue(acc[j][p], bias[j], a.relu), yr,
+                 act_offset<eb>(a.cpack, n, a.K, co, a.OT, ot, a.OH, oh, a.OW, ow));
     }
   }
 }
@@ -544,6 +563,7 @@ long tap_floats_per_channel(const TapTile& t, int dtype) {
 }
 
 bool tap_fits(const TapTile& t, const Problem& p) {
+  if (p.cpack) return false;  // plain layout only
   if (p.KT != 1 || p.st != 1 || p.pt != 0 || p.ptb != 0) return false;
   if (p.KH != t.KH || p.KW != t.KW || p.sh != t.SH || p.sw != t.SW) return false;
   if (t.vx) {
@@ -676,11 +696,14 @@ libconv_status direct_launch(const Problem& p, const Plan& plan) {
   a.col_tiles = (p.OW + 64 * t->p - 1) / (64 * t->p);
   a.row_tiles = (p.OH + kRows - 1) / kRows;
   a.cc = g.cc; a.hr = g.hr; a.hc = g.hc; a.ws_off = g.ws_off;
+  a.cpack = p.cpack ? 1 : 0;
   const int eb = dtype_bytes(p.dtype);
-  a.x_bytes = (uint32_t)((long long)p.N * p.C * p.T * p.H * p.W * eb);
+  a.x_bytes = (uint32_t)(p.cpack ? cpack_bytes(p.N, p.C, (long long)p.T * p.H * p.W, p.dtype)
+                                 : (long long)p.N * p.C * p.T * p.H * p.W * eb);
   a.w_bytes = (uint32_t)((long long)p.K * p.C * p.KT * p.KH * p.KW * eb);
   a.b_bytes = p.b ? (uint32_t)(p.K * eb) : 0u;
-  a.y_bytes = (uint32_t)((long long)p.N * p.K * p.OT * p.OH * p.OW * eb);
+  a.y_bytes = (uint32_t)(p.cpack ? cpack_bytes(p.N, p.K, (long long)p.OT * p.OH * p.OW, p.dtype)
+                                 : (long long)p.N * p.K * p.OT * p.OH * p.OW * eb);
   const long long spatial_tiles = (long long)p.N * p.OT * a.row_tiles * a.col_tiles;
   const int co_tiles = (p.K + t->cot - 1) / t->cot;
   if (spatial_tiles > 0x7fffffffLL || co_tiles > 65535) return LIBCONV_ERR_UNSUPPORTED;

@@ -136,7 +136,12 @@ struct Cfg {
   // of the layer in one stage; one LDS buffer, no overlap machinery)
   static constexpr bool PK = (PK_ & 1) != 0;
   static constexpr bool ONE = (PK_ & 2) != 0;
-  static constexpr bool VX = VX_ != 0;
+  static constexpr bool VX = VX_ == 1;
+  // VX_ == 2: channel-packed activations, x [N][C/SE][T][H][W][SE] and y
+  // likewise over C_out.  A halo row of one channel group is then a run of
+  // 16-byte words in memory, copied straight into LDS (no registers, no
+  // repacking), and the accumulators leave as 16-byte channel groups.
+  static constexpr bool XP = VX_ == 2;
   static constexpr int EB = Elem<DT>::bytes;
   static constexpr int SE = Mma<DT>::SE;
   static constexpr int CK = CG * SE;
@@ -162,7 +167,11 @@ struct Cfg {
   static constexpr int NROWS = CG * HR;            // halo rows of a stage (all groups)
   static constexpr int XPLANE = HR * PITCH;        // LDS words per channel group
   static constexpr int WBYTES = NSLOT * BM * 16;
-  static constexpr int XBYTES = CG * XPLANE * 16;
+  // channel-packed input: CG x HR x HC words per stage, 64 per wave-wide
+  // direct-to-LDS copy (the buffer is rounded up to whole copies)
+  static constexpr int XDMA = XP ? (CG * HR * HC + 63) / 64 : 0;
+  static constexpr int NXDMA = (XDMA + 3) / 4;     // copies per wave
+  static constexpr int XBYTES = XP ? XDMA * 1024 : CG * XPLANE * 16;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int FA = WTM / 32, FB = WTN / 32;
   static constexpr int BPR = TW / 32;              // 32-pixel blocks per tile row
@@ -176,7 +185,8 @@ struct Cfg {
   // into a 1 KB scratch area at the end of LDS
   static constexpr int WCHUNKS = NSLOT * BM / 64;
   static constexpr int NDMA = (WCHUNKS + 3) / 4;
-  static constexpr int DMA_PAD = (PK && WCHUNKS % 4 != 0) ? 1024 : 0;
+  static constexpr int DMA_PAD =
+      ((PK && WCHUNKS % 4 != 0) || (XP && XDMA % 4 != 0)) ? 1024 : 0;
   // LDS: two weight and two input buffers (one of each for single-stage tiles)
   static constexpr int NBUF = ONE ? 1 : 2;
   // the vectorised epilogue reuses LDS as four wave-private 32x32 tiles
@@ -192,7 +202,8 @@ struct Cfg {
   // input staging: one unit = one run (VX) or one halo pixel of one channel
   // group; VX units come in blocks of 8 rows x NRUN runs
   static constexpr int XUNITS = VX ? (NROWS + 7) / 8 * 8 * NRUN : CG * HR * HC;
-  static constexpr int XPASS = (XUNITS + kThreads - 1) / kThreads;
+  static constexpr int XPASS = XP ? 0 : (XUNITS + kThreads - 1) / kThreads;
+  static constexpr int XPASS1 = XPASS > 0 ? XPASS : 1;  // array extent
   // global reads into registers each wave issues per stage
   static constexpr int REG_LOADS = XPASS * SE + WPASS * TS;
   // slot pair before whose MFMAs the next stage's registers are written to
@@ -206,6 +217,7 @@ struct Cfg {
   static_assert(BM % 64 == 0 || !PK, "packed tiles move whole 64-channel chunks");
   static_assert(BM <= kPackAlign, "packed channel padding covers one tile");
   static_assert(PK || KT == 1, "weights from OIHW: 2-D tiles only");
+  static_assert(!XP || (PK && !ONE), "channel-packed tiles read packed weights, two stages");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -218,8 +230,8 @@ template <class G>
 struct StageRegs {
   using XE = typename Elem<G::DT>::raw_t;
   u32x4_t wv[G::WPASS > 0 ? G::WPASS : 1][G::TS];
-  XE xe[G::VX ? 1 : G::XPASS][G::VX ? 1 : G::SE];       // one element per read
-  u32x4_t xr[G::VX ? G::XPASS : 1][G::VX ? G::SE : 1];  // one run per read
+  XE xe[G::VX ? 1 : G::XPASS1][G::VX ? 1 : G::SE];       // one element per read
+  u32x4_t xr[G::VX ? G::XPASS1 : 1][G::VX ? G::SE : 1];  // one run per read
 };
 
 // Make a register's value opaque to the optimiser at this point.  Applied to
@@ -399,9 +411,9 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
   // multiple of RUN a run lies wholly inside or wholly outside the row.
   // Otherwise: unit u = (g * HR + hr) * HC + hc, one offset per channel.
   const int shift = G::VX ? (iw0 & (G::RUN - 1)) : 0;
-  int xoff[G::VX ? 1 : G::XPASS][G::VX ? 1 : SE];  // kFar when the position is padding
-  int xv[G::VX ? G::XPASS : 1];
-  int xgrp[G::XPASS];
+  int xoff[G::VX ? 1 : G::XPASS1][G::VX ? 1 : SE];  // kFar when the position is padding
+  int xv[G::VX ? G::XPASS1 : 1];
+  int xgrp[G::XPASS1];
 #pragma unroll
   for (int i = 0; i < G::XPASS; ++i) {
     const int u = tid + i * kThreads;
@@ -429,6 +441,25 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
     }
   }
   const int ch_bytes = plane * EB;       // scalar offset between channels
+  // Channel-packed input: copy k of this wave is words (wave + 4k) * 64 +
+  // lane of the stage's halo, word f = (g * HR + hr) * HC + hc, i.e. the
+  // 16-byte channel group g of halo pixel (hr, hc); one offset per copy,
+  // relative to the stage's first channel group at the stage's frame.
+  const int cgs = (a.C + SE - 1) / SE;    // channel groups of x
+  int xdo[G::XP ? G::NXDMA : 1];
+  int xdg[G::XP ? G::NXDMA : 1];
+  if constexpr (G::XP) {
+#pragma unroll
+    for (int k = 0; k < G::NXDMA; ++k) {
+      const int f = (wave + 4 * k) * 64 + lane;
+      const int g = f / (G::HR * G::HC);
+      const int hr = (f / G::HC) % G::HR, hc = f % G::HC;
+      const int ih = ih0 + hr, iw = iw0 + hc;
+      const bool ok = f < G::XUNITS && (unsigned)ih < (unsigned)a.H && (unsigned)iw < (unsigned)a.W;
+      xdo[k] = guard_offset(true, ok ? (g * a.T * hw + ih * a.W + iw) * 16 : kFar);
+      xdg[k] = g;
+    }
+  }
   // OIHW weight unit u = g * BM + col
   int woff[G::WPASS > 0 ? G::WPASS : 1];
   int wgrp[G::WPASS > 0 ? G::WPASS : 1];
@@ -473,7 +504,8 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
   auto x_src = [&](int chunk, int kt) -> Src {
     Src q;
     q.ci0 = chunk * G::CK;
-    const int sb = n_base + (q.ci0 * plane + (it0 + kt) * hw) * EB;
+    const int sb = G::XP ? (((n * cgs + chunk * G::CG) * a.T + it0 + kt) * hw) * 16
+                         : n_base + (q.ci0 * plane + (it0 + kt) * hw) * EB;
     q.rs = make_rsrc((const char*)a.x + sb, a.x_bytes - sb);
     q.wrun = 0;
     return q;
@@ -514,6 +546,20 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
       if constexpr (rg) v = guard_offset(q.ci0 + xgrp[i] * SE + j < a.C, v);
       r.xe[i][j] = E::load_raw(q.rs, v);
     }
+  };
+
+  // Channel-packed input: copy k of this wave straight into the halo buffer
+  // `xdst` (copies past the halo land in the scratch area and read nothing);
+  // in a ragged last chunk the groups past the input's read zero.
+  auto read_xd = [&](auto ragged, auto kc, const Src& q, unsigned char* xdst)
+      __attribute__((always_inline)) {
+    constexpr int k = decltype(kc)::value;
+    const int ins = wave + 4 * k;
+    int off = xdo[k];
+    if constexpr (decltype(ragged)::value)
+      off = guard_offset(true, q.ci0 / SE + xdg[k] < cgs ? off : kFar);
+    unsigned char* dst = ins < G::XDMA ? xdst + ins * 1024 : lds + G::LDS - 1024;
+    copy16_to_lds(q.rs, dst, off);
   };
 
   // Registers of a stage -> LDS (weights into `wdst` unless they were copied
@@ -763,11 +809,58 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
     if (s < nstages) step(s, ra, rb);
     wait_vmcnt<0>();  // no copy into LDS may outlive the workgroup
   };
+  // Channel-packed input: weights and input of stage s+1 are both copied
+  // straight into the free LDS buffers while stage s is multiplied (spread
+  // over its slot pairs); a step ends when the copies have landed and every
+  // wave is done with stage s.  The free buffers held stage s-1, whose reads
+  // finished before the barrier that ended stage s-1.
+  auto main_loop_dma = [&](auto ragged) __attribute__((always_inline)) {
+    StageRegs<G> unused;  // packed weights go straight to LDS
+    Cursor c{chunk0, kt_lo, 0};
+    {
+      const Src qw = w_src(c.chunk, c.kt), qx = x_src(c.chunk, c.kt);
+      static_for<0, NWP>([&](auto kc) { read_w(ragged, kc, qw, unused, wbuf(0)); });
+      static_for<0, G::NXDMA>([&](auto kc) { read_xd(ragged, kc, qx, xbuf(0)); });
+      advance(c);
+    }
+    wait_vmcnt<0>();
+    lds_barrier();
+    constexpr int NP = NWP + G::NXDMA;
+    for (int s = 0; s < nstages; ++s) {
+      const bool more = s + 1 < nstages;
+      const Src qw = w_src(c.chunk, c.kt), qx = x_src(c.chunk, c.kt);
+      unsigned char* wdst = wbuf((s + 1) & 1);
+      unsigned char* xdst = xbuf((s + 1) & 1);
+      compute(wbuf(s & 1), xbuf(s & 1), [&](auto pc) {
+        constexpr int p = decltype(pc)::value;
+        constexpr int lo = p * NP / G::NPAIR, hi = (p + 1) * NP / G::NPAIR;
+        if (more) {
+          static_for<lo, hi>([&](auto kc) {
+            constexpr int k = decltype(kc)::value;
+            if constexpr (k < NWP)
+              read_w(ragged, kc, qw, unused, wdst);
+            else
+              read_xd(ragged, std::integral_constant<int, k - NWP>{}, qx, xdst);
+          });
+        }
+      });
+      advance(c);
+      wait_vmcnt<0>();
+      lds_barrier();
+    }
+  };
   if (nstages > 0) {
-    if (a.C % G::CK == 0)
-      main_loop(std::false_type{});
-    else
-      main_loop(std::true_type{});
+    if constexpr (G::XP) {
+      if (cgs % G::CG == 0)
+        main_loop_dma(std::false_type{});
+      else
+        main_loop_dma(std::true_type{});
+    } else {
+      if (a.C % G::CK == 0)
+        main_loop(std::false_type{});
+      else
+        main_loop(std::true_type{});
+    }
   }
 
   // ---- epilogue
@@ -793,6 +886,50 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
   }
   const __amdgpu_buffer_rsrc_t yr = make_rsrc(a.y, a.y_bytes);
   const __amdgpu_buffer_rsrc_t br = make_rsrc(a.b, a.b_bytes);
+  if constexpr (G::XP) {
+    // Channel-packed output: accumulator elements 4q .. 4q+3 of a lane are
+    // 4 consecutive output channels of one pixel (rows 8q + 4hf .. +3 of the
+    // 32x32 block), i.e. half a 16-byte group (16-bit) or a whole one (fp32):
+    // one store each, the 32 pixels of a half-wave side by side.  Channels
+    // past C_out in the last group are written as 0 (their packed weights
+    // and bias read 0).
+    const int kgs = (a.K + SE - 1) / SE;
+#pragma unroll
+    for (int i = 0; i < G::FA; ++i) {
+      float bias[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int co = co0 + co_w0 + i * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+        bias[r] = E::load(br, guard_offset(a.b && co < a.K, co * EB));
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int cob = co0 + co_w0 + i * 32 + 8 * q + 4 * hf;
+        const int grp = cob / SE, sub = cob % SE;
+#pragma unroll
+        for (int j = 0; j < G::FB; ++j) {
+          const int b = blk0 + j;
+          const int oh = oh0 + b / G::BPR;
+          const int ow = ow0 + (b % G::BPR) * 32 + il;
+          const bool ok = grp < kgs && oh < a.OH && ow < a.OW;
+          const int off = ((((n * kgs + grp) * a.OT + ot) * a.OH + oh) * a.OW + ow) * 16 + sub * EB;
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = epilogue(acc[i][j][4 * q + e], bias[4 * q + e], a.relu);
+          if constexpr (EB == 4) {
+            const u32x4_t word{__builtin_bit_cast(uint32_t, v[0]), __builtin_bit_cast(uint32_t, v[1]),
+                               __builtin_bit_cast(uint32_t, v[2]), __builtin_bit_cast(uint32_t, v[3])};
+            __builtin_amdgcn_raw_buffer_store_b128(word, yr, guard_offset(ok, off), 0, 0);
+          } else {
+            const u32x2_t word{(uint32_t)E::from_f32(v[0]) | ((uint32_t)E::from_f32(v[1]) << 16),
+                               (uint32_t)E::from_f32(v[2]) | ((uint32_t)E::from_f32(v[3]) << 16)};
+            __builtin_amdgcn_raw_buffer_store_b64(word, yr, guard_offset(ok, off), 0, 0);
+          }
+        }
+      }
+    }
+    return;
+  }
   if constexpr (G::POOLABLE) {
     if (a.pool) {
       // Fused 2x2 stride-2 max pooling: blocks j and j+1 of the wave are output
@@ -1023,7 +1160,10 @@ struct ReduceArgs {
   const void* b;
   void* y;
   int S, K, plane, relu;
-  long long n_out;  // N * K * plane
+  // output channels written: K, or for channel-packed y (the _cpack kernel)
+  // K rounded up to whole groups (the channels past K are written as 0)
+  int K_out;
+  long long n_out;  // N * K_out * plane
   uint32_t part_bytes, b_bytes, y_bytes;
 };
 
@@ -1052,6 +1192,48 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(ReduceArgs a) {
   }
 #pragma unroll
   for (int m = 0; m < V; ++m) E::store(epilogue(v[m], bias, a.relu), yr, (int)((e0 + m) * E::bytes));
+}
+
+// The same sum for channel-packed y: one thread per output channel group of
+// one pixel, u = (n, group, s); lanes walk s, so each channel's partial sums
+// are read as contiguous runs across the wave and the 16-byte groups are
+// written contiguously.  Channels past K read nothing and are written as 0.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void splitk_reduce_cpack_kernel(ReduceArgs a) {
+  using E = Elem<DT>;
+  constexpr int SE = 16 / E::bytes;
+  const long long u = (long long)blockIdx.x * kThreads + threadIdx.x;
+  const int groups = a.K_out / SE;
+  if (u >= (long long)a.n_out / SE) return;
+  const int s = (int)(u % a.plane);
+  const long long ng = u / a.plane;
+  const int g = (int)(ng % groups);
+  const long long n = ng / groups;
+  const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.part, a.part_bytes);
+  const __amdgpu_buffer_rsrc_t br = make_rsrc(a.b, a.b_bytes);
+  const __amdgpu_buffer_rsrc_t yr = make_rsrc(a.y, a.y_bytes);
+  const long long part_elems = (long long)a.part_bytes / 4 / a.S;
+  float v[SE];
+#pragma unroll
+  for (int j = 0; j < SE; ++j) {
+    const int co = g * SE + j;
+    const bool real = co < a.K;
+    float acc = 0.0f;
+    for (int sp = 0; sp < a.S; ++sp) {
+      const long long e = sp * part_elems + (n * a.K + co) * a.plane + s;
+      acc += Elem<DT_F32>::load(pr, guard_offset(real, (int)(e * 4)));
+    }
+    v[j] = epilogue(acc, E::load(br, guard_offset(a.b != nullptr && real, co * E::bytes)), a.relu);
+  }
+  u32x4_t w;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    if constexpr (SE == 4)
+      w[m] = __builtin_bit_cast(uint32_t, v[m]);
+    else
+      w[m] = (uint32_t)E::from_f32(v[2 * m]) | ((uint32_t)E::from_f32(v[2 * m + 1]) << 16);
+  }
+  __builtin_amdgcn_raw_buffer_store_b128(w, yr, (int)(u * 16), 0, 0);
 }
 
 // ------------------------------------------------------------------ tiles
@@ -1084,7 +1266,8 @@ struct TileDesc {
   int flat;       // 1: 1x1 stride-1 pad-0 layer viewed as one long row per plane
   int BM, TH, TW, CG;
   int packed;     // 1: reads packed weights
-  int vx;         // 1: reads the input as aligned 16-byte runs (W a multiple of the run)
+  int vx;         // 1: reads the input as aligned 16-byte runs (W a multiple of the run);
+                  // 2: channel-packed activations (input copied straight to LDS)
   int eff;        // fraction of MFMA peak one CU reaches on this tile, in percent
                   // (measured on MI355X on large grids; used to rank tiles)
   int occ;        // workgroups one CU holds at once (registers and LDS of the
@@ -1178,6 +1361,17 @@ const TileDesc kTiles[] = {
     LIBCONV_TILE(272, 1, 1, 3, 3, 1, 1, 0, 128, 4, 32, 2, 2, 2, 1, 1, 23, 1, "igemm16p_k3s1_m128_n4x32"),
     LIBCONV_TILE(275, 1, 1, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 1, 0, 24, 2, "igemm16p_k3s1_m64_n8x32_e"),
     LIBCONV_TILE(276, 1, 1, 3, 3, 1, 1, 0, 128, 8, 32, 1, 4, 2, 1, 1, 34, 1, "igemm16p_k3s1_m128w_n8x32"),
+    // channel-packed activations (packed weights; input halo copied straight
+    // to LDS, output stored as channel groups)
+    LIBCONV_TILE(280, 1, 3, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 1, 2, 33, 2, "igemm16x_k333s1_m64_n8x32"),
+    LIBCONV_TILE(281, 1, 3, 3, 3, 1, 1, 0, 128, 8, 32, 1, 4, 2, 1, 2, 31, 1, "igemm16x_k333s1_m128w_n8x32"),
+    LIBCONV_TILE(282, 1, 1, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 1, 2, 36, 2, "igemm16x_k3s1_m64_n8x32"),
+    LIBCONV_TILE(283, 1, 1, 3, 3, 1, 1, 0, 128, 8, 32, 1, 4, 2, 1, 2, 34, 1, "igemm16x_k3s1_m128w_n8x32"),
+    LIBCONV_TILE(284, 1, 1, 3, 3, 2, 2, 0, 64, 4, 32, 2, 2, 2, 1, 2, 20, 2, "igemm16x_k3s2_m64_n4x32"),
+    LIBCONV_TILE(285, 1, 1, 1, 1, 1, 1, 1, 128, 1, 128, 2, 2, 8, 1, 2, 20, 2, "igemm16x_k1_m128_n128"),
+    LIBCONV_TILE(290, 0, 1, 3, 3, 1, 1, 0, 64, 8, 32, 1, 4, 2, 1, 2, 50, 2, "igemm32x_k3s1_m64_n8x32"),
+    LIBCONV_TILE(291, 0, 1, 3, 3, 2, 2, 0, 64, 4, 32, 2, 2, 2, 1, 2, 50, 2, "igemm32x_k3s2_m64_n4x32"),
+    LIBCONV_TILE(292, 0, 1, 1, 1, 1, 1, 1, 64, 1, 128, 2, 2, 8, 1, 2, 15, 3, "igemm32x_k1_m64_n128"),
 };
 
 #undef LIBCONV_TILE
@@ -1200,9 +1394,14 @@ bool tile_fits(const TileDesc& t, const Problem& p) {
   // 16-byte weight vectors read from OIHW must not straddle channels; packed
   // weights are zero-padded to whole groups instead.
   if (!t.packed && p.C % se != 0) return false;
+  // channel-packed activations only on the tiles made for them; their
+  // copies and stores move 16-byte channel groups
+  if ((t.vx == 2) != p.cpack) return false;
+  if (t.vx == 2 && ((reinterpret_cast<uintptr_t>(p.x) | reinterpret_cast<uintptr_t>(p.y)) & 15))
+    return false;
   // 16-byte runs (8 pixels of a 16-bit type, 4 of fp32): rows (flattened
   // planes for 1x1 tiles) of whole runs, and an input aligned for 16-byte reads
-  if (t.vx) {
+  if (t.vx == 1) {
     const long long row = t.flat ? (long long)p.H * p.W : p.W;
     if (row % (16 / dtype_bytes(p.dtype)) != 0 || (reinterpret_cast<uintptr_t>(p.x) & 15) != 0)
       return false;
@@ -1419,6 +1618,11 @@ hipError_t launch_reduce(const ReduceArgs& a, unsigned grid, hipStream_t s) {
   hipLaunchKernelGGL((splitk_reduce_kernel<DT, V>), dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
+template <int DT>
+hipError_t launch_reduce_cpack(const ReduceArgs& a, unsigned grid, hipStream_t s) {
+  hipLaunchKernelGGL((splitk_reduce_cpack_kernel<DT>), dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
 
 libconv_status igemm_launch(const Problem& p, const Plan& plan) {
   const TileDesc* t = find_tile(plan.tile);
@@ -1452,11 +1656,13 @@ libconv_status igemm_launch(const Problem& p, const Plan& plan) {
   const long long w_tile = (long long)t->BM * std::min(p.C, a.cps * t->CG * (t->wide ? 8 : 4)) *
                            p.KT * p.KH * p.KW * eb;
   a.co_group = (int)std::max(1LL, std::min<long long>(c.co, (2LL << 20) / std::max(1LL, w_tile)));
-  a.x_bytes = (uint32_t)((long long)p.N * p.C * p.T * p.H * p.W * eb);
+  a.x_bytes = (uint32_t)(p.cpack ? cpack_bytes(p.N, p.C, (long long)p.T * p.H * p.W, p.dtype)
+                                 : (long long)p.N * p.C * p.T * p.H * p.W * eb);
   a.w_bytes = t->packed ? (uint32_t)packed_weight_bytes(p.C, p.K, p.KT, p.KH, p.KW, p.dtype)
                         : (uint32_t)((long long)p.K * p.C * p.KT * p.KH * p.KW * eb);
   a.b_bytes = p.b ? (uint32_t)(p.K * eb) : 0u;
-  a.y_bytes = (uint32_t)((long long)p.N * p.K * p.OT * p.OH * p.OW * eb);
+  a.y_bytes = (uint32_t)(p.cpack ? cpack_bytes(p.N, p.K, (long long)p.OT * p.OH * p.OW, p.dtype)
+                                 : (long long)p.N * p.K * p.OT * p.OH * p.OW * eb);
   a.part = nullptr;
   a.part_bytes = 0;
   a.vec_out = (a.OW % (16 / eb)) == 0 && (reinterpret_cast<uintptr_t>(p.y) & 15) == 0;
@@ -1487,16 +1693,27 @@ libconv_status igemm_launch(const Problem& p, const Plan& plan) {
     ReduceArgs r;
     r.part = a.part; r.b = p.b; r.y = p.y;
     r.S = ks; r.K = p.K; r.plane = p.OT * p.OH * p.OW; r.relu = a.relu;
-    r.n_out = out_elems(p);
+    const int se = 16 / eb;
+    r.K_out = p.cpack ? (p.K + se - 1) / se * se : p.K;
+    r.n_out = (long long)p.N * r.K_out * r.plane;
     r.part_bytes = a.part_bytes; r.b_bytes = a.b_bytes; r.y_bytes = a.y_bytes;
     const bool v4 = r.plane % 4 == 0;
-    const int V = v4 ? 4 : 1;
+    const int V = p.cpack ? se : v4 ? 4 : 1;
     const unsigned grid = (unsigned)((r.n_out / V + kThreads - 1) / kThreads);
     ReduceFn rf = nullptr;
     switch (p.dtype) {
-      case LIBCONV_F32: rf = v4 ? &launch_reduce<DT_F32, 4> : &launch_reduce<DT_F32, 1>; break;
-      case LIBCONV_F16: rf = v4 ? &launch_reduce<DT_F16, 4> : &launch_reduce<DT_F16, 1>; break;
-      default: rf = v4 ? &launch_reduce<DT_BF16, 4> : &launch_reduce<DT_BF16, 1>; break;
+      case LIBCONV_F32:
+        rf = p.cpack ? &launch_reduce_cpack<DT_F32>
+                     : v4 ? &launch_reduce<DT_F32, 4> : &launch_reduce<DT_F32, 1>;
+        break;
+      case LIBCONV_F16:
+        rf = p.cpack ? &launch_reduce_cpack<DT_F16>
+                     : v4 ? &launch_reduce<DT_F16, 4> : &launch_reduce<DT_F16, 1>;
+        break;
+      default:
+        rf = p.cpack ? &launch_reduce_cpack<DT_BF16>
+                     : v4 ? &launch_reduce<DT_BF16, 4> : &launch_reduce<DT_BF16, 1>;
+        break;
     }
     if (rf(r, grid, p.stream) != hipSuccess) st = LIBCONV_ERR_LAUNCH;
   }

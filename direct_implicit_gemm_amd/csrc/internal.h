@@ -31,6 +31,9 @@ struct Problem {
   int cus;         // compute units of the current device (filled before a launch)
   bool no_temps;   // plan without stream-ordered temporaries (the stream is capturing)
   bool pool;       // y is the 2x2 stride-2 max pool of the activated conv output (2-D only)
+  // x and y are channel-packed: [N][ceil(C/g)][T][H][W][g] (g channels = 16
+  // bytes, zero past C) and likewise y over C_out; else plain NC(T)HW
+  bool cpack;
 };
 
 // What the dispatcher decided.
@@ -76,6 +79,12 @@ long long packed_weight_bytes(int C, int K, int KT, int KH, int KW, int dtype);
 bool pack_supported(int KT, int KH, int KW, int dtype);
 libconv_status pack_launch(const void* w, void* wp, int C, int K, int KT, int KH, int KW,
                            int dtype, hipStream_t stream);
+
+// Channel-packed activations: bytes of a tensor, and the conversions from and
+// to the plain layout (spatial = T*H*W elements per channel).
+long long cpack_bytes(int N, int C, long long spatial, int dtype);
+libconv_status layout_launch(const void* src, void* dst, int N, int C, long long spatial,
+                             int dtype, bool to_packed, hipStream_t stream);
 
 const char* direct_tile_name(int id);
 const char* igemm_tile_name(int id);

@@ -223,6 +223,52 @@ libconv_status conv3d_forward_tpad(const void* x, const void* w, const void* pac
                                    int dtype, int act, void* stream);
 
 /*
+ * Channel-packed activations.  The page "PP-OCR on Vulkan compute shaders"
+ * (section 2.3) moved its tensors to a channels-together layout for
+ * contiguous reads of the channels of a pixel, converting once at the edges
+ * rather than in the hot path; the page "SeedVR2 NCNN Vulkan" (section 9)
+ * plans to keep its channel packing (pack4) through the whole network so
+ * that layers stop packing and unpacking between each other.  Here a group
+ * is one 16-byte vector of channels, g = 8 for 16-bit dtypes and 4 for fp32:
+ *   x_packed [N][ceil(C/g)][T][H][W][g],  element (n, c, t, h, w) at
+ *   [n][c / g][t][h][w][c % g];  channels past C in the last group are 0.
+ * (2-D tensors: T = 1.)  In this layout a halo row of one channel group is
+ * contiguous memory, which the implicit-GEMM kernels copy straight into
+ * on-chip memory, and an output group leaves as one vector store.
+ *
+ * libconv_cpack_bytes: bytes of such a tensor, or -1 for invalid arguments
+ * or 2^31 bytes or more.
+ * libconv_pack_activations / libconv_unpack_activations: conversion from
+ * and to the plain [N][C][T][H][W] layout, on the device (both pointers
+ * device, caller-owned, not overlapping), enqueued on `stream`; unpacking
+ * drops the channels past C.  Errors as the convolution calls.
+ */
+long long libconv_cpack_bytes(int N, int C, int T, int H, int W, int dtype);
+libconv_status libconv_pack_activations(const void* x, void* x_packed, int N, int C, int T,
+                                        int H, int W, int dtype, void* stream);
+libconv_status libconv_unpack_activations(const void* x_packed, void* x, int N, int C, int T,
+                                          int H, int W, int dtype, void* stream);
+
+/*
+ * conv3d_forward_tpad on channel-packed activations: x is x_packed over
+ * C_in channels, y (written) is packed over C_out channels, including the
+ * zeros past C_out.  The channels past C_in in x must be finite (they meet
+ * zero weights; pack_activations and this call write zeros there).  Both
+ * must be 16-byte aligned.  Weights and bias as conv3d_forward_tpad (exactly
+ * one of w and packed_w; with packed_w only the MFMA kernels run and nothing
+ * is allocated).  2-D: T = KT = 1, time pads 0.  The MFMA kernels for this
+ * layout cover 3x3x3 and 3x3 (stride 1), 3x3 stride 2 and 1x1; other shapes
+ * run on the vector-ALU kernel (not with packed_w: LIBCONV_ERR_UNSUPPORTED).
+ */
+libconv_status conv3d_forward_cpack(const void* x, const void* w, const void* packed_w,
+                                    const void* bias, void* y,
+                                    int N, int C_in, int T, int H, int W,
+                                    int C_out, int KT, int KH, int KW,
+                                    int pad_t_front, int pad_t_back, int pad_h, int pad_w,
+                                    int stride_t, int stride_h, int stride_w,
+                                    int dtype, int act, void* stream);
+
+/*
  * Frame windows of a long video.  A 3-D convolution can be computed a few
  * output frames at a time, each piece from only the input frames it reads;
  * consecutive pieces share the frames their taps overlap on (KT - stride_t
@@ -326,7 +372,8 @@ libconv_status libconv_query_algo(int N, int C_in, int T, int H, int W,
 /* Flags of libconv_query_plan. */
 enum {
   LIBCONV_PLAN_CAPTURING = 1,  /* the call is made while its stream is captured into a graph */
-  LIBCONV_PLAN_POOL2 = 2       /* the call is conv2d_forward_pool */
+  LIBCONV_PLAN_POOL2 = 2,      /* the call is conv2d_forward_pool */
+  LIBCONV_PLAN_CPACK = 4       /* the call is conv3d_forward_cpack (channel-packed activations) */
 };
 
 /*
@@ -336,7 +383,8 @@ enum {
  * made while its stream is being captured into a HIP graph (such a call takes
  * no stream-ordered temporaries: no split-K and no per-call weight packing,
  * so it can run another kernel than the same call made eagerly); with
- * LIBCONV_PLAN_POOL2, the plan of conv2d_forward_pool.  Pure host
+ * LIBCONV_PLAN_POOL2, the plan of conv2d_forward_pool; with
+ * LIBCONV_PLAN_CPACK, the plan of conv3d_forward_cpack.  Pure host
  * arithmetic: works without a GPU.  Output pointers may not be NULL.
  */
 libconv_status libconv_query_plan(int N, int C_in, int T, int H, int W,

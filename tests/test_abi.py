@@ -280,3 +280,34 @@ def test_fold_batchnorm_errors():
     assert lib.libconv_fold_batchnorm(fp(w), None, fp(v), fp(v), fp(v), fp(neg), 1e-5, 2, 4,
                                       fp(wo), fp(bo)) == 2
     assert np.all(wo == 7)  # nothing written
+
+
+def test_cpack_bytes():
+    # [N][ceil(C/g)][T][H][W] x 16 bytes, g = 16 bytes of channels
+    assert L.libconv_cpack_bytes(2, 13, 1, 5, 7, L.F16) == 2 * 2 * 5 * 7 * 16
+    assert L.libconv_cpack_bytes(1, 13, 3, 5, 7, L.F32) == 1 * 4 * 3 * 5 * 7 * 16
+    assert L.libconv_cpack_bytes(1, 8, 1, 1, 1, L.BF16) == 16
+    assert L.libconv_cpack_bytes(0, 8, 1, 4, 4, L.F16) == 0
+    assert L.libconv_cpack_bytes(1, 0, 1, 4, 4, L.F16) == -1
+    assert L.libconv_cpack_bytes(1, 8, 1, 4, 4, 9) == -1
+    assert L.libconv_cpack_bytes(1, 1 << 20, 1, 1 << 10, 1 << 10, L.F32) == -1
+
+
+def test_cpack_argument_errors_without_gpu():
+    """Rejected before any device access; a valid call reaches the device
+    check (this host has none)."""
+    fake = 1 << 40
+    y = fake + (1 << 32)
+    geo = (1, 16, 5, 8, 32, 24, 3, 3, 3, 1, 1, 1, 1, 1, 1, 1)
+    assert L.conv3d_forward_cpack(fake, fake, fake, None, y, *geo, L.F16, 0, None) == 1
+    assert L.conv3d_forward_cpack(fake, None, None, None, y, *geo, L.F16, 0, None) == 1
+    assert L.conv3d_forward_cpack(fake, fake, None, None, y, *geo, 7, 0, None) == 3
+    assert L.conv3d_forward_cpack(fake, fake, None, None, y, *geo, L.F16, 3, None) == 4
+    assert L.conv3d_forward_cpack(fake, fake, None, None, fake, *geo, L.F16, 0, None) == 5
+    assert L.conv3d_forward_cpack(fake, fake, None, None, y, *geo, L.F16, 0, None) == 7
+    assert L.libconv_pack_activations(fake, y, 1, 16, 5, 8, 32, 5, None) == 3
+    assert L.libconv_pack_activations(fake, y, 1, 0, 5, 8, 32, L.F16, None) == 2
+    assert L.libconv_pack_activations(None, y, 1, 16, 5, 8, 32, L.F16, None) == 1
+    assert L.libconv_pack_activations(fake, fake + 64, 1, 16, 5, 8, 32, L.F16, None) == 5
+    assert L.libconv_unpack_activations(fake, y, 1, 16, 5, 8, 32, L.F16, None) == 7
+

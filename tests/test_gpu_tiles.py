@@ -32,12 +32,14 @@ def note(msg):
     sys.stdout.flush()
 
 
-def _tiles():
+def _tiles(plain_layout_only: bool = False):
+    """The MFMA tiles; plain_layout_only drops the channel-packed ones
+    ("igemm16x" / "igemm32x", tested with their own layout elsewhere)."""
     import direct_implicit_gemm_amd as L
     out = []
     for tid in range(1, 400):
         name = L.libconv_tile_name(tid)
-        if name.startswith("igemm"):
+        if name.startswith("igemm") and not (plain_layout_only and name[7:8] == "x"):
             out.append((tid, name))
     return out
 
@@ -87,7 +89,7 @@ def _layer_for(tid: int, name: str, ragged: bool) -> W.Layer:
 @pytest.mark.parametrize("ragged", [False, True])
 def test_every_tile(ragged, monkeypatch):
     import direct_implicit_gemm_amd as L
-    tiles = _tiles()
+    tiles = _tiles(plain_layout_only=True)
     assert len(tiles) >= 20
     for i, (tid, name) in enumerate(tiles):
         monkeypatch.setenv("LIBCONV_FORCE_TILE", str(tid))

@@ -59,6 +59,9 @@ class Layer:
     pad_t_back: Optional[int] = None
     # 2x2 stride-2 max pooling after the activation, fused into the conv
     pool: bool = False
+    # activations channel-packed ([N][C/g][T][H][W][g], g = 16 bytes of
+    # channels) instead of plain NC(T)HW
+    cpack: bool = False
 
     @property
     def taps(self) -> int:
@@ -143,6 +146,15 @@ EXTRA_WORKLOADS: Dict[str, Tuple[int, List[Layer]]] = {
         _l3("c5c_B", "f16", 1, 512, 5, 64, 120, 512, 3, 1, 1, "relu", "N01", "N01",
             "U0.05").with_(pad=(2, 1, 1), pad_t_back=0),
     ]),
+    # the video-VAE and diffusion-UNet layers on channel-packed activations
+    # (the network-wide channel packing of "SeedVR2 NCNN Vulkan", section 9);
+    # same shapes and values as the plain-layout workloads
+    "vae3d_cpack_f16": (WORKLOADS["vae3d_f16"][0],
+                        [l.with_(name=l.name.replace("c5_", "c5x_"), cpack=True)
+                         for l in WORKLOADS["vae3d_f16"][1]]),
+    "unet_cpack_bf16": (WORKLOADS["unet_bf16"][0],
+                        [l.with_(name=l.name.replace("c4_", "c4x_"), cpack=True)
+                         for l in WORKLOADS["unet_bf16"][1]]),
 }
 
 
