@@ -63,6 +63,8 @@ WORKLOAD_TEXT = {
                          "3x3x3 512->512 on 64x120 +ReLU"),
     "vae3d_cpack_f16": ("the video-VAE f16 conv3d layers on channel-packed activations "
                         "([N][C/8][T][H][W][8], packed once before timing)"),
+    "ocr_cpack_f32": ("the OCR-detection fp32 stack (chained) on channel-packed activations "
+                      "([N][C/4][H][W][4]) and packed weights, both packed once before timing"),
     "unet_cpack_bf16": ("the diffusion-UNet bf16 layers on channel-packed activations "
                         "([N][C/8][H][W][8], packed once before timing)"),
 }
@@ -256,12 +258,15 @@ def main():
     # Inputs: the workload's seeded tensors; the stack is chained, so only the
     # first layer's x is used when layers feed each other.
     inputs = [W.make_inputs(l) for l in layers]
-    chained = args.workload in ("ocr_stack",)
+    chained = args.workload in ("ocr_stack", "ocr_cpack_f32")
     xs, ws, bs = [], [], []
     for l, (x, w, b) in zip(layers, inputs):
-        # channel-packed layers: the input is packed once, at the network's edge
+        # channel-packed layers: the network is kept in the packed form, so the
+        # input is packed once at its edge, before timing; prepacked layers
+        # get their weights packed once at load (as the pages reorder weights
+        # at export / load), the others pass OI(D)HW weights on every call
         xs.append(L.pack_activations(x.torch(dev)) if l.cpack else x.torch(dev))
-        ws.append(w.torch(dev))
+        ws.append(L.pack_weights(w.torch(dev)) if l.prepacked else w.torch(dev))
         bs.append(b.torch(dev))
     outs = []
     for i, l in enumerate(layers):
@@ -360,7 +365,7 @@ def main():
             l.N, l.C_in, l.T, l.H, l.W, l.C_out, l.KT, l.KH, l.KW, *pad, *l.stride,
             W.DTYPE_CODE[l.dtype], W.ACT_CODE[l.act], L.ALGO_AUTO,
             (L.PLAN_CAPTURING if capturing else 0) | (L.PLAN_POOL2 if l.pool else 0)
-            | (L.PLAN_CPACK if l.cpack else 0))
+            | (L.PLAN_CPACK if l.cpack else 0) | (L.PLAN_PACKED_W if l.prepacked else 0))
         return algo, tile, grid, ks
 
     b2b, b2b_graph = [], []

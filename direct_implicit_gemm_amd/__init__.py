@@ -143,7 +143,7 @@ def libconv_forward_algo(x, w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW, pad
                                        dtype, act, algo, stream)
 
 
-PLAN_CAPTURING, PLAN_POOL2, PLAN_CPACK = 1, 2, 4
+PLAN_CAPTURING, PLAN_POOL2, PLAN_CPACK, PLAN_PACKED_W = 1, 2, 4, 8
 
 
 def conv2d_forward_pool(x, w, bias, y, N, C_in, H, W, C_out, KH, KW, pad_h, pad_w, stride_h,

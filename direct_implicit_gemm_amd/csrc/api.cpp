@@ -791,10 +791,16 @@ libconv_status libconv_query_plan(int N, int C_in, int T, int H, int W, int C_ou
   p.no_temps = (capturing & LIBCONV_PLAN_CAPTURING) != 0;
   p.pool = (capturing & LIBCONV_PLAN_POOL2) != 0;
   p.cpack = (capturing & LIBCONV_PLAN_CPACK) != 0;
+  const bool packed_w = (capturing & LIBCONV_PLAN_PACKED_W) != 0;
+  static const char packed_marker = 0;  // planning only asks whether packed weights exist
+  if (packed_w) {  // as the calls that take packed weights
+    p.no_temps = true;
+    p.wp = &packed_marker;
+  }
   libconv_status st = validate(p, algo, false);
   if (st != LIBCONV_OK) return st;
   Plan plan;
-  st = plan_for(p, algo, &plan);
+  st = plan_for(p, packed_w ? LIBCONV_ALGO_IGEMM : algo, &plan, packed_w);
   if (st != LIBCONV_OK) return st;
   *algo_out = plan.algo;
   *tile_out = plan.tile;

@@ -373,7 +373,9 @@ libconv_status libconv_query_algo(int N, int C_in, int T, int H, int W,
 enum {
   LIBCONV_PLAN_CAPTURING = 1,  /* the call is made while its stream is captured into a graph */
   LIBCONV_PLAN_POOL2 = 2,      /* the call is conv2d_forward_pool */
-  LIBCONV_PLAN_CPACK = 4       /* the call is conv3d_forward_cpack (channel-packed activations) */
+  LIBCONV_PLAN_CPACK = 4,      /* the call is conv3d_forward_cpack (channel-packed activations) */
+  LIBCONV_PLAN_PACKED_W = 8    /* the call passes packed weights (libconv_forward_packed, or
+                                  packed_w of the _tpad / _cpack / _frames calls) */
 };
 
 /*
@@ -384,7 +386,9 @@ enum {
  * no stream-ordered temporaries: no split-K and no per-call weight packing,
  * so it can run another kernel than the same call made eagerly); with
  * LIBCONV_PLAN_POOL2, the plan of conv2d_forward_pool; with
- * LIBCONV_PLAN_CPACK, the plan of conv3d_forward_cpack.  Pure host
+ * LIBCONV_PLAN_CPACK, the plan of conv3d_forward_cpack; with
+ * LIBCONV_PLAN_PACKED_W, the plan of a call given packed weights (MFMA
+ * tiles that read them, no temporaries).  Pure host
  * arithmetic: works without a GPU.  Output pointers may not be NULL.
  */
 libconv_status libconv_query_plan(int N, int C_in, int T, int H, int W,

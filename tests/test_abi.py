@@ -311,3 +311,20 @@ def test_cpack_argument_errors_without_gpu():
     assert L.libconv_pack_activations(fake, fake + 64, 1, 16, 5, 8, 32, L.F16, None) == 5
     assert L.libconv_unpack_activations(fake, y, 1, 16, 5, 8, 32, L.F16, None) == 7
 
+
+
+def test_query_plan_packed_weights_and_cpack_flags():
+    """PLAN_PACKED_W plans as a call given packed weights (packed MFMA tiles,
+    no split); PLAN_CPACK plans the channel-packed layout's own tiles."""
+    vae = (1, 512, 5, 64, 120, 512, 3, 3, 3, 1, 1, 1, 1, 1, 1, L.F16, 1, L.ALGO_AUTO)
+    st, algo, tile, grid, ks = L.libconv_query_plan(*vae, L.PLAN_PACKED_W)
+    assert st == 0 and algo == L.ALGO_IGEMM and ks == 1
+    assert L.libconv_tile_name(tile).startswith("igemm16p_")
+    st, algo, tile, grid, ks = L.libconv_query_plan(*vae, L.PLAN_CPACK)
+    assert st == 0 and L.libconv_tile_name(tile).startswith("igemm16x_")
+    # a 5x5 layer: no packed kernels at all
+    k5 = (1, 16, 1, 32, 32, 16, 1, 5, 5, 0, 2, 2, 1, 1, 1, L.F16, 0, L.ALGO_AUTO)
+    assert L.libconv_query_plan(*k5, L.PLAN_PACKED_W)[0] == 6
+    # the channel-packed layout without packed weights: the vector-ALU kernel
+    st, algo, tile, grid, ks = L.libconv_query_plan(*k5, L.PLAN_CPACK)
+    assert st == 0 and algo == L.ALGO_DIRECT and not L.libconv_tile_name(tile).startswith("tap_")

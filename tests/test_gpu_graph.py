@@ -157,3 +157,54 @@ def test_graph_layers_that_take_temporaries_eagerly(monkeypatch):
         run(fresh())  # the program's own eager work between replays (with temporaries)
         torch.cuda.synchronize()
         note(f"replay {r} ok")
+
+
+def test_graph_packed_layout_frames_and_causal():
+    """Channel-packed layers (packed weights: MFMA tiles, nothing allocated),
+    a causal layer and a frame-window call, recorded into one graph: every
+    replay equals the eager result bit for bit."""
+    import direct_implicit_gemm_amd as L
+    dev = "cuda:0"
+    l1 = W.Layer("gp1", "f16", 1, 16, 4, 8, 40, 40, 3, 3, 3, (1, 1, 1), (1, 1, 1), "relu", 3,
+                 "N01", "N01", "U0.05")
+    l2 = l1.with_(C_in=40, C_out=24)
+    x, w1, b1 = W.make_inputs(l1, 610)
+    _, w2, b2 = W.make_inputs(l2, 611)
+    xt = x.torch(dev)
+    p1, p2 = L.pack_weights(w1.torch(dev)), L.pack_weights(w2.torch(dev))
+    bt1, bt2 = b1.torch(dev), b2.torch(dev)
+    xp = L.pack_activations(xt)
+    y1 = L.conv_cpack(xp, p1, bt1, 1, 1, act="relu")           # allocate outputs eagerly
+    y2 = L.conv_cpack(y1, p2, bt2, 1, 1, act="relu")
+    yc = L.conv3d_tpad(xt, p1, bt1, (2, 0), 1, 1, "relu")        # causal
+    st_, f0, tw = L.libconv_frame_window(4, 3, 2, 0, 1, 2, 2)
+    assert st_ == 0
+    xw = xt[:, :, f0:f0 + tw].contiguous()
+    yf = L.conv3d_frames(xw, p1, bt1, 4, (2, 2), (2, 0), 1, 1, "relu")
+
+    def run():
+        L.conv_cpack(xp, p1, bt1, 1, 1, act="relu", out=y1)
+        L.conv_cpack(y1, p2, bt2, 1, 1, act="relu", out=y2)
+        L.conv3d_tpad(xt, p1, bt1, (2, 0), 1, 1, "relu", out=yc)
+        L.conv3d_frames(xw, p1, bt1, 4, (2, 2), (2, 0), 1, 1, "relu", out=yf)
+
+    run()
+    torch.cuda.synchronize()
+    eager = [y1.data.clone(), y2.data.clone(), yc.clone(), yf.clone()]
+    # the window's frames equal those frames of the causal whole-clip call
+    assert torch.equal(yf, yc[:, :, 2:4]) or torch.allclose(yf.float(), yc[:, :, 2:4].float(),
+                                                            rtol=2 ** -9, atol=2 ** -12)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    for r in range(3):
+        for t in (y1.data, y2.data):
+            t.zero_()
+        yc.fill_(float("nan"))
+        yf.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for i, t in enumerate((y1.data, y2.data, yc, yf)):
+            assert torch.equal(t, eager[i]), f"replay {r}, output {i}"
+        note(f"replay {r}: packed, causal and window outputs equal the eager ones")

@@ -62,6 +62,9 @@ class Layer:
     # activations channel-packed ([N][C/g][T][H][W][g], g = 16 bytes of
     # channels) instead of plain NC(T)HW
     cpack: bool = False
+    # weights packed once at load (libconv_pack_weights) instead of passed
+    # as OI(D)HW on every call
+    prepacked: bool = False
 
     @property
     def taps(self) -> int:
@@ -152,6 +155,11 @@ EXTRA_WORKLOADS: Dict[str, Tuple[int, List[Layer]]] = {
     "vae3d_cpack_f16": (WORKLOADS["vae3d_f16"][0],
                         [l.with_(name=l.name.replace("c5_", "c5x_"), cpack=True)
                          for l in WORKLOADS["vae3d_f16"][1]]),
+    # (the OCR stack's weights packed once at load: its plain-layout tiles
+    # read OIHW weights, the packed-layout tiles packed ones)
+    "ocr_cpack_f32": (WORKLOADS["ocr_stack"][0],
+                      [l.with_(name=l.name.replace("c2_", "c2x_"), cpack=True, prepacked=True)
+                       for l in WORKLOADS["ocr_stack"][1]]),
     "unet_cpack_bf16": (WORKLOADS["unet_bf16"][0],
                         [l.with_(name=l.name.replace("c4_", "c4x_"), cpack=True)
                          for l in WORKLOADS["unet_bf16"][1]]),
