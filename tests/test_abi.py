@@ -328,3 +328,19 @@ def test_query_plan_packed_weights_and_cpack_flags():
     # the channel-packed layout without packed weights: the vector-ALU kernel
     st, algo, tile, grid, ks = L.libconv_query_plan(*k5, L.PLAN_CPACK)
     assert st == 0 and algo == L.ALGO_DIRECT and not L.libconv_tile_name(tile).startswith("tap_")
+
+
+def test_new_calls_with_an_empty_batch_do_nothing():
+    """N = 0: nothing to compute, OK without touching a device (this host has
+    none) for the window, chunked, packed-layout and conversion calls."""
+    fake = 1 << 40
+    y = fake + (1 << 32)
+    geo = (0, 16, 5, 8, 32, 24, 3, 3, 3, 2, 0, 1, 1, 1, 1, 1)
+    assert L.conv3d_forward_cpack(fake, fake, None, None, y, *geo, L.F16, 0, None) == 0
+    assert L.conv3d_forward_frames(fake, fake, None, None, y, *geo, 1, 2, L.F16, 0, None) == 0
+    need = L.libconv_chunked_workspace_bytes(*geo, 2, L.F16)
+    assert need >= 0
+    assert L.conv3d_forward_chunked(fake, fake, None, None, y, *geo, 2, fake + (1 << 34),
+                                    max(need, 1), L.F16, 0, None, None, None) == 0
+    assert L.libconv_pack_activations(fake, y, 0, 16, 5, 8, 32, L.F16, None) == 0
+    assert L.libconv_unpack_activations(fake, y, 0, 16, 5, 8, 32, L.F16, None) == 0
