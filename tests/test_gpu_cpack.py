@@ -82,6 +82,10 @@ TILE_CASES = [
     (290, "f32", 12, 40, 1, 17, 40, (1, 3, 3), (1, 1, 1), (0, 1, 1), None, True),
     (291, "f32", 8, 70, 1, 19, 67, (1, 3, 3), (1, 2, 2), (0, 1, 1), None, True),
     (292, "f32", 32, 70, 1, 9, 31, (1, 1, 1), (1, 1, 1), (0, 0, 0), None, False),
+    # a 3-channel stem (one group, padded) and 5 channels: fewer groups than a stage
+    (291, "f32", 3, 32, 1, 40, 64, (1, 3, 3), (1, 2, 2), (0, 1, 1), None, True),
+    (290, "f32", 5, 24, 1, 12, 36, (1, 3, 3), (1, 1, 1), (0, 1, 1), None, False),
+    (282, "bf16", 3, 16, 1, 10, 33, (1, 3, 3), (1, 1, 1), (0, 1, 1), None, True),
 ]
 
 
