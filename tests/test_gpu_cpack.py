@@ -228,3 +228,28 @@ def test_cpack_split_k(tid, dt, ks, monkeypatch):
     x, w, b = W.make_inputs(layer, 1300 + tid + ks)
     yp = _run_cpack(layer, x, w, b, packed_w=False)
     _check(layer, x, w, b, yp, f"split {tid}/{ks}")
+
+
+def test_cpack_batch_no_bias():
+    """N = 3, no bias, through a forced packed tile and the vector-ALU kernel."""
+    import direct_implicit_gemm_amd as L
+    import os
+    for tid, ks in ((282, (1, 3, 3)), (None, (1, 5, 5))):
+        layer = W.Layer("cpb", "f16", 3, 24, 1, 11, 40, 40, *ks, (0, ks[1] // 2, ks[2] // 2),
+                        (1, 1, 1), "none", 2, "N01", "N01", "zero")
+        x, w, b = W.make_inputs(layer, 1500 + (tid or 0))
+        if tid:
+            os.environ["LIBCONV_FORCE_TILE"] = str(tid)
+        try:
+            note(f"cpack N=3 no bias, tile {tid}, kernel {ks}")
+            xp = L.pack_activations(x.torch("cuda"))
+            wq = L.pack_weights(w.torch("cuda")) if tid else w.torch("cuda")
+            yp = L.conv_cpack(xp, wq, None, 1, layer.pad[1:])
+            torch.cuda.synchronize()
+        finally:
+            os.environ.pop("LIBCONV_FORCE_TILE", None)
+        ref, s = oracle.conv(x.f64(), w.f64(), None, 1, layer.pad[1:])
+        y = _to_f64(oracle.unpack_channels(_packed_numpy(yp, "f16"), 40), "f16")
+        m = metrics(y, ref, s, "f16")
+        note(f"  {m}")
+        assert_gates(m, "f16", f"cpack N=3 {tid}")

@@ -185,3 +185,33 @@ def test_chunked_long_video_full_size():
     m = metrics(yd.ravel()[idx], ref, s, layer.dtype)
     note(f"  sampled {m}")
     assert_gates(m, layer.dtype, "long video")
+
+
+@pytest.mark.parametrize("where", ["host", "device"])
+def test_chunked_batch_of_two_no_bias(where):
+    """N = 2 (the copies take N * C rows of frames) and no bias."""
+    import direct_implicit_gemm_amd as L
+    layer = W.Layer("frames", "bf16", 2, 16, 7, 6, 40, 72, 3, 3, 3, (2, 1, 1), (1, 1, 1),
+                    "relu", 3, "N01", "N01", "zero")
+    x, w, b = W.make_inputs(layer, 813)
+    ref, s = oracle.conv(x.f64(), w.f64(), None, layer.stride, layer.pad, relu=True,
+                         pad_t_back=0)
+    if where == "host":
+        xs = torch.empty(x.shape, dtype=torch.bfloat16, pin_memory=True)
+        xs.copy_(x.torch("cpu"))
+    else:
+        xs = x.torch("cuda")
+    note(f"chunked N=2 no bias, x on {where}")
+    y = L.conv3d_chunked(xs, w.torch("cuda"), None, 3, (2, 0), 1, 1, "relu")
+    torch.cuda.synchronize()
+    m = metrics(to_f64(y), ref, s, "bf16")
+    note(f"  {m}")
+    assert_gates(m, "bf16", "chunked N=2")
+    # the window call on its own, batch of two
+    st_, f0, tw = L.libconv_frame_window(7, 3, 2, 0, 1, 3, 4)
+    assert st_ == 0
+    yw = L.conv3d_frames(x.torch("cuda")[:, :, f0:f0 + tw].contiguous(), w.torch("cuda"), None,
+                         7, (3, 4), (2, 0), 1, 1, "relu")
+    torch.cuda.synchronize()
+    m = metrics(to_f64(yw), ref[:, :, 3:7], s[:, :, 3:7], "bf16")
+    assert_gates(m, "bf16", "frames N=2")
