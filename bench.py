@@ -217,7 +217,7 @@ def main():
                     help="instead of the workload, the video-VAE 128-channel causal layer over "
                          "FRAMES frames: whole on the device, and streamed in chunks of "
                          "--chunk output frames from device and from pinned host memory")
-    ap.add_argument("--chunk", type=int, default=5)
+    ap.add_argument("--chunk", type=int, default=3)
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

@@ -697,7 +697,10 @@ libconv_status conv3d_forward_chunked(const void* x, const void* w, const void* 
   };
   // Input window of chunk c into xb[c & 1]: N*C_in rows of tw frames, taken
   // at frame f0 of rows T frames apart.  Its buffer was last read by
-  // conv(c - 2).
+  // conv(c - 2).  Frames the previous window also holds (the time halo) are
+  // copied from xb[(c - 1) & 1] on the device, so that each frame of x is
+  // read from its source once.
+  int prev_f0 = 0, prev_tw = 0;
   auto copy_in = [&](int c) -> libconv_status {
     const int o0 = c * chunk, on = std::min(chunk, cp.OT - o0);
     int f0 = 0, tw = 0;
@@ -705,10 +708,27 @@ libconv_status conv3d_forward_chunked(const void* x, const void* w, const void* 
                                                   on, &f0, &tw);
     if (s != LIBCONV_OK) return s;
     if (c >= 2 && !wait(ki, ev_conv[c & 1])) return LIBCONV_ERR_LAUNCH;
-    const char* src = static_cast<const char*>(x) + (size_t)f0 * x_frame;
-    if (!ok(hipMemcpy2DAsync(xb[c & 1], tw * x_frame, src, (size_t)T * x_frame, tw * x_frame,
-                             (size_t)N * C_in, hipMemcpyDefault, ki)))
-      return LIBCONV_ERR_LAUNCH;
+    char* dst = static_cast<char*>(xb[c & 1]);
+    const size_t rows = (size_t)N * C_in, pitch = tw * x_frame;
+    // windows only move forward in time, so a shared part is the head of
+    // this window and the tail of the previous one
+    const int shared =
+        c == 0 ? 0 : std::max(0, std::min(prev_f0 + prev_tw, f0 + tw) - std::max(prev_f0, f0));
+    if (shared > 0 && f0 >= prev_f0) {
+      const char* held = static_cast<const char*>(xb[(c - 1) & 1]) + (f0 - prev_f0) * x_frame;
+      if (!ok(hipMemcpy2DAsync(dst, pitch, held, prev_tw * x_frame, shared * x_frame, rows,
+                               hipMemcpyDeviceToDevice, ki)))
+        return LIBCONV_ERR_LAUNCH;
+    }
+    const int own = shared > 0 && f0 >= prev_f0 ? shared : 0;
+    if (own < tw) {
+      const char* src = static_cast<const char*>(x) + (size_t)(f0 + own) * x_frame;
+      if (!ok(hipMemcpy2DAsync(dst + own * x_frame, pitch, src, (size_t)T * x_frame,
+                               (tw - own) * x_frame, rows, hipMemcpyDefault, ki)))
+        return LIBCONV_ERR_LAUNCH;
+    }
+    prev_f0 = f0;
+    prev_tw = tw;
     return record(ev_in[c & 1], ki) ? LIBCONV_OK : LIBCONV_ERR_LAUNCH;
   };
   // Output chunk c from yb[c & 1] into frames [o0, o0 + on) of y, once

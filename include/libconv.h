@@ -331,7 +331,9 @@ long long libconv_chunked_workspace_bytes(int N, int C_in, int T, int H, int W,
  * libconv_chunked_workspace_bytes).  Chunk c + 1's window is copied in on
  * copy_in_stream and chunk c - 1's output copied out on copy_out_stream
  * while chunk c computes on `stream` (the two copy streams let the two
- * directions of the host link run at once).  The copies start after the
+ * directions of the host link run at once).  Each input frame is copied
+ * from x once: the frames consecutive windows share (the time halo) move
+ * from one window buffer to the other on the device.  The copies start after the
  * work already on `stream`, and `stream` waits for the last of them.
  * copy_out_stream NULL: outputs are copied on copy_in_stream; both NULL:
  * everything runs in order on `stream`.  Weights and bias are on the device;

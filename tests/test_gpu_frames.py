@@ -49,6 +49,7 @@ CASES = [
     ("f16", 16, 64, 9, 6, 32, 2, 1, 1, False),    # time stride 2
     ("f32", 12, 20, 6, 6, 24, 1, 1, 1, False),    # fp32: the direct kernel
     ("bf16", 8, 96, 5, 7, 40, 1, 0, 2, True),     # padding only after
+    ("f16", 16, 64, 10, 6, 32, 3, 0, 0, False),   # stride = KT: windows share no frame
 ]
 
 
