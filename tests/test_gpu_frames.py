@@ -127,6 +127,30 @@ def test_chunks_equal_whole_video_one_tile(monkeypatch, where):
         assert torch.equal(y.cuda(), whole)
 
 
+def test_chunked_pageable_host_memory():
+    """x and y in ordinary (pageable) host memory: the copies block the host
+    but the result is the one pinned memory gives, bit for bit, and within
+    the oracle gates."""
+    import direct_implicit_gemm_amd as L
+    layer = _layer("bf16", 16, 72, 8, 8, 40, 1, 2)
+    x, w, b = W.make_inputs(layer, 813)
+    ref, s = _oracle(layer, x, w, b, 0)
+    wt, bt = w.torch("cuda"), b.torch("cuda")
+    pinned = torch.empty(x.shape, dtype=torch.bfloat16, pin_memory=True)
+    pinned.copy_(x.torch("cpu"))
+    plain = x.torch("cpu").clone()
+    assert not plain.is_pinned()
+    note("chunked, pageable x and y")
+    y_pinned = L.conv3d_chunked(pinned, wt, bt, 3, (2, 0), 1, 1, "relu")
+    y_plain = L.conv3d_chunked(plain, wt, bt, 3, (2, 0), 1, 1, "relu",
+                               out=torch.empty(tuple(y_pinned.shape), dtype=torch.bfloat16))
+    torch.cuda.synchronize()
+    assert not y_plain.is_pinned()
+    assert torch.equal(y_plain, y_pinned)
+    m = metrics(to_f64(y_plain), ref, s, "bf16")
+    assert_gates(m, "bf16", "pageable")
+
+
 @pytest.mark.parametrize("streams", ["one", "one_copy"])
 def test_chunked_stream_modes(streams):
     """Everything on the compute stream, or both copy directions on one copy
