@@ -710,21 +710,19 @@ libconv_status conv3d_forward_chunked(const void* x, const void* w, const void* 
     if (c >= 2 && !wait(ki, ev_conv[c & 1])) return LIBCONV_ERR_LAUNCH;
     char* dst = static_cast<char*>(xb[c & 1]);
     const size_t rows = (size_t)N * C_in, pitch = tw * x_frame;
-    // windows only move forward in time, so a shared part is the head of
-    // this window and the tail of the previous one
-    const int shared =
-        c == 0 ? 0 : std::max(0, std::min(prev_f0 + prev_tw, f0 + tw) - std::max(prev_f0, f0));
-    if (shared > 0 && f0 >= prev_f0) {
-      const char* held = static_cast<const char*>(xb[(c - 1) & 1]) + (f0 - prev_f0) * x_frame;
-      if (!ok(hipMemcpy2DAsync(dst, pitch, held, prev_tw * x_frame, shared * x_frame, rows,
+    // windows only move forward in time: the frames this window shares with
+    // the previous one are that window's tail, held in xb[(c - 1) & 1]
+    const int held = c > 0 && f0 >= prev_f0 ? std::clamp(prev_f0 + prev_tw - f0, 0, tw) : 0;
+    if (held > 0) {
+      const char* tail = static_cast<const char*>(xb[(c - 1) & 1]) + (f0 - prev_f0) * x_frame;
+      if (!ok(hipMemcpy2DAsync(dst, pitch, tail, prev_tw * x_frame, held * x_frame, rows,
                                hipMemcpyDeviceToDevice, ki)))
         return LIBCONV_ERR_LAUNCH;
     }
-    const int own = shared > 0 && f0 >= prev_f0 ? shared : 0;
-    if (own < tw) {
-      const char* src = static_cast<const char*>(x) + (size_t)(f0 + own) * x_frame;
-      if (!ok(hipMemcpy2DAsync(dst + own * x_frame, pitch, src, (size_t)T * x_frame,
-                               (tw - own) * x_frame, rows, hipMemcpyDefault, ki)))
+    if (held < tw) {
+      const char* src = static_cast<const char*>(x) + (size_t)(f0 + held) * x_frame;
+      if (!ok(hipMemcpy2DAsync(dst + held * x_frame, pitch, src, (size_t)T * x_frame,
+                               (tw - held) * x_frame, rows, hipMemcpyDefault, ki)))
         return LIBCONV_ERR_LAUNCH;
     }
     prev_f0 = f0;
