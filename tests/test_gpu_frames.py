@@ -50,6 +50,7 @@ CASES = [
     ("f32", 12, 20, 6, 6, 24, 1, 1, 1, False),    # fp32: the direct kernel
     ("bf16", 8, 96, 5, 7, 40, 1, 0, 2, True),     # padding only after
     ("f16", 16, 64, 10, 6, 32, 3, 0, 0, False),   # stride = KT: windows share no frame
+    ("bf16", 8, 64, 13, 6, 32, 4, 1, 0, True),    # stride > KT: frames between windows unread
 ]
 
 
