@@ -3,27 +3,34 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
 
 A step is one pass of the workload's convolution layers over one batch of
-synthetic input, chained on the GPU (layer k reads layer k-1's output), with
-every layer through libconv.  The default workload is the fp32 OCR-detection
-stack (N=1, 3x640x640; conv3x3/s2 3->32 +ReLU, conv3x3 32->32 +ReLU,
-conv1x1 32->64 +ReLU, conv3x3/s2 64->64 +ReLU).
+synthetic input, every layer through libconv with OI(D)HW weights given on
+every call.  The default workload is the largest configuration, the video-VAE
+3-D convolutions in f16 (N=1, T=5: 3x3x3 128->128 on 256x480, and 3x3x3
+512->512 on 64x120 +ReLU), 1087 effective GFLOP per step.
 
-Printed: ONE JSON line.  ``value`` is the step's effective TFLOP/s
-(2*N*C_out*out_spatial*C_in*taps summed over layers, divided by the time of a
-step); per-layer figures (µs, TFLOP/s, GB/s, binding roofline and fraction)
-are in ``layers``; ``roofline`` describes the layer whose kernel takes the most
-time; ``cpu_baseline`` is the fp64 oracle timed on the host cores.
+Timing (cold protocol, the primary figures): before every timed call a 512 MB
+scratch buffer is written (evicting the 256 MB Infinity Cache and the L2s),
+outside the event pair; one event pair on the launch stream brackets each call.
+K steps (at least 20; layers under 10 us get at least 200 reps) give the median
+and the minimum.  `ms_per_step` is the median cold step (the sum of its layers'
+times), `value` = effective FLOP per step / that time.  Warm figures, labelled
+as such: K steps back to back between one event pair, eagerly and as replays of
+the step captured once as a HIP graph.
 
-The step is timed twice, K eager steps and K replays of the step captured
-once as a HIP graph (no host launch overhead; ``--no-graph`` skips it), and
-the faster is reported (``config.step_mode``; both times are in ``config``).
-Per-layer times: ``us_b2b``, one event pair around R back-to-back launches of
-the layer alone, divided by R (for short kernels this is bounded by the host's
-call rate); ``us_graph``, the same R launches captured once as a HIP graph and
-replayed between one event pair (no host in the timed region; only when the
-call plans the same kernel under capture).  ``us`` is the smaller, and the
-roofline fractions use it; it matches the kernel durations of a rocprofv3
-kernel trace.
+Per layer, three calls of the same convolution, each timed cold:
+  * `step`: libconv_forward_ex with the OI(D)HW weights and the workspace
+    libconv_workspace_size names (what conv3d_forward_ws / conv2d_forward_ws
+    do): the weights are packed into the workspace on every call when the
+    chosen kernel reads packed weights, and a split reduction keeps its
+    partial sums there.  This is the call the step times.
+  * `kernel`: the same call on weights packed beforehand, which runs the
+    convolution kernel alone (plus the split-K sum when the plan splits):
+    the `roofline` figures of the dominant layer come from it.
+  * `export`: conv2d_forward / conv3d_forward themselves (no workspace: no
+    per-call packing, no split).
+
+Printed: ONE JSON line (see the keys below).  `cpu_baseline` is the fp64 oracle
+timed on the host cores on a bounded sample of the same step.
 """
 from __future__ import annotations
 
@@ -32,6 +39,7 @@ import hashlib
 import json
 import os
 import platform
+import statistics
 import sys
 import time
 
@@ -46,6 +54,7 @@ import workloads as W  # noqa: E402
 PEAK_HBM_GBS = 8000.0
 PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6, "bf16": 2516.6}   # dense MFMA
 METRIC = "conv fwd effective TFLOP/s + HBM GB/s per layer, % of binding MI355X roofline"
+FLUSH_MB = 512
 
 WORKLOAD_TEXT = {
     "conv1": "single conv2d fp32 N=1 3x32x32 -> 8, 3x3 s1 p1, bias",
@@ -69,6 +78,7 @@ WORKLOAD_TEXT = {
                         "([N][C/8][H][W][8], packed once before timing)"),
 }
 ALL_WORKLOADS = {**W.WORKLOADS, **W.EXTRA_WORKLOADS}
+CHAINED = ("ocr_stack", "ocr_cpack_f32")
 
 
 def time_pads(layer: W.Layer):
@@ -77,13 +87,13 @@ def time_pads(layer: W.Layer):
 
 
 def out_shape(layer: W.Layer, lib):
-    o = [lib.libconv_out_size2(layer.T, layer.KT, *time_pads(layer), layer.stride[0]),
-         lib.libconv_out_size(layer.H, layer.KH, layer.pad[1], layer.stride[1]),
-         lib.libconv_out_size(layer.W, layer.KW, layer.pad[2], layer.stride[2])]
-    return o
+    return [lib.libconv_out_size2(layer.T, layer.KT, *time_pads(layer), layer.stride[0]),
+            lib.libconv_out_size(layer.H, layer.KH, layer.pad[1], layer.stride[1]),
+            lib.libconv_out_size(layer.W, layer.KW, layer.pad[2], layer.stride[2])]
 
 
 def layer_work(layer: W.Layer, lib):
+    """Effective FLOP (padded taps included) and algorithmic bytes (x, w, b, y once)."""
     ot, oh, ow = out_shape(layer, lib)
     out_spatial = ot * oh * ow
     flops = 2 * layer.N * layer.C_out * out_spatial * layer.C_in * layer.taps
@@ -106,16 +116,18 @@ def roofline_of(layer, flops, nbytes, seconds):
 
 def kernel_source_sha():
     h = hashlib.sha256()
-    for f in ("direct.hip", "igemm.hip", "device_common.h"):
-        with open(os.path.join(ROOT, "direct_implicit_gemm_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    csrc = os.path.join(ROOT, "direct_implicit_gemm_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h", ".def")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str, layer: str, tile_name: str):
-    """HBM bytes per launch of a layer from committed rocprofv3 counter runs
-    (profiles/traffic.json), if they were taken on the current kernel sources
-    and the same kernel; else None."""
+    """HBM bytes per launch of a layer's kernel from committed rocprofv3 counter
+    runs (profiles/traffic.json), if they were taken on the current kernel
+    sources and the same kernel; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -127,24 +139,68 @@ def measured_traffic(workload: str, layer: str, tile_name: str):
     return e.get("bytes_per_launch")
 
 
-def cpu_baseline(layers, inputs, budget_s: float):
-    """The oracle (as it stands) on the same step, repeated to ~budget_s."""
+def sp(l):
+    return (l.stride[1:], l.pad[1:]) if l.dims == 2 else (l.stride, l.pad)
+
+
+def cpu_baseline(layers, inputs, budget_s: float, chained: bool):
+    """The oracle (as it stands, fp64, with its |x*w| pass) on a bounded sample
+    of the step: for every layer, the same fraction of its output rows (all
+    batches, channels, frames and columns), computed from the input rows they
+    read; the fraction starts at about 2 GFLOP of work and is doubled (up to
+    the whole step) while one pass takes under budget_s / 8, then the pass is
+    repeated to about budget_s.  The rate is the effective FLOP of the outputs
+    computed, over the time."""
     import oracle
     threads = oracle.threads(len(os.sched_getaffinity(0)))
-    total_flops = 0
-    runs = 0
-    t0 = time.perf_counter()
+
+    def sample(frac, build=True):
+        jobs, flops, rows_taken = [], 0, []
+        for layer, (x, w, b) in zip(layers, inputs):
+            s_, p_ = sp(layer)
+            sh, ph, kh = layer.stride[1], layer.pad[1], layer.KH
+            oh_all = (layer.H + 2 * ph - kh) // sh + 1
+            rows = max(1, int(round(oh_all * frac)))
+            h_in = min(layer.H, (rows - 1) * sh + kh - ph)   # rows those outputs read
+            pf, pb = time_pads(layer)
+            o_t = (layer.T + pf + pb - layer.KT) // layer.stride[0] + 1 if layer.dims == 3 else 1
+            o_h = (h_in + 2 * ph - kh) // sh + 1
+            o_w = (layer.W + 2 * layer.pad[2] - layer.KW) // layer.stride[2] + 1
+            flops += 2 * layer.N * layer.C_out * o_t * o_h * o_w * layer.C_in * layer.taps
+            rows_taken.append(f"{layer.name}: {o_h} of {oh_all} rows")
+            if build:
+                xs = W.Tensor(x.dtype, np.ascontiguousarray(x.storage[..., :h_in, :])).f64()
+                jobs.append((layer, xs, w.f64(), b.f64(), s_, p_))
+        return jobs, flops, rows_taken
+
+    def run(jobs):
+        for layer, xs, w, b, s_, p_ in jobs:
+            y, _ = oracle.conv(xs, w, b, s_, p_, relu=layer.act == "relu",
+                               pad_t_back=layer.pad_t_back)
+            if layer.pool:
+                oracle.max_pool2x2(y)
+
+    _, whole, _ = sample(1.0, build=False)
+    frac = min(1.0, 2e9 / max(whole, 1))
     while True:
-        x = inputs[0][0].f64()
-        for layer, (_, w, b) in zip(layers, inputs):
-            st, pd = (layer.stride[1:], layer.pad[1:]) if layer.dims == 2 else (layer.stride, layer.pad)
-            y, _ = oracle.conv(x, w.f64(), b.f64(), st, pd, relu=layer.act == "relu")
-            x = W.Tensor.quantise(y, layer.dtype).f64()
+        jobs, flops, rows_taken = sample(frac)
+        t0 = time.perf_counter()
+        run(jobs)
+        one = time.perf_counter() - t0
+        if one >= budget_s / 8 or frac >= 1.0:
+            break
+        frac = min(1.0, frac * 2)
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        run(jobs)
         runs += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     el = time.perf_counter() - t0
-    return el / runs, threads, runs
+    note = (f"the first output rows of every layer ({'; '.join(rows_taken)}; all batches, "
+            f"channels, frames, columns; {flops / 1e9:.2f} effective GFLOP per pass), fp64 with "
+            f"the |x*w| sum, {runs} pass(es) in {el:.1f} s")
+    return flops * runs / el, threads, note
 
 
 def long_video(args, torch, L, dev):
@@ -200,16 +256,110 @@ def long_video(args, torch, L, dev):
         "note": "host-pinned rates include both PCIe directions; not the bench value"}))
 
 
+class LayerCalls:
+    """The three calls of one layer (step / kernel / export) on device tensors."""
+
+    def __init__(self, L, lib, torch, dev, layer, x, w, b):
+        self.L, self.lib, self.torch, self.layer = L, lib, torch, layer
+        l = layer
+        self.dt, self.act = W.DTYPE_CODE[l.dtype], W.ACT_CODE[l.act]
+        self.flags = (L.PLAN_POOL2 if l.pool else 0) | (L.PLAN_CPACK if l.cpack else 0)
+        pf, pb = time_pads(l)
+        self.dims = (l.N, l.C_in, l.T, l.H, l.W, l.C_out, l.KT, l.KH, l.KW)
+        self.pads = (pf, pb, l.pad[1], l.pad[2])
+        self.strides = tuple(l.stride)
+        self.x = L.pack_activations(x.torch(dev)) if l.cpack else x.torch(dev)
+        self.xp = self.x.data.data_ptr() if l.cpack else self.x.data_ptr()
+        self.w = w.torch(dev)
+        self.b = b.torch(dev)
+        ot, oh, ow = out_shape(l, lib)
+        if l.pool:
+            oh, ow = oh // 2, ow // 2
+        shape = (l.N, l.C_out, oh, ow) if l.dims == 2 else (l.N, l.C_out, ot, oh, ow)
+        if l.cpack:
+            nb = lib.libconv_cpack_bytes(l.N, l.C_out, ot, oh, ow, self.dt)
+            self.y = L.PackedActivations(torch.empty(nb, dtype=torch.uint8, device=dev), shape,
+                                         self.x.dtype)
+            self.yp = self.y.data.data_ptr()
+        else:
+            self.y = torch.empty(shape, dtype=self.x.dtype, device=dev)
+            self.yp = self.y.data_ptr()
+        self.ws_n = lib.libconv_workspace_size(*self.dims, *self.pads, *self.strides, self.dt,
+                                               self.act, L.ALGO_AUTO, self.flags)
+        assert self.ws_n >= 0, l.name
+        self.ws = torch.empty(max(self.ws_n, 1), dtype=torch.uint8, device=dev)
+        self.plan_step = self.plan(self.ws_n, packed=False)
+        # weights packed once, for the kernel-only call (when a packed kernel runs)
+        self.packed = None
+        if L.libconv_tile_name(self.plan_step[1]).startswith(("igemm16p", "igemm32p", "igemm16x",
+                                                               "igemm32x")):
+            self.packed = L.pack_weights(self.w)
+            kw_n = lib.libconv_workspace_size(*self.dims, *self.pads, *self.strides, self.dt,
+                                              self.act, L.ALGO_AUTO,
+                                              self.flags | L.PLAN_PACKED_W)
+            self.kws_n = max(kw_n, 0)
+            self.kws = torch.empty(max(self.kws_n, 1), dtype=torch.uint8, device=dev)
+            self.plan_kernel = self.plan(self.kws_n, packed=True)
+        else:
+            self.plan_kernel = self.plan_step
+        self.plan_export = self.plan(0, packed=False)
+
+    def plan(self, ws_bytes, packed):
+        l = self.layer
+        pad = (sum(self.pads[:2]) // 2,) + self.pads[2:]   # the query takes one time pad
+        st, algo, tile, grid, ks = self.L.libconv_query_plan(
+            *self.dims, *pad, *self.strides, self.dt, self.act, self.L.ALGO_AUTO,
+            self.flags | (self.L.PLAN_PACKED_W if packed else 0), ws_bytes)
+        assert st == 0, (l.name, st)
+        return algo, tile, grid, ks
+
+    def _ex(self, x_ptr, w_ptr, pw_ptr, ws, ws_n, stream):
+        st = self.lib.libconv_forward_ex(x_ptr, w_ptr, pw_ptr, self.b.data_ptr(), self.yp,
+                                         *self.dims, *self.pads, *self.strides, self.dt,
+                                         self.act, self.L.ALGO_AUTO, self.flags, ws, ws_n,
+                                         stream)
+        if st != 0:
+            raise self.L.LibconvError(st, f"{self.layer.name} libconv_forward_ex")
+
+    def step(self, stream, x_ptr=None):
+        self._ex(x_ptr or self.xp, self.w.data_ptr(), None,
+                 self.ws.data_ptr() if self.ws_n > 0 else None, self.ws_n, stream)
+
+    def kernel(self, stream):
+        if self.packed is None:
+            return self.step(stream)
+        self._ex(self.xp, None, self.packed.data.data_ptr(),
+                 self.kws.data_ptr() if self.kws_n > 0 else None, self.kws_n, stream)
+
+    def export(self, stream):
+        l = self.layer
+        if l.cpack or l.pool or l.pad_t_back is not None:
+            self._ex(self.xp, self.w.data_ptr(), None, None, 0, stream)
+            return
+        if l.dims == 2:
+            st = self.lib.conv2d_forward(self.xp, self.w.data_ptr(), self.b.data_ptr(), self.yp,
+                                         l.N, l.C_in, l.H, l.W, l.C_out, l.KH, l.KW, l.pad[1],
+                                         l.pad[2], l.stride[1], l.stride[2], self.dt, self.act,
+                                         stream)
+        else:
+            st = self.lib.conv3d_forward(self.xp, self.w.data_ptr(), self.b.data_ptr(), self.yp,
+                                         *self.dims, *l.pad, *l.stride, self.dt, self.act,
+                                         stream)
+        if st != 0:
+            raise self.L.LibconvError(st, f"{l.name} conv_forward")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="ocr_stack", choices=sorted(ALL_WORKLOADS))
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="vae3d_f16", choices=sorted(ALL_WORKLOADS))
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--no-graph", action="store_true",
-                    help="time eager steps instead of replays of the step captured as a HIP graph")
-    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle work")
+    ap.add_argument("--no-graph", action="store_true", help="skip the warm graph-replay figures")
+    ap.add_argument("--no-export", action="store_true",
+                    help="skip timing the no-workspace export calls")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the workload, copy MIB MiB device-to-device --steps times "
                          "(a plain copy of known size, to scale HBM byte counters)")
@@ -221,7 +371,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
 
@@ -255,176 +405,145 @@ def main():
         return
 
     _, layers = ALL_WORKLOADS[args.workload]
-    # Inputs: the workload's seeded tensors; the stack is chained, so only the
-    # first layer's x is used when layers feed each other.
+    chained = args.workload in CHAINED
     inputs = [W.make_inputs(l) for l in layers]
-    chained = args.workload in ("ocr_stack", "ocr_cpack_f32")
-    xs, ws, bs = [], [], []
-    for l, (x, w, b) in zip(layers, inputs):
-        # channel-packed layers: the network is kept in the packed form, so the
-        # input is packed once at its edge, before timing; prepacked layers
-        # get their weights packed once at load (as the pages reorder weights
-        # at export / load), the others pass OI(D)HW weights on every call
-        xs.append(L.pack_activations(x.torch(dev)) if l.cpack else x.torch(dev))
-        ws.append(L.pack_weights(w.torch(dev)) if l.prepacked else w.torch(dev))
-        bs.append(b.torch(dev))
-    outs = []
-    for i, l in enumerate(layers):
-        ot, oh, ow = out_shape(l, lib)
-        if l.pool:
-            oh, ow = oh // 2, ow // 2
-        shape = (l.N, l.C_out, oh, ow) if l.dims == 2 else (l.N, l.C_out, ot, oh, ow)
-        if l.cpack:
-            nb = lib.libconv_cpack_bytes(l.N, l.C_out, ot, oh, ow, W.DTYPE_CODE[l.dtype])
-            outs.append(L.PackedActivations(torch.empty(nb, dtype=torch.uint8, device=dev),
-                                            shape, xs[i].dtype))
-        else:
-            outs.append(torch.empty(shape, dtype=xs[i].dtype, device=dev))
+    calls = [LayerCalls(L, lib, torch, dev, l, *inp) for l, inp in zip(layers, inputs)]
+    scratch = torch.empty(FLUSH_MB << 20, dtype=torch.uint8, device=dev)
 
-    def sp(l):
-        return (l.stride[1:], l.pad[1:]) if l.dims == 2 else (l.stride, l.pad)
+    def x_of(i):  # a chained stack feeds each layer the previous layer's output
+        return calls[i - 1].yp if (chained and i > 0) else None
 
-    def conv(l, x_in, w, b, out):
-        if l.cpack:  # channel-packed activations in and out
-            s, p = sp(l)
-            L.conv_cpack(x_in, w, b, s, p, time_pads(l) if l.dims == 3 else None, l.act, out=out)
-        elif l.pool:  # conv + activation + 2x2 max pool in one call
-            L.conv2d_pool(x_in, w, b, l.stride[1:], l.pad[1:], l.act, out=out)
-        elif l.pad_t_back is not None:  # time padding differs before / after the frames
-            L.conv3d_tpad(x_in, w, b, time_pads(l), l.stride, l.pad[1:], l.act, out=out)
-        else:
-            s, p = sp(l)
-            L.conv_nd(x_in, w, b, s, p, l.act, out=out)
+    def step_eager(stream):
+        for i, c in enumerate(calls):
+            c.step(stream, x_of(i))
 
-    def step():
-        for i, l in enumerate(layers):
-            x_in = outs[i - 1] if (chained and i > 0) else xs[i]
-            conv(l, x_in, ws[i], bs[i], outs[i])
-
+    stream = torch.cuda.current_stream(dev).cuda_stream   # the stream libconv launches on
     for _ in range(args.warmup):
-        step()
+        step_eager(stream)
+        for c in calls:
+            c.kernel(stream)
+            if not args.no_export:
+                c.export(stream)
     torch.cuda.synchronize()
 
-    # The step as a HIP graph (captured once through torch's graph capture, on
-    # torch's capture stream, which is the stream libconv launches on): a
-    # replay issues the layers back to back without host launch overhead.
-    # Under capture libconv plans without temporaries (no split-K, no weight
-    # packing per call), which can be slower for some layers, so both the
-    # eager step and the replayed step are timed over K steps and the faster
-    # is reported (both are in `config`).
-    graph, graph_note = None, "off"
+    Ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def cold(fn, reps):
+        """reps timed calls of fn, each after the scratch write, events on the
+        launch stream; returns the per-call times in microseconds."""
+        pairs = []
+        for _ in range(reps):
+            scratch.zero_()                       # outside the event pair
+            e0, e1 = Ev(), Ev()
+            e0.record()
+            fn()
+            e1.record()
+            pairs.append((e0, e1))
+        torch.cuda.synchronize()
+        return [1000.0 * a.elapsed_time(b) for a, b in pairs]
+
+    K = max(args.steps, 20)
+    # ---- the timed steps (cold): each layer's call after its own scratch write
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    step_pairs = []
+    for _ in range(K):
+        lp = []
+        for i, c in enumerate(calls):
+            scratch.zero_()
+            e0, e1 = Ev(), Ev()
+            e0.record()
+            c.step(stream, x_of(i))
+            e1.record()
+            lp.append((e0, e1))
+        step_pairs.append(lp)
+    torch.cuda.synchronize()
+    wall_timed = time.perf_counter() - wall0
+    layer_step_us = [[1000.0 * p[i][0].elapsed_time(p[i][1]) for p in step_pairs]
+                     for i in range(len(calls))]
+    step_us = [sum(layer_step_us[i][k] for i in range(len(calls))) for k in range(K)]
+    ms_per_step = statistics.median(step_us) / 1000.0
+
+    # ---- per layer: more reps for short layers; kernel-only and export calls
+    per_layer = []
+    step_flops = 0
+    for i, c in enumerate(calls):
+        us_step = layer_step_us[i]
+        if statistics.median(us_step) < 10.0 and K < 200:
+            us_step = us_step + cold(lambda: c.step(stream, x_of(i)), 200 - K)
+        us_kernel = us_step if c.packed is None else cold(lambda: c.kernel(stream), len(us_step))
+        us_export = None if args.no_export else cold(lambda: c.export(stream), len(us_step))
+        # warm: the same call back to back
+        for _ in range(3):
+            c.step(stream, x_of(i))
+        torch.cuda.synchronize()
+        e0, e1 = Ev(), Ev()
+        e0.record()
+        for _ in range(K):
+            c.step(stream, x_of(i))
+        e1.record()
+        torch.cuda.synchronize()
+        warm_b2b = 1000.0 * e0.elapsed_time(e1) / K
+        flops, nbytes = layer_work(c.layer, lib)
+        step_flops += flops
+        med_k = statistics.median(us_kernel)
+        bound, tflops, gbs, frac = roofline_of(c.layer, flops, nbytes, med_k * 1e-6)
+        med_s = statistics.median(us_step)
+        _, tf_s, gb_s, fr_s = roofline_of(c.layer, flops, nbytes, med_s * 1e-6)
+        ent = {
+            "layer": c.layer.name,
+            "kernel": L.libconv_tile_name(c.plan_kernel[1]), "grid": c.plan_kernel[2],
+            "ksplit": c.plan_kernel[3],
+            "kernel_us_median": round(med_k, 3), "kernel_us_min": round(min(us_kernel), 3),
+            "kernel_reps": len(us_kernel),
+            "tflops": round(tflops, 3), "gbs": round(gbs, 1), "bound": bound,
+            "frac": round(frac, 4),
+            "step_call": ("OI(D)HW weights + workspace (" +
+                          ("weights packed on the call, " if c.packed is not None else "") +
+                          f"{c.ws_n} bytes)"),
+            "step_kernel": L.libconv_tile_name(c.plan_step[1]), "step_ksplit": c.plan_step[3],
+            "step_us_median": round(med_s, 3), "step_us_min": round(min(us_step), 3),
+            "step_frac": round(fr_s, 4),
+            "warm_b2b_us": round(warm_b2b, 3),
+            "gflop": round(flops / 1e9, 4), "mbytes": round(nbytes / 1e6, 3),
+        }
+        if us_export is not None:
+            me = statistics.median(us_export)
+            ent.update({"export_kernel": L.libconv_tile_name(c.plan_export[1]),
+                        "export_us_median": round(me, 3), "export_us_min": round(min(us_export), 3),
+                        "export_frac": round(roofline_of(c.layer, flops, nbytes, me * 1e-6)[3], 4)})
+        per_layer.append(ent)
+
+    # ---- warm steps: eager back to back, and replays of the step as a HIP graph
+    e0, e1 = Ev(), Ev()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(K):
+        step_eager(stream)
+    e1.record()
+    torch.cuda.synchronize()
+    warm_eager = e0.elapsed_time(e1) / K
+    warm_graph, graph_note = None, "off"
     if not args.no_graph:
         try:
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                step()
+                step_eager(torch.cuda.current_stream(dev).cuda_stream)
             torch.cuda.synchronize()
             g.replay()
             torch.cuda.synchronize()
-            graph, graph_note = g, "captured"
-        except Exception as e:  # a layer whose call cannot be captured: eager steps
-            graph, graph_note = None, f"capture failed ({type(e).__name__})"
+            e0.record()
+            for _ in range(K):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            warm_graph, graph_note = e0.elapsed_time(e1) / K, "captured"
+            del g
+        except Exception as e:  # a call that cannot be captured: no graph figure
+            graph_note = f"capture failed ({type(e).__name__}: {e})"
             torch.cuda.synchronize()
 
-    K = args.steps
-
-    def timed(run_one):
-        torch.cuda.synchronize()
-        t_start = torch.cuda.Event(enable_timing=True)
-        t_end = torch.cuda.Event(enable_timing=True)
-        w0 = time.perf_counter()
-        t_start.record()
-        for _ in range(K):
-            run_one()
-        t_end.record()
-        torch.cuda.synchronize()
-        return t_start.elapsed_time(t_end) / K, time.perf_counter() - w0
-
-    ms_eager, wall_eager = timed(step)
-    ms_graph, wall_graph = timed(graph.replay) if graph is not None else (None, None)
-    if ms_graph is not None and ms_graph < ms_eager:
-        ms_per_step, wall, mode = ms_graph, wall_graph, "graph replay"
-    else:
-        ms_per_step, wall, mode = ms_eager, wall_eager, "eager"
-
-    # Each layer alone, R launches back to back, timed two ways on the launch
-    # stream: (1) issued eagerly between one event pair -- for short kernels
-    # this is bounded by the host's call rate (Python, ctypes, planning,
-    # launch); (2) the same R launches captured once as a HIP graph and
-    # replayed between one event pair, which removes the host from the timed
-    # region.  (2) is taken only when the call plans the same kernel under
-    # capture as eagerly (libconv_query_plan), so both time one kernel.
-    R = max(10, K)
-    GRAPH_REPLAYS = 3
-
-    def plan_of(l, capturing):
-        # the query takes one time pad: one-sided padding is asked as the
-        # symmetric padding with the same number of output frames
-        pad = (sum(time_pads(l)) // 2,) + tuple(l.pad[1:])
-        st_, algo, tile, grid, ks = L.libconv_query_plan(
-            l.N, l.C_in, l.T, l.H, l.W, l.C_out, l.KT, l.KH, l.KW, *pad, *l.stride,
-            W.DTYPE_CODE[l.dtype], W.ACT_CODE[l.act], L.ALGO_AUTO,
-            (L.PLAN_CAPTURING if capturing else 0) | (L.PLAN_POOL2 if l.pool else 0)
-            | (L.PLAN_CPACK if l.cpack else 0) | (L.PLAN_PACKED_W if l.prepacked else 0))
-        return algo, tile, grid, ks
-
-    b2b, b2b_graph = [], []
-    for i, l in enumerate(layers):
-        x_in = outs[i - 1] if (chained and i > 0) else xs[i]
-
-        def launch_r():
-            for _ in range(R):
-                conv(l, x_in, ws[i], bs[i], outs[i])
-
-        conv(l, x_in, ws[i], bs[i], outs[i])
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        launch_r()
-        e1.record()
-        torch.cuda.synchronize()
-        b2b.append(1000.0 * e0.elapsed_time(e1) / R)
-        ug = None
-        if not args.no_graph and plan_of(l, False) == plan_of(l, True):
-            try:
-                gl = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(gl):
-                    launch_r()
-                gl.replay()
-                torch.cuda.synchronize()
-                e0.record()
-                for _ in range(GRAPH_REPLAYS):
-                    gl.replay()
-                e1.record()
-                torch.cuda.synchronize()
-                ug = 1000.0 * e0.elapsed_time(e1) / (R * GRAPH_REPLAYS)
-                del gl
-            except Exception:  # capture refused: keep the eager figure
-                torch.cuda.synchronize()
-                ug = None
-        b2b_graph.append(ug)
-
-    per_layer = []
-    step_flops = 0
-    for i, l in enumerate(layers):
-        ue, ug = b2b[i], b2b_graph[i]
-        us, mode = (ug, "graph") if ug is not None and ug < ue else (ue, "eager")
-        flops, nbytes = layer_work(l, lib)
-        step_flops += flops
-        bound, tflops, gbs, frac = roofline_of(l, flops, nbytes, us * 1e-6)
-        algo, tile, grid, ks = plan_of(l, False)
-        per_layer.append({
-            "layer": l.name, "kernel": L.libconv_tile_name(tile), "grid": grid, "ksplit": ks,
-            "us": round(us, 3), "timing": mode,
-            "us_b2b": round(ue, 3), "us_graph": None if ug is None else round(ug, 3),
-            "b2b_reps": R,
-            "gflop": round(flops / 1e9, 4), "mbytes": round(nbytes / 1e6, 3),
-            "tflops": round(tflops, 3), "gbs": round(gbs, 1),
-            "bound": bound, "frac": round(frac, 4),
-        })
-
-    dom = max(range(len(layers)), key=lambda i: per_layer[i]["us"])
+    dom = max(range(len(calls)), key=lambda i: per_layer[i]["kernel_us_median"])
     dl = per_layer[dom]
     flops, nbytes = layer_work(layers[dom], lib)
     if dl["bound"] == "mfma":
@@ -433,36 +552,20 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": dl["gbs"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": dl["frac"]}
-    traffic = measured_traffic(args.workload, dl["layer"], dl["kernel"])
-    roof["traffic"] = traffic
-    roof["layer"] = dl["layer"]
-    roof["kernel"] = dl["kernel"]
-    roof["algorithmic"] = flops if dl["bound"] == "mfma" else nbytes
+    roof["traffic"] = measured_traffic(args.workload, dl["layer"], dl["kernel"])
+    roof.update({"layer": dl["layer"], "kernel": dl["kernel"],
+                 "algorithmic": flops if dl["bound"] == "mfma" else nbytes,
+                 "algorithmic_unit": "FLOP per launch" if dl["bound"] == "mfma"
+                 else "bytes per launch",
+                 "duration_us_median_cold": dl["kernel_us_median"],
+                 "timing": "hipEvents on the launch stream around each call, cold protocol"})
 
     value = step_flops / (ms_per_step * 1e-3) / 1e12
     cpu = None
     if not args.no_cpu:
-        sec, threads, runs = cpu_baseline(layers, inputs, args.cpu_budget) if chained else (None, None, None)
-        if sec is None:  # unchained workloads: each layer on its own input
-            import oracle
-            threads = oracle.threads(len(os.sched_getaffinity(0)))
-            t0 = time.perf_counter()
-            runs = 0
-            while True:  # whole steps, repeated to about the CPU budget
-                for l, (x, w, b) in zip(layers, inputs):
-                    s, p = sp(l)
-                    y, _ = oracle.conv(x.f64(), w.f64(), b.f64(), s, p, relu=l.act == "relu",
-                                       pad_t_back=l.pad_t_back)
-                    if l.pool:
-                        oracle.max_pool2x2(y)
-                runs += 1
-                if time.perf_counter() - t0 >= args.cpu_budget:
-                    break
-            sec = (time.perf_counter() - t0) / runs
-        cpu = {"value": round(step_flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-               "kind": "oracle",
-               "sample": f"the whole step ({len(layers)} layers, fp64, incl. the |x*w| sum), "
-                         f"{runs} run(s), {sec:.3f} s per step",
+        rate, threads, note = cpu_baseline(layers, inputs, args.cpu_budget, chained)
+        cpu = {"value": round(rate / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+               "kind": "oracle", "sample": note,
                "cpu": platform.processor() or platform.machine()}
 
     line = {
@@ -479,10 +582,15 @@ def main():
         "dtype": layers[0].dtype,
         "data": "synthetic (seeded; shapes and value distributions of the workload)",
         "config": {"workload": args.workload, "description": WORKLOAD_TEXT[args.workload],
-                   "chained": chained, "step_mode": mode, "graph": graph_note,
-                   "ms_per_step_eager": round(ms_eager, 5),
-                   "ms_per_step_graph": None if ms_graph is None else round(ms_graph, 5),
-                   "wall_s_timed": round(wall, 4)},
+                   "chained": chained,
+                   "timing": f"cold: {FLUSH_MB} MB scratch write before each call, outside "
+                             "the event pair; ms_per_step = median over steps of the summed "
+                             "layer times",
+                   "ms_per_step_min": round(min(step_us) / 1000.0, 5),
+                   "warm_ms_per_step_eager": round(warm_eager, 5),
+                   "warm_ms_per_step_graph": None if warm_graph is None else round(warm_graph, 5),
+                   "graph": graph_note,
+                   "wall_s_timed": round(wall_timed, 4)},
         "roofline": roof,
         "cpu_baseline": cpu,
         "layers": per_layer,

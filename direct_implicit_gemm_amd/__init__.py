@@ -29,6 +29,7 @@ STATUS = {
     0: "OK", 1: "ERR_NULL_POINTER", 2: "ERR_BAD_SHAPE", 3: "ERR_BAD_DTYPE",
     4: "ERR_BAD_ACTIVATION", 5: "ERR_ALIAS", 6: "ERR_UNSUPPORTED", 7: "ERR_NO_DEVICE",
     8: "ERR_LAUNCH", 9: "ERR_BAD_ALGO", 10: "ERR_TOO_LARGE", 11: "ERR_OUT_OF_MEMORY",
+    12: "ERR_MISALIGNED",
 }
 _ALGOS = {"auto": ALGO_AUTO, "direct": ALGO_DIRECT, "igemm": ALGO_IGEMM}
 _ACTS = {"none": ACT_NONE, "relu": ACT_RELU}
@@ -62,9 +63,17 @@ def load() -> ctypes.CDLL:
     lib.libconv_query_algo.argtypes = [I] * 18 + [ctypes.POINTER(I), ctypes.POINTER(I),
                                                   ctypes.POINTER(LL)]
     lib.libconv_query_algo.restype = I
-    lib.libconv_query_plan.argtypes = [I] * 19 + [ctypes.POINTER(I), ctypes.POINTER(I),
+    lib.libconv_query_plan.argtypes = [I] * 19 + [LL, ctypes.POINTER(I), ctypes.POINTER(I),
                                                   ctypes.POINTER(LL), ctypes.POINTER(I)]
     lib.libconv_query_plan.restype = I
+    lib.conv2d_forward_ws.argtypes = [P, P, P, P] + [I] * 13 + [P, LL, P]
+    lib.conv2d_forward_ws.restype = I
+    lib.conv3d_forward_ws.argtypes = [P, P, P, P] + [I] * 17 + [P, LL, P]
+    lib.conv3d_forward_ws.restype = I
+    lib.libconv_forward_ex.argtypes = [P, P, P, P, P] + [I] * 20 + [P, LL, P]
+    lib.libconv_forward_ex.restype = I
+    lib.libconv_workspace_size.argtypes = [I] * 20
+    lib.libconv_workspace_size.restype = LL
     lib.libconv_tile_name.argtypes = [I]
     lib.libconv_tile_name.restype = ctypes.c_char_p
     lib.libconv_tile_occupancy.argtypes = [I, I, I]
@@ -144,6 +153,38 @@ def libconv_forward_algo(x, w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW, pad
 
 
 PLAN_CAPTURING, PLAN_POOL2, PLAN_CPACK, PLAN_PACKED_W = 1, 2, 4, 8
+
+
+def conv2d_forward_ws(x, w, bias, y, N, C_in, H, W, C_out, KH, KW, pad_h, pad_w, stride_h,
+                      stride_w, dtype, act, workspace, workspace_bytes, stream) -> int:
+    return load().conv2d_forward_ws(x, w, bias, y, N, C_in, H, W, C_out, KH, KW, pad_h, pad_w,
+                                    stride_h, stride_w, dtype, act, workspace, workspace_bytes,
+                                    stream)
+
+
+def conv3d_forward_ws(x, w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW, pad_t, pad_h, pad_w,
+                      stride_t, stride_h, stride_w, dtype, act, workspace, workspace_bytes,
+                      stream) -> int:
+    return load().conv3d_forward_ws(x, w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW, pad_t,
+                                    pad_h, pad_w, stride_t, stride_h, stride_w, dtype, act,
+                                    workspace, workspace_bytes, stream)
+
+
+def libconv_forward_ex(x, w, packed_w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW,
+                       pad_t_front, pad_t_back, pad_h, pad_w, stride_t, stride_h, stride_w,
+                       dtype, act, algo, flags, workspace, workspace_bytes, stream) -> int:
+    return load().libconv_forward_ex(x, w, packed_w, bias, y, N, C_in, T, H, W, C_out, KT, KH,
+                                     KW, pad_t_front, pad_t_back, pad_h, pad_w, stride_t,
+                                     stride_h, stride_w, dtype, act, algo, flags, workspace,
+                                     workspace_bytes, stream)
+
+
+def libconv_workspace_size(N, C_in, T, H, W, C_out, KT, KH, KW, pad_t_front, pad_t_back,
+                           pad_h, pad_w, stride_t, stride_h, stride_w, dtype, act, algo,
+                           flags) -> int:
+    return load().libconv_workspace_size(N, C_in, T, H, W, C_out, KT, KH, KW, pad_t_front,
+                                         pad_t_back, pad_h, pad_w, stride_t, stride_h, stride_w,
+                                         dtype, act, algo, flags)
 
 
 def conv2d_forward_pool(x, w, bias, y, N, C_in, H, W, C_out, KH, KW, pad_h, pad_w, stride_h,
@@ -270,13 +311,13 @@ def libconv_query_algo(N, C_in, T, H, W, C_out, KT, KH, KW, pad_t, pad_h, pad_w,
 
 def libconv_query_plan(N, C_in, T, H, W, C_out, KT, KH, KW, pad_t, pad_h, pad_w,
                        stride_t, stride_h, stride_w, dtype, act, algo,
-                       capturing) -> Tuple[int, int, int, int, int]:
+                       flags, workspace_bytes=0) -> Tuple[int, int, int, int, int]:
     """Returns (status, algo, tile_id, grid, ksplit)."""
     a, t, g, k = ctypes.c_int(-1), ctypes.c_int(-1), ctypes.c_longlong(-1), ctypes.c_int(-1)
     st = load().libconv_query_plan(N, C_in, T, H, W, C_out, KT, KH, KW, pad_t, pad_h, pad_w,
-                                   stride_t, stride_h, stride_w, dtype, act, algo, capturing,
-                                   ctypes.byref(a), ctypes.byref(t), ctypes.byref(g),
-                                   ctypes.byref(k))
+                                   stride_t, stride_h, stride_w, dtype, act, algo, flags,
+                                   int(workspace_bytes), ctypes.byref(a), ctypes.byref(t),
+                                   ctypes.byref(g), ctypes.byref(k))
     return st, a.value, t.value, g.value, k.value
 
 
@@ -329,10 +370,44 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _run_ex(what, x_ptr, w, b, y_ptr, dims, pads, strides, dt, act, algo, flags, device,
+            stream, workspace):
+    """libconv_forward_ex with a workspace sized by libconv_workspace_size.
+
+    w is a device tensor (OI(D)HW) or PackedWeights; dims (N, C, T, H, W, K,
+    KT, KH, KW), pads (front, back, h, w), strides (t, h, w).  workspace: True
+    (allocate what the best plan takes, through torch), False/None (none: the
+    plan packs nothing and splits nothing), or a uint8 device tensor to use.
+    """
+    import torch
+    lib = load()
+    packed = isinstance(w, PackedWeights)
+    ws_ptr, ws_n = None, 0
+    if workspace is not None and workspace is not False:
+        need = lib.libconv_workspace_size(*dims, *pads, *strides, dt, _ACTS[act], _ALGOS[algo],
+                                          flags | (PLAN_PACKED_W if packed else 0))
+        if workspace is True:
+            if need > 0:
+                buf = torch.empty(need, dtype=torch.uint8, device=device)
+                ws_ptr, ws_n = buf.data_ptr(), need
+        else:
+            ws_ptr, ws_n = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    if stream is None:
+        stream = torch.cuda.current_stream(device).cuda_stream
+    st_ = lib.libconv_forward_ex(x_ptr, None if packed else _ptr(w),
+                                 w.data.data_ptr() if packed else None, _ptr(b), y_ptr, *dims,
+                                 *pads, *strides, dt, _ACTS[act], _ALGOS[algo], flags, ws_ptr,
+                                 ws_n, stream)
+    if st_ != 0:
+        raise LibconvError(st_, what)
+
+
 def conv_nd(x, w, b=None, stride: Union[int, Sequence[int]] = 1,
             padding: Union[int, Sequence[int]] = 0, act: str = "none", algo: str = "auto",
-            out=None, stream=None):
-    """Convolution of CUDA (HIP) tensors through libconv; 2-D or 3-D by x.ndim."""
+            out=None, stream=None, workspace=True):
+    """Convolution of CUDA (HIP) tensors through libconv; 2-D or 3-D by x.ndim.
+    workspace: True (allocate what the best plan takes), False (none, as
+    conv2d_forward / conv3d_forward), or a uint8 device tensor."""
     import torch
     nd = x.dim() - 2
     if nd not in (2, 3) or w.dim() != x.dim():
@@ -366,13 +441,8 @@ def conv_nd(x, w, b=None, stride: Union[int, Sequence[int]] = 1,
     y = torch.empty(shape, dtype=x.dtype, device=x.device) if out is None else out
     if tuple(y.shape) != shape or not y.is_contiguous() or y.dtype != x.dtype:
         raise ValueError("bad output tensor")
-    if stream is None:
-        stream = torch.cuda.current_stream(x.device).cuda_stream
-    st_ = lib.libconv_forward_algo(_ptr(x), _ptr(w), _ptr(b), _ptr(y), N, C, T, H, W, K, KT, KH,
-                                   KW, pt, ph, pw, st, sh, sw, dt, _ACTS[act], _ALGOS[algo],
-                                   stream)
-    if st_ != 0:
-        raise LibconvError(st_, "libconv_forward_algo")
+    _run_ex("libconv_forward_ex", _ptr(x), w, b, _ptr(y), (N, C, T, H, W, K, KT, KH, KW),
+            (pt, pt, ph, pw), (st, sh, sw), dt, act, algo, 0, x.device, stream, workspace)
     return y
 
 
@@ -408,8 +478,10 @@ def pack_weights(w, stream=None) -> PackedWeights:
 
 
 def conv_nd_packed(x, pw: PackedWeights, b=None, stride=1, padding=0, act="none", out=None,
-                   stream=None):
-    """Convolution with weights packed by pack_weights (never allocates in libconv)."""
+                   stream=None, workspace=None):
+    """Convolution with weights packed by pack_weights (libconv_forward_packed;
+    with a workspace (True or a tensor), libconv_forward_ex, which may split
+    the reduction)."""
     import torch
     nd = x.dim() - 2
     if pw.dtype != x.dtype or len(pw.w_shape) != x.dim():
@@ -437,15 +509,21 @@ def conv_nd_packed(x, pw: PackedWeights, b=None, stride=1, padding=0, act="none"
     y = torch.empty(shape, dtype=x.dtype, device=x.device) if out is None else out
     if stream is None:
         stream = torch.cuda.current_stream(x.device).cuda_stream
-    st_ = lib.libconv_forward_packed(x.data_ptr(), pw.data.data_ptr(), _ptr(b), y.data_ptr(), N, C,
-                                     T, H, W, K, KT, KH, KW, pt, ph, pw_, st, sh, sw,
-                                     _dtype_code(x), _ACTS[act], stream)
-    if st_ != 0:
-        raise LibconvError(st_, "libconv_forward_packed")
+    if workspace is None or workspace is False:
+        st_ = lib.libconv_forward_packed(x.data_ptr(), pw.data.data_ptr(), _ptr(b), y.data_ptr(),
+                                         N, C, T, H, W, K, KT, KH, KW, pt, ph, pw_, st, sh, sw,
+                                         _dtype_code(x), _ACTS[act], stream)
+        if st_ != 0:
+            raise LibconvError(st_, "libconv_forward_packed")
+    else:
+        _run_ex("libconv_forward_ex", x.data_ptr(), pw, b, y.data_ptr(),
+                (N, C, T, H, W, K, KT, KH, KW), (pt, pt, ph, pw_), (st, sh, sw), _dtype_code(x),
+                act, "igemm", 0, x.device, stream, workspace)
     return y
 
 
-def conv2d_pool(x, w, b=None, stride=1, padding=0, act="none", out=None, stream=None):
+def conv2d_pool(x, w, b=None, stride=1, padding=0, act="none", out=None, stream=None,
+                workspace=True):
     """2-D convolution, activation and 2x2 stride-2 max pooling in one call
     (conv2d_forward_pool); returns y [N][C_out][OH/2][OW/2]."""
     import torch
@@ -467,17 +545,14 @@ def conv2d_pool(x, w, b=None, stride=1, padding=0, act="none", out=None, stream=
     y = torch.empty(shape, dtype=x.dtype, device=x.device) if out is None else out
     if tuple(y.shape) != shape or not y.is_contiguous() or y.dtype != x.dtype:
         raise ValueError("bad output tensor")
-    if stream is None:
-        stream = torch.cuda.current_stream(x.device).cuda_stream
-    st_ = lib.conv2d_forward_pool(_ptr(x), _ptr(w), _ptr(b), _ptr(y), N, C, H, W, K, KH, KW, ph,
-                                  pw_, sh, sw, _dtype_code(x), _ACTS[act], stream)
-    if st_ != 0:
-        raise LibconvError(st_, "conv2d_forward_pool")
+    _run_ex("conv2d_forward_pool", _ptr(x), w, b, _ptr(y), (N, C, 1, H, W, K, 1, KH, KW),
+            (0, 0, ph, pw_), (1, sh, sw), _dtype_code(x), act, "auto", PLAN_POOL2, x.device,
+            stream, workspace)
     return y
 
 
 def conv3d_tpad(x, w, b=None, pad_t=(0, 0), stride=1, padding_hw=0, act="none", out=None,
-                stream=None):
+                stream=None, workspace=True):
     """3-D convolution with pad_t = (frames before, frames after); (KT-1, 0) is
     the causal convolution.  w: OIDHW device tensor or PackedWeights."""
     import torch
@@ -507,14 +582,9 @@ def conv3d_tpad(x, w, b=None, pad_t=(0, 0), stride=1, padding_hw=0, act="none", 
     y = torch.empty(shape, dtype=x.dtype, device=x.device) if out is None else out
     if tuple(y.shape) != shape or not y.is_contiguous() or y.dtype != x.dtype:
         raise ValueError("bad output tensor")
-    if stream is None:
-        stream = torch.cuda.current_stream(x.device).cuda_stream
-    st_ = lib.conv3d_forward_tpad(_ptr(x), None if packed else _ptr(w),
-                                  w.data.data_ptr() if packed else None, _ptr(b), _ptr(y),
-                                  N, C, T, H, W, K, KT, KH, KW, pf, pb, ph, pw_, st, sh, sw,
-                                  _dtype_code(x), _ACTS[act], stream)
-    if st_ != 0:
-        raise LibconvError(st_, "conv3d_forward_tpad")
+    _run_ex("conv3d_forward_tpad", _ptr(x), w, b, _ptr(y), (N, C, T, H, W, K, KT, KH, KW),
+            (pf, pb, ph, pw_), (st, sh, sw), _dtype_code(x), act, "auto", 0, x.device, stream,
+            workspace)
     return y
 
 
@@ -545,9 +615,19 @@ def conv3d_frames(x, w, b=None, T=None, out_frames=(0, 1), pad_t=(0, 0), stride=
     import torch
     packed, w_shape, (st, sh, sw), (ph, pw_), (pf, pb) = _video_args(
         x, w, b, stride, padding_hw, pad_t, "conv3d_frames", False)
-    N, C, _, H, W = x.shape
+    N, C, TX, H, W = x.shape
     K, _, KT, KH, KW = w_shape
     o0, on = int(out_frames[0]), int(out_frames[1])
+    if T is None:
+        raise ValueError("conv3d_frames: T (the whole video's frame count) is required")
+    # x must hold exactly the window the library will read for these frames:
+    # the C side takes its frame count from that window, not from x
+    wst, f0, nfr = libconv_frame_window(int(T), KT, pf, pb, st, o0, on)
+    if wst != 0:
+        raise LibconvError(wst, "libconv_frame_window")
+    if TX != nfr:
+        raise ValueError(f"conv3d_frames: x holds {TX} frames, but output frames "
+                         f"[{o0}, {o0 + on}) read the {nfr} input frames from {f0}")
     lib = load()
     oh = lib.libconv_out_size(H, KH, ph, sh)
     ow = lib.libconv_out_size(W, KW, pw_, sw)
@@ -626,7 +706,7 @@ def unpack_activations(xp: PackedActivations, out=None, stream=None):
 
 
 def conv_cpack(xp: PackedActivations, w, b=None, stride=1, padding=0, pad_t=None, act="none",
-               out=None, stream=None) -> PackedActivations:
+               out=None, stream=None, workspace=True) -> PackedActivations:
     """Convolution on channel-packed activations; returns the packed output.
     w: OI(D)HW device tensor or PackedWeights.  2-D when xp stands for NCHW.
     padding: (h, w) or (t, h, w); pad_t = (front, back) overrides the time
@@ -669,14 +749,9 @@ def conv_cpack(xp: PackedActivations, w, b=None, stride=1, padding=0, pad_t=None
                                 shape, xp.dtype)
     elif out.shape != shape or out.dtype != xp.dtype or out.data.numel() < nb:
         raise ValueError("bad output tensor")
-    if stream is None:
-        stream = torch.cuda.current_stream(xp.data.device).cuda_stream
-    st_ = lib.conv3d_forward_cpack(xp.data.data_ptr(), None if packed else _ptr(w),
-                                   w.data.data_ptr() if packed else None, _ptr(b),
-                                   out.data.data_ptr(), N, C, T, H, W, K, KT, KH, KW, pf, pb, ph,
-                                   pw_, st, sh, sw, dt, _ACTS[act], stream)
-    if st_ != 0:
-        raise LibconvError(st_, "conv3d_forward_cpack")
+    _run_ex("conv3d_forward_cpack", xp.data.data_ptr(), w, b, out.data.data_ptr(),
+            (N, C, T, H, W, K, KT, KH, KW), (pf, pb, ph, pw_), (st, sh, sw), dt, act, "auto",
+            PLAN_CPACK, xp.data.device, stream, workspace)
     return out
 
 
@@ -740,13 +815,15 @@ def conv3d_chunked(x, w, b=None, chunk_frames=17, pad_t=(0, 0), stride=1, paddin
     return out
 
 
-def conv2d(x, w, b=None, stride=1, padding=0, act="none", algo="auto", out=None, stream=None):
+def conv2d(x, w, b=None, stride=1, padding=0, act="none", algo="auto", out=None, stream=None,
+           workspace=True):
     if x.dim() != 4:
         raise ValueError("conv2d takes NCHW")
-    return conv_nd(x, w, b, stride, padding, act, algo, out, stream)
+    return conv_nd(x, w, b, stride, padding, act, algo, out, stream, workspace)
 
 
-def conv3d(x, w, b=None, stride=1, padding=0, act="none", algo="auto", out=None, stream=None):
+def conv3d(x, w, b=None, stride=1, padding=0, act="none", algo="auto", out=None, stream=None,
+           workspace=True):
     if x.dim() != 5:
         raise ValueError("conv3d takes NCDHW")
-    return conv_nd(x, w, b, stride, padding, act, algo, out, stream)
+    return conv_nd(x, w, b, stride, padding, act, algo, out, stream, workspace)

@@ -18,7 +18,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libconv.so")
-SOURCES = ["api.cpp", "direct.hip", "igemm.hip", "layout.hip"]
+SOURCES = ["api.cpp", "direct.hip", "igemm.hip", "layout.hip",
+           # the implicit-GEMM tiles, one unit per group so that they build in parallel
+           "igemm_inst_a.hip", "igemm_inst_b.hip", "igemm_inst_c.hip", "igemm_inst_d.hip",
+           "igemm_inst_e.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -61,7 +64,7 @@ def _check_stubs(lib: str) -> None:
 def build(verbose: bool = True) -> str:
     with tempfile.TemporaryDirectory(prefix="libconv_build_") as tmp:
         objs = [os.path.join(tmp, s.rsplit(".", 1)[0] + ".o") for s in SOURCES]
-        with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(SOURCES), 8)) as ex:
             list(ex.map(_compile, SOURCES, objs))
         out_tmp = LIB_PATH + ".tmp"
         cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", out_tmp, *objs]

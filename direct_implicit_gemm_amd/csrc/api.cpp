@@ -94,11 +94,21 @@ libconv_status validate(Problem& p, int algo, bool with_pointers) {
   if (xb > kMaxBytes || wb > kMaxBytes || yb > kMaxBytes) return LIBCONV_ERR_TOO_LARGE;
   const long long pb = packed_weight_bytes(p.C, p.K, p.KT, p.KH, p.KW, p.dtype);
   if (pb > kMaxBytes) return LIBCONV_ERR_TOO_LARGE;
+  if (p.ws_bytes < 0) return LIBCONV_ERR_BAD_SHAPE;
   if (with_pointers) {
     if (!p.x || !(p.w || p.wp) || !p.y) return LIBCONV_ERR_NULL_POINTER;
+    const long long bb = (long long)p.K * eb;
     if (yb > 0 && (overlaps(p.y, yb, p.x, xb) || overlaps(p.y, yb, p.w, wb) ||
-                   overlaps(p.y, yb, p.wp, pb) || overlaps(p.y, yb, p.b, (long long)p.K * eb)))
+                   overlaps(p.y, yb, p.wp, pb) || overlaps(p.y, yb, p.b, bb)))
       return LIBCONV_ERR_ALIAS;
+    if (p.ws) {
+      if ((reinterpret_cast<uintptr_t>(p.ws) & 255) != 0) return LIBCONV_ERR_MISALIGNED;
+      const long long wsb = p.ws_bytes;
+      if (overlaps(p.ws, wsb, p.x, xb) || overlaps(p.ws, wsb, p.w, wb) ||
+          overlaps(p.ws, wsb, p.wp, pb) || overlaps(p.ws, wsb, p.b, bb) ||
+          overlaps(p.ws, wsb, p.y, yb))
+        return LIBCONV_ERR_ALIAS;
+    }
   }
   return LIBCONV_OK;
 }
@@ -127,34 +137,6 @@ void init_devices() {
 bool device_ok(int d) {
   std::call_once(g_dev_once, init_devices);
   return d >= 0 && d < g_dev_count && g_dev_ok[d];
-}
-
-// Per-device pool for the stream-ordered temporaries of a call.  Its release
-// threshold keeps freed blocks cached in the pool, so once a size has been
-// used, later calls take their temporaries without a driver allocation.  If
-// the pool cannot be made, the device's default pool is used.
-std::once_flag g_pool_once[kMaxDevices];
-hipMemPool_t g_pool[kMaxDevices];
-
-hipMemPool_t device_pool(int d) {
-  std::call_once(g_pool_once[d], [d] {
-    hipMemPoolProps props;
-    std::memset(&props, 0, sizeof(props));
-    props.allocType = hipMemAllocationTypePinned;
-    props.handleTypes = hipMemHandleTypeNone;
-    props.location.type = hipMemLocationTypeDevice;
-    props.location.id = d;
-    hipMemPool_t pool = nullptr;
-    if (hipMemPoolCreate(&pool, &props) == hipSuccess) {
-      uint64_t keep = ~0ull;
-      (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
-      g_pool[d] = pool;
-    } else {
-      g_pool[d] = nullptr;
-    }
-    (void)hipGetLastError();
-  });
-  return g_pool[d];
 }
 
 // The dispatcher.  The vector-ALU direct kernel takes layers whose
@@ -218,14 +200,15 @@ libconv_status plan_for(const Problem& p, int algo, Plan* plan, bool packed_only
 // capture state, which weight forms exist, 16-byte alignment of x, compute
 // units, fused pooling).  Not used while a LIBCONV_FORCE_* override is set.
 struct PlanKey {
-  int v[27];
+  int v[28];
   bool operator==(const PlanKey& o) const { return std::memcmp(v, o.v, sizeof(v)) == 0; }
 };
 
 PlanKey plan_key(const Problem& p, int algo) {
   PlanKey k;
-  const int v[27] = {p.N, p.C, p.T, p.H, p.W, p.K, p.KT, p.KH, p.KW, p.pt, p.ph, p.pw, p.st, p.sh,
-                     p.sw, p.dtype, p.act, algo, (int)p.no_temps, p.w == nullptr,
+  const int v[28] = {p.N, p.C, p.T, p.H, p.W, p.K, p.KT, p.KH, p.KW, p.pt, p.ph, p.pw, p.st, p.sh,
+                     p.sw, p.dtype, p.act, algo, (int)(p.ws_bytes & 0x7fffffff),
+                     (int)(p.ws_bytes >> 31), p.w == nullptr,
                      (int)(reinterpret_cast<uintptr_t>(p.x) & 15), p.cus, p.wp != nullptr, p.ptb,
                      (int)p.pool, (int)p.cpack, (int)(reinterpret_cast<uintptr_t>(p.y) & 15)};
   std::memcpy(k.v, v, sizeof(v));
@@ -270,15 +253,9 @@ libconv_status run(Problem& p, int algo) {
     return LIBCONV_ERR_NO_DEVICE;
   }
   p.cus = g_dev_cus[dev];
-  // While the stream is being captured into a graph, plan without
-  // stream-ordered temporaries: an allocation recorded into a graph is not
-  // guaranteed to be mapped when the graph's kernels run.
-  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(p.stream, &cap) != hipSuccess) {
-    (void)hipGetLastError();
-    cap = hipStreamCaptureStatusNone;
-  }
-  p.no_temps = p.no_temps || cap != hipStreamCaptureStatusNone;
+  // The plan is a function of the shape, the weight forms and the workspace
+  // size only: a call recorded into a HIP graph runs the kernels the same
+  // call runs eagerly (the fixed-shape rule of capture and replay).
   Plan plan;
   st = cached_plan(p, algo, &plan);
   if (st != LIBCONV_OK) return st;
@@ -291,21 +268,7 @@ libconv_status run(Problem& p, int algo) {
                  p.KH, p.KW);
   }
   if (plan.algo == LIBCONV_ALGO_DIRECT) return direct_launch(p, plan);
-  if (!igemm_tile_packed(plan.tile) || p.wp) return igemm_launch(p, plan);
-  if (p.no_temps) return LIBCONV_ERR_UNSUPPORTED;  // never reached: planning excludes it
-  // The tile reads packed weights but the caller passed OIHW weights: pack
-  // them into a stream-ordered temporary on the call's stream (no device-wide
-  // synchronisation; recordable in a HIP graph), run, and release it.
-  const long long pb = packed_weight_bytes(p.C, p.K, p.KT, p.KH, p.KW, p.dtype);
-  void* tmp = nullptr;
-  if (stream_alloc((size_t)pb, p.stream, &tmp) != LIBCONV_OK) return LIBCONV_ERR_OUT_OF_MEMORY;
-  st = pack_launch(p.w, tmp, p.C, p.K, p.KT, p.KH, p.KW, p.dtype, p.stream);
-  if (st == LIBCONV_OK) {
-    p.wp = tmp;
-    st = igemm_launch(p, plan);
-  }
-  if (stream_free(tmp, p.stream) != LIBCONV_OK && st == LIBCONV_OK) st = LIBCONV_ERR_LAUNCH;
-  return st;
+  return igemm_launch(p, plan);
 }
 
 Problem make_problem(const void* x, const void* w, const void* bias, void* y, int N, int C_in,
@@ -323,6 +286,8 @@ Problem make_problem(const void* x, const void* w, const void* bias, void* y, in
   p.x = x; p.w = w; p.b = bias; p.y = y;
   p.stream = reinterpret_cast<hipStream_t>(stream);
   p.cus = 256;  // MI355X; the device's own count replaces it before a launch
+  p.ws = nullptr;
+  p.ws_bytes = 0;
   return p;
 }
 
@@ -346,7 +311,6 @@ libconv_status window_problem(Problem* out, const void* x, const void* w, const 
                            stream);
   p.ptb = (int)(hi - (f0 + tw));
   p.wp = packed_w;
-  p.no_temps = packed_w != nullptr;  // as libconv_forward_packed: never allocates
   *out = p;
   return LIBCONV_OK;
 }
@@ -360,6 +324,7 @@ struct ChunkPlan {
   int max_window;        // frames of the largest input window
   long long x_buf;       // bytes of one input-window buffer (256-byte multiple)
   long long y_buf;       // bytes of one output-chunk buffer (256-byte multiple)
+  long long w_buf;       // bytes for the weights packed once (0: no packed kernels)
 };
 
 libconv_status chunk_plan(int N, int C_in, int T, int H, int W, int C_out, int KT, int KH, int KW,
@@ -396,6 +361,10 @@ libconv_status chunk_plan(int N, int C_in, int T, int H, int W, int C_out, int K
   if (xb > kMaxBytes || yb > kMaxBytes) return LIBCONV_ERR_TOO_LARGE;
   cp->x_buf = (xb + 255) / 256 * 256;
   cp->y_buf = (yb + 255) / 256 * 256;
+  cp->w_buf = pack_supported(KT, KH, KW, dtype)
+                  ? (packed_weight_bytes(C_in, C_out, KT, KH, KW, dtype) + 255) / 256 * 256
+                  : 0;
+  if (cp->w_buf > kMaxBytes) cp->w_buf = 0;
   return LIBCONV_OK;
 }
 
@@ -421,34 +390,44 @@ libconv_status layout_call(const void* src, void* dst, int N, int C, int T, int 
                        reinterpret_cast<hipStream_t>(stream));
 }
 
+// Everything a convolution call can ask for, in one place: OIHW / OIDHW
+// weights (w) or packed ones (packed_w, exactly one of them), time padding
+// before and after the frames, channel-packed activations or fused pooling
+// (flags), a forced kernel family, and the caller's workspace.
+libconv_status forward_ex(const void* x, const void* w, const void* packed_w, const void* bias,
+                          void* y, int N, int C_in, int T, int H, int W, int C_out, int KT, int KH,
+                          int KW, int pad_t_front, int pad_t_back, int pad_h, int pad_w,
+                          int stride_t, int stride_h, int stride_w, int dtype, int act, int algo,
+                          int flags, void* workspace, long long workspace_bytes, void* stream) {
+  if ((w == nullptr) == (packed_w == nullptr)) return LIBCONV_ERR_NULL_POINTER;
+  Problem p = make_problem(x, w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW, pad_t_front,
+                           pad_h, pad_w, stride_t, stride_h, stride_w, dtype, act, stream);
+  p.ptb = pad_t_back;
+  p.wp = packed_w;
+  p.pool = (flags & LIBCONV_PLAN_POOL2) != 0;
+  p.cpack = (flags & LIBCONV_PLAN_CPACK) != 0;
+  p.ws = workspace;
+  p.ws_bytes = workspace ? workspace_bytes : 0;
+  if (workspace && workspace_bytes < 0) return LIBCONV_ERR_BAD_SHAPE;
+  if (packed_w && algo == LIBCONV_ALGO_DIRECT) return LIBCONV_ERR_UNSUPPORTED;
+  return run(p, packed_w ? LIBCONV_ALGO_IGEMM : algo);
+}
+
+// The plan a call with these arguments makes (no pointers are looked at);
+// flags as libconv_query_plan.
+libconv_status plan_query(Problem& p, int algo, int flags, Plan* plan) {
+  p.pool = (flags & LIBCONV_PLAN_POOL2) != 0;
+  p.cpack = (flags & LIBCONV_PLAN_CPACK) != 0;
+  const bool packed_w = (flags & LIBCONV_PLAN_PACKED_W) != 0;
+  static const char packed_marker = 0;  // planning only asks whether packed weights exist
+  if (packed_w) p.wp = &packed_marker;
+  libconv_status st = validate(p, algo, false);
+  if (st != LIBCONV_OK) return st;
+  if (packed_w && algo == LIBCONV_ALGO_DIRECT) return LIBCONV_ERR_UNSUPPORTED;
+  return plan_for(p, packed_w ? LIBCONV_ALGO_IGEMM : algo, plan, packed_w);
+}
+
 }  // namespace
-
-libconv_status stream_alloc(size_t bytes, hipStream_t stream, void** out) {
-  *out = nullptr;
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
-    (void)hipGetLastError();
-    return LIBCONV_ERR_NO_DEVICE;
-  }
-  const hipMemPool_t pool = device_pool(dev);
-  const hipError_t e = pool ? hipMallocFromPoolAsync(out, bytes, pool, stream)
-                            : hipMallocAsync(out, bytes, stream);
-  if (e != hipSuccess || !*out) {
-    (void)hipGetLastError();
-    *out = nullptr;
-    return LIBCONV_ERR_OUT_OF_MEMORY;
-  }
-  return LIBCONV_OK;
-}
-
-libconv_status stream_free(void* p, hipStream_t stream) {
-  if (!p) return LIBCONV_OK;
-  if (hipFreeAsync(p, stream) != hipSuccess) {
-    (void)hipGetLastError();
-    return LIBCONV_ERR_LAUNCH;
-  }
-  return LIBCONV_OK;
-}
 
 }  // namespace libconv
 
@@ -460,18 +439,63 @@ libconv_status conv2d_forward(const void* x, const void* w, const void* bias, vo
                               int C_in, int H, int W, int C_out, int KH, int KW, int pad_h,
                               int pad_w, int stride_h, int stride_w, int dtype, int act,
                               void* stream) {
-  Problem p = make_problem(x, w, bias, y, N, C_in, 1, H, W, C_out, 1, KH, KW, 0, pad_h, pad_w, 1,
-                           stride_h, stride_w, dtype, act, stream);
-  return run(p, LIBCONV_ALGO_AUTO);
+  return forward_ex(x, w, nullptr, bias, y, N, C_in, 1, H, W, C_out, 1, KH, KW, 0, 0, pad_h,
+                    pad_w, 1, stride_h, stride_w, dtype, act, LIBCONV_ALGO_AUTO, 0, nullptr, 0,
+                    stream);
+}
+
+libconv_status conv2d_forward_ws(const void* x, const void* w, const void* bias, void* y, int N,
+                                 int C_in, int H, int W, int C_out, int KH, int KW, int pad_h,
+                                 int pad_w, int stride_h, int stride_w, int dtype, int act,
+                                 void* workspace, long long workspace_bytes, void* stream) {
+  return forward_ex(x, w, nullptr, bias, y, N, C_in, 1, H, W, C_out, 1, KH, KW, 0, 0, pad_h,
+                    pad_w, 1, stride_h, stride_w, dtype, act, LIBCONV_ALGO_AUTO, 0, workspace,
+                    workspace_bytes, stream);
 }
 
 libconv_status conv3d_forward(const void* x, const void* w, const void* bias, void* y, int N,
                               int C_in, int T, int H, int W, int C_out, int KT, int KH, int KW,
                               int pad_t, int pad_h, int pad_w, int stride_t, int stride_h,
                               int stride_w, int dtype, int act, void* stream) {
-  Problem p = make_problem(x, w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW, pad_t, pad_h, pad_w,
-                           stride_t, stride_h, stride_w, dtype, act, stream);
-  return run(p, LIBCONV_ALGO_AUTO);
+  return forward_ex(x, w, nullptr, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW, pad_t, pad_t,
+                    pad_h, pad_w, stride_t, stride_h, stride_w, dtype, act, LIBCONV_ALGO_AUTO, 0,
+                    nullptr, 0, stream);
+}
+
+libconv_status conv3d_forward_ws(const void* x, const void* w, const void* bias, void* y, int N,
+                                 int C_in, int T, int H, int W, int C_out, int KT, int KH, int KW,
+                                 int pad_t, int pad_h, int pad_w, int stride_t, int stride_h,
+                                 int stride_w, int dtype, int act, void* workspace,
+                                 long long workspace_bytes, void* stream) {
+  return forward_ex(x, w, nullptr, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW, pad_t, pad_t,
+                    pad_h, pad_w, stride_t, stride_h, stride_w, dtype, act, LIBCONV_ALGO_AUTO, 0,
+                    workspace, workspace_bytes, stream);
+}
+
+libconv_status libconv_forward_ex(const void* x, const void* w, const void* packed_w,
+                                  const void* bias, void* y, int N, int C_in, int T, int H, int W,
+                                  int C_out, int KT, int KH, int KW, int pad_t_front,
+                                  int pad_t_back, int pad_h, int pad_w, int stride_t,
+                                  int stride_h, int stride_w, int dtype, int act, int algo,
+                                  int flags, void* workspace, long long workspace_bytes,
+                                  void* stream) {
+  return forward_ex(x, w, packed_w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW, pad_t_front,
+                    pad_t_back, pad_h, pad_w, stride_t, stride_h, stride_w, dtype, act, algo,
+                    flags, workspace, workspace_bytes, stream);
+}
+
+long long libconv_workspace_size(int N, int C_in, int T, int H, int W, int C_out, int KT, int KH,
+                                 int KW, int pad_t_front, int pad_t_back, int pad_h, int pad_w,
+                                 int stride_t, int stride_h, int stride_w, int dtype, int act,
+                                 int algo, int flags) {
+  Problem p = make_problem(nullptr, nullptr, nullptr, nullptr, N, C_in, T, H, W, C_out, KT, KH,
+                           KW, pad_t_front, pad_h, pad_w, stride_t, stride_h, stride_w, dtype,
+                           act, nullptr);
+  p.ptb = pad_t_back;
+  p.ws_bytes = 1LL << 40;  // as much as the best plan wants
+  Plan plan;
+  if (plan_query(p, algo, flags, &plan) != LIBCONV_OK) return -1;
+  return plan_workspace(p, plan);
 }
 
 libconv_status libconv_forward_algo(const void* x, const void* w, const void* bias, void* y, int N,
@@ -479,9 +503,9 @@ libconv_status libconv_forward_algo(const void* x, const void* w, const void* bi
                                     int KW, int pad_t, int pad_h, int pad_w, int stride_t,
                                     int stride_h, int stride_w, int dtype, int act, int algo,
                                     void* stream) {
-  Problem p = make_problem(x, w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW, pad_t, pad_h, pad_w,
-                           stride_t, stride_h, stride_w, dtype, act, stream);
-  return run(p, algo);
+  return forward_ex(x, w, nullptr, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW, pad_t, pad_t,
+                    pad_h, pad_w, stride_t, stride_h, stride_w, dtype, act, algo, 0, nullptr, 0,
+                    stream);
 }
 
 long long libconv_packed_weight_bytes(int C_in, int C_out, int KT, int KH, int KW, int dtype) {
@@ -517,10 +541,9 @@ libconv_status conv2d_forward_pool(const void* x, const void* w, const void* bia
                                    int C_in, int H, int W, int C_out, int KH, int KW, int pad_h,
                                    int pad_w, int stride_h, int stride_w, int dtype, int act,
                                    void* stream) {
-  Problem p = make_problem(x, w, bias, y, N, C_in, 1, H, W, C_out, 1, KH, KW, 0, pad_h, pad_w, 1,
-                           stride_h, stride_w, dtype, act, stream);
-  p.pool = true;
-  return run(p, LIBCONV_ALGO_AUTO);
+  return forward_ex(x, w, nullptr, bias, y, N, C_in, 1, H, W, C_out, 1, KH, KW, 0, 0, pad_h,
+                    pad_w, 1, stride_h, stride_w, dtype, act, LIBCONV_ALGO_AUTO,
+                    LIBCONV_PLAN_POOL2, nullptr, 0, stream);
 }
 
 libconv_status conv3d_forward_tpad(const void* x, const void* w, const void* packed_w,
@@ -528,16 +551,9 @@ libconv_status conv3d_forward_tpad(const void* x, const void* w, const void* pac
                                    int C_out, int KT, int KH, int KW, int pad_t_front,
                                    int pad_t_back, int pad_h, int pad_w, int stride_t,
                                    int stride_h, int stride_w, int dtype, int act, void* stream) {
-  if ((w == nullptr) == (packed_w == nullptr)) return LIBCONV_ERR_NULL_POINTER;
-  Problem p = make_problem(x, w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW, pad_t_front,
-                           pad_h, pad_w, stride_t, stride_h, stride_w, dtype, act, stream);
-  p.ptb = pad_t_back;
-  if (packed_w) {
-    p.wp = packed_w;
-    p.no_temps = true;  // as libconv_forward_packed: never allocates
-    return run(p, LIBCONV_ALGO_IGEMM);
-  }
-  return run(p, LIBCONV_ALGO_AUTO);
+  return forward_ex(x, w, packed_w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW, pad_t_front,
+                    pad_t_back, pad_h, pad_w, stride_t, stride_h, stride_w, dtype, act,
+                    LIBCONV_ALGO_AUTO, 0, nullptr, 0, stream);
 }
 
 libconv_status conv3d_forward_cpack(const void* x, const void* w, const void* packed_w,
@@ -546,17 +562,9 @@ libconv_status conv3d_forward_cpack(const void* x, const void* w, const void* pa
                                     int pad_t_back, int pad_h, int pad_w, int stride_t,
                                     int stride_h, int stride_w, int dtype, int act,
                                     void* stream) {
-  if ((w == nullptr) == (packed_w == nullptr)) return LIBCONV_ERR_NULL_POINTER;
-  Problem p = make_problem(x, w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW, pad_t_front,
-                           pad_h, pad_w, stride_t, stride_h, stride_w, dtype, act, stream);
-  p.ptb = pad_t_back;
-  p.cpack = true;
-  if (packed_w) {
-    p.wp = packed_w;
-    p.no_temps = true;  // as libconv_forward_packed: never allocates
-    return run(p, LIBCONV_ALGO_IGEMM);
-  }
-  return run(p, LIBCONV_ALGO_AUTO);
+  return forward_ex(x, w, packed_w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW, pad_t_front,
+                    pad_t_back, pad_h, pad_w, stride_t, stride_h, stride_w, dtype, act,
+                    LIBCONV_ALGO_AUTO, LIBCONV_PLAN_CPACK, nullptr, 0, stream);
 }
 
 long long libconv_cpack_bytes(int N, int C, int T, int H, int W, int dtype) {
@@ -624,7 +632,7 @@ long long libconv_chunked_workspace_bytes(int N, int C_in, int T, int H, int W, 
   if (chunk_plan(N, C_in, T, H, W, C_out, KT, KH, KW, pad_t_front, pad_t_back, pad_h, pad_w,
                  stride_t, stride_h, stride_w, chunk_frames, dtype, &cp) != LIBCONV_OK)
     return -1;
-  return 2 * (cp.x_buf + cp.y_buf);
+  return 2 * (cp.x_buf + cp.y_buf) + cp.w_buf;
 }
 
 libconv_status conv3d_forward_chunked(const void* x, const void* w, const void* packed_w,
@@ -643,7 +651,7 @@ libconv_status conv3d_forward_chunked(const void* x, const void* w, const void* 
                                  &cp);
   if (st != LIBCONV_OK) return st;
   if (!x || !y || !workspace) return LIBCONV_ERR_NULL_POINTER;
-  if (workspace_bytes < 2 * (cp.x_buf + cp.y_buf)) return LIBCONV_ERR_BAD_SHAPE;
+  if (workspace_bytes < 2 * (cp.x_buf + cp.y_buf) + cp.w_buf) return LIBCONV_ERR_BAD_SHAPE;
   const size_t eb = (size_t)dtype_bytes(dtype);
   const size_t x_frame = (size_t)H * W * eb, y_frame = (size_t)cp.OH * cp.OW * eb;
   const size_t x_all = (size_t)N * C_in * T * x_frame, y_all = (size_t)N * C_out * cp.OT * y_frame;
@@ -673,6 +681,28 @@ libconv_status conv3d_forward_chunked(const void* x, const void* w, const void* 
   char* ws = static_cast<char*>(workspace);
   void* xb[2] = {ws, ws + cp.x_buf};
   void* yb[2] = {ws + 2 * cp.x_buf, ws + 2 * cp.x_buf + cp.y_buf};
+  // OIDHW weights: packed once, into the workspace after the four buffers,
+  // for every chunk (the chunks then run the packed kernels), when an MFMA
+  // kernel that reads packed weights takes the chunk's shape
+  bool pack_once = false;
+  if (w && cp.w_buf > 0) {
+    static const char packed_marker = 0;  // planning only asks whether packed weights exist
+    Problem q;
+    Plan pl;
+    pack_once = window_problem(&q, xb[0], nullptr, &packed_marker, bias, yb[0], N, C_in, T, H,
+                               W, C_out, KT, KH, KW, pad_t_front, pad_t_back, pad_h, pad_w,
+                               stride_t, stride_h, stride_w, 0, chunk, dtype, act,
+                               stream) == LIBCONV_OK &&
+                validate(q, LIBCONV_ALGO_IGEMM, false) == LIBCONV_OK &&
+                plan_for(q, LIBCONV_ALGO_IGEMM, &pl, true) == LIBCONV_OK;
+  }
+  if (pack_once) {
+    void* wpk = ws + 2 * (cp.x_buf + cp.y_buf);
+    const libconv_status ps = pack_launch(w, wpk, C_in, C_out, KT, KH, KW, dtype, cs);
+    if (ps != LIBCONV_OK) return ps;
+    packed_w = wpk;
+    w = nullptr;
+  }
   // ev_in[b] / ev_conv[b] / ev_out[b]: the latest copy into xb[b], convolution
   // into yb[b], copy out of yb[b]; ev_edge: the start and the end of the call.
   hipEvent_t ev[7] = {};
@@ -780,12 +810,10 @@ libconv_status libconv_forward_packed(const void* x, const void* packed_w, const
                                       int KT, int KH, int KW, int pad_t, int pad_h, int pad_w,
                                       int stride_t, int stride_h, int stride_w, int dtype,
                                       int act, void* stream) {
-  Problem p = make_problem(x, nullptr, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW, pad_t, pad_h,
-                           pad_w, stride_t, stride_h, stride_w, dtype, act, stream);
-  p.wp = packed_w;
-  p.no_temps = true;  // this entry point never allocates: no split-K either
   if (!packed_w && x && y) return LIBCONV_ERR_NULL_POINTER;
-  return run(p, LIBCONV_ALGO_IGEMM);
+  return forward_ex(x, nullptr, packed_w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW, pad_t,
+                    pad_t, pad_h, pad_w, stride_t, stride_h, stride_w, dtype, act,
+                    LIBCONV_ALGO_IGEMM, 0, nullptr, 0, stream);
 }
 
 libconv_status libconv_query_algo(int N, int C_in, int T, int H, int W, int C_out, int KT, int KH,
@@ -794,31 +822,22 @@ libconv_status libconv_query_algo(int N, int C_in, int T, int H, int W, int C_ou
                                   int* algo_out, int* tile_out, long long* grid_out) {
   int ksplit = 1;
   return libconv_query_plan(N, C_in, T, H, W, C_out, KT, KH, KW, pad_t, pad_h, pad_w, stride_t,
-                            stride_h, stride_w, dtype, act, algo, 0, algo_out, tile_out, grid_out,
-                            &ksplit);
+                            stride_h, stride_w, dtype, act, algo, 0, 0, algo_out, tile_out,
+                            grid_out, &ksplit);
 }
 
 libconv_status libconv_query_plan(int N, int C_in, int T, int H, int W, int C_out, int KT, int KH,
                                   int KW, int pad_t, int pad_h, int pad_w, int stride_t,
                                   int stride_h, int stride_w, int dtype, int act, int algo,
-                                  int capturing, int* algo_out, int* tile_out,
-                                  long long* grid_out, int* ksplit_out) {
+                                  int flags, long long workspace_bytes, int* algo_out,
+                                  int* tile_out, long long* grid_out, int* ksplit_out) {
   if (!algo_out || !tile_out || !grid_out || !ksplit_out) return LIBCONV_ERR_NULL_POINTER;
+  if (workspace_bytes < 0) return LIBCONV_ERR_BAD_SHAPE;
   Problem p = make_problem(nullptr, nullptr, nullptr, nullptr, N, C_in, T, H, W, C_out, KT, KH, KW,
                            pad_t, pad_h, pad_w, stride_t, stride_h, stride_w, dtype, act, nullptr);
-  p.no_temps = (capturing & LIBCONV_PLAN_CAPTURING) != 0;
-  p.pool = (capturing & LIBCONV_PLAN_POOL2) != 0;
-  p.cpack = (capturing & LIBCONV_PLAN_CPACK) != 0;
-  const bool packed_w = (capturing & LIBCONV_PLAN_PACKED_W) != 0;
-  static const char packed_marker = 0;  // planning only asks whether packed weights exist
-  if (packed_w) {  // as the calls that take packed weights
-    p.no_temps = true;
-    p.wp = &packed_marker;
-  }
-  libconv_status st = validate(p, algo, false);
-  if (st != LIBCONV_OK) return st;
+  p.ws_bytes = workspace_bytes;
   Plan plan;
-  st = plan_for(p, packed_w ? LIBCONV_ALGO_IGEMM : algo, &plan, packed_w);
+  const libconv_status st = plan_query(p, algo, flags, &plan);
   if (st != LIBCONV_OK) return st;
   *algo_out = plan.algo;
   *tile_out = plan.tile;
@@ -884,7 +903,8 @@ const char* libconv_status_string(int status) {
     case LIBCONV_ERR_LAUNCH: return "kernel launch failed";
     case LIBCONV_ERR_BAD_ALGO: return "bad algorithm";
     case LIBCONV_ERR_TOO_LARGE: return "tensor too large";
-    case LIBCONV_ERR_OUT_OF_MEMORY: return "out of device memory for packed weights";
+    case LIBCONV_ERR_OUT_OF_MEMORY: return "out of device memory";
+    case LIBCONV_ERR_MISALIGNED: return "a pointer is not aligned as the call requires";
     default: return "unknown status";
   }
 }
@@ -893,6 +913,6 @@ libconv_status libconv_device_supported(int device) {
   return device_ok(device) ? LIBCONV_OK : LIBCONV_ERR_NO_DEVICE;
 }
 
-int libconv_version(void) { return 100; }
+int libconv_version(void) { return 200; }
 
 }  // extern "C"

@@ -29,7 +29,12 @@ struct Problem {
   void* y;
   hipStream_t stream;
   int cus;         // compute units of the current device (filled before a launch)
-  bool no_temps;   // plan without stream-ordered temporaries (the stream is capturing)
+  // Caller-owned device workspace (256-byte aligned) for a plan that packs
+  // OIHW weights per call or splits the reduction (split-K partial sums);
+  // ws_bytes == 0 (ws null): neither.  Plans depend on ws_bytes, never on
+  // whether the stream is being captured into a graph.
+  void* ws;
+  long long ws_bytes;
   bool pool;       // y is the 2x2 stride-2 max pool of the activated conv output (2-D only)
   // x and y are channel-packed: [N][ceil(C/g)][T][H][W][g] (g channels = 16
   // bytes, zero past C) and likewise y over C_out; else plain NC(T)HW
@@ -44,11 +49,10 @@ struct Plan {
   int ksplit = 1;   // MFMA tiles: workgroups sharing one tile's reduction (split-K)
 };
 
-// Device memory for one call's temporaries (packed weights, split-K partial
-// sums), ordered on `stream`: taken from a per-device pool that keeps freed
-// memory cached, so calls after the first do not go to the driver.
-libconv_status stream_alloc(size_t bytes, hipStream_t stream, void** out);
-libconv_status stream_free(void* p, hipStream_t stream);
+// Workspace bytes a plan needs: the packed copy of OIHW weights when the
+// tile reads packed weights and the caller passed OIHW ones, then (256-byte
+// aligned) the fp32 partial sums of a split-K plan.  0 for direct plans.
+long long plan_workspace(const Problem& p, const Plan& plan);
 
 inline int dtype_bytes(int dt) { return dt == LIBCONV_F32 ? 4 : 2; }
 

@@ -25,22 +25,26 @@
  *               libconv keeps no pointer after the call returns, copies
  *               nothing between host and device and never synchronises the
  *               host.
- *   Memory      libconv_pack_weights allocates nothing.  A convolution
- *               call may take one stream-ordered temporary: the packed copy
- *               of OIHW weights when the dispatcher runs the shape on packed
- *               weights, or the fp32 partial sums of a split-K plan.  It is
- *               taken from and returned to a per-device pool on `stream`
- *               (no device-wide synchronisation; the pool keeps freed memory
- *               cached, so calls after the first do not reach the driver).
+ *   Memory      no call allocates device memory, and none keeps any
+ *               between calls (the page "PP-OCR on Vulkan compute shaders",
+ *               section 5.2, lists small per-operation allocations among the
+ *               costs to remove).  Device memory beyond the operands comes
+ *               from the caller, as a workspace (the *_ws calls and
+ *               libconv_forward_ex): a plan may pack OIHW weights into it
+ *               once per call, for the kernels that copy packed weights
+ *               straight into on-chip memory, and keep the fp32 partial sums
+ *               of a split reduction (split-K) there.  Without a workspace
+ *               (NULL, or the calls without one) a plan does neither.
+ *               libconv_workspace_size gives the bytes the best plan uses.
  *   Stream      work is enqueued on `stream` (a hipStream_t; NULL means the
  *               null stream) and the call returns as soon as it is enqueued.
  *               Inputs must stay valid until the stream reaches the kernel.
  *               The calls make no host sync, so they may be recorded into a
- *               HIP graph.  While `stream` is capturing, the dispatcher
- *               picks plans that need no temporary (no split-K, no per-call
- *               weight packing), so a captured call may run a different
- *               kernel than the same call made eagerly; pass packed weights
- *               (libconv_forward_packed) to keep the packed MFMA kernels.
+ *               HIP graph, and the plan depends only on the shape, the
+ *               weight form and the workspace size: a captured call runs the
+ *               same kernels as the same call made eagerly (grid, block and
+ *               addresses fixed at capture, the rule of capture and replay
+ *               in "SDXL UNet under CUDA Graph", sections 2.2-2.3).
  *   Dtypes      x, w, bias and y share one storage dtype (libconv_dtype).
  *               Products and sums are formed in fp32 (fp16/bf16 products are
  *               exact in fp32) and y is rounded once, to nearest even.
@@ -93,7 +97,8 @@ typedef enum {
   LIBCONV_ERR_LAUNCH = 8,         /* the kernel launch failed */
   LIBCONV_ERR_BAD_ALGO = 9,       /* algo is not a libconv_algo */
   LIBCONV_ERR_TOO_LARGE = 10,     /* a tensor (or the packed weights) spans 2^31 bytes or more */
-  LIBCONV_ERR_OUT_OF_MEMORY = 11  /* the stream-ordered temporary for packed weights failed */
+  LIBCONV_ERR_OUT_OF_MEMORY = 11, /* not returned by this version (no call allocates) */
+  LIBCONV_ERR_MISALIGNED = 12     /* a workspace is not 256-byte aligned */
 } libconv_status;
 
 /*
@@ -130,6 +135,74 @@ libconv_status conv3d_forward(const void* x, const void* w, const void* bias, vo
                               int pad_t, int pad_h, int pad_w,
                               int stride_t, int stride_h, int stride_w,
                               int dtype, int act, void* stream);
+
+/*
+ * conv2d_forward / conv3d_forward with a caller-owned device workspace
+ * (`workspace`, 256-byte aligned, `workspace_bytes` long; NULL means none).
+ * With room enough the dispatcher may pack the OIHW / OIDHW weights into the
+ * workspace on this call (for the kernels that read packed weights) and
+ * split the reduction over several workgroups, keeping their fp32 partial
+ * sums there; libconv_workspace_size says how much the best plan takes, and
+ * with less the dispatcher picks the best plan that fits.  The workspace
+ * must not overlap x, w, bias or y; its contents on entry do not matter and
+ * are undefined after the call.  Calls that share a workspace must be
+ * ordered (one stream, or events).  Errors as conv2d_forward, plus
+ * LIBCONV_ERR_MISALIGNED and LIBCONV_ERR_ALIAS for the workspace.
+ */
+libconv_status conv2d_forward_ws(const void* x, const void* w, const void* bias, void* y,
+                                 int N, int C_in, int H, int W, int C_out, int KH, int KW,
+                                 int pad_h, int pad_w, int stride_h, int stride_w,
+                                 int dtype, int act, void* workspace, long long workspace_bytes,
+                                 void* stream);
+libconv_status conv3d_forward_ws(const void* x, const void* w, const void* bias, void* y,
+                                 int N, int C_in, int T, int H, int W,
+                                 int C_out, int KT, int KH, int KW,
+                                 int pad_t, int pad_h, int pad_w,
+                                 int stride_t, int stride_h, int stride_w,
+                                 int dtype, int act, void* workspace, long long workspace_bytes,
+                                 void* stream);
+
+/* Flags of libconv_forward_ex, libconv_workspace_size and libconv_query_plan. */
+enum {
+  LIBCONV_PLAN_CAPTURING = 1,  /* accepted and ignored: plans do not depend on graph capture */
+  LIBCONV_PLAN_POOL2 = 2,      /* conv2d_forward_pool: 2x2 max pooling fused after the activation */
+  LIBCONV_PLAN_CPACK = 4,      /* channel-packed activations (conv3d_forward_cpack) */
+  LIBCONV_PLAN_PACKED_W = 8    /* (queries only) the call passes packed weights */
+};
+
+/*
+ * Every convolution this library computes, with every option: exactly one
+ * of w (OIHW / OIDHW) and packed_w (libconv_pack_weights; then only the
+ * MFMA kernels run); the frame axis padded by pad_t_front zero frames before
+ * the first frame and pad_t_back after the last (as conv3d_forward_tpad);
+ * flags LIBCONV_PLAN_POOL2 (as conv2d_forward_pool; 2-D only) or
+ * LIBCONV_PLAN_CPACK (channel-packed x and y, as conv3d_forward_cpack);
+ * algo a libconv_algo; a workspace as conv3d_forward_ws.  The other calls
+ * are this one with some arguments fixed.  2-D: T = KT = 1, time pads 0,
+ * stride_t = 1.
+ */
+libconv_status libconv_forward_ex(const void* x, const void* w, const void* packed_w,
+                                  const void* bias, void* y,
+                                  int N, int C_in, int T, int H, int W,
+                                  int C_out, int KT, int KH, int KW,
+                                  int pad_t_front, int pad_t_back, int pad_h, int pad_w,
+                                  int stride_t, int stride_h, int stride_w,
+                                  int dtype, int act, int algo, int flags,
+                                  void* workspace, long long workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes the best plan for libconv_forward_ex with these
+ * arguments uses (0 when it uses none; flags as libconv_forward_ex, plus
+ * LIBCONV_PLAN_PACKED_W for a call given packed weights), or -1 for
+ * arguments the call would reject.  Pure host arithmetic: works without a
+ * GPU.  The answer is fixed for a shape, so it can be allocated once per
+ * layer.
+ */
+long long libconv_workspace_size(int N, int C_in, int T, int H, int W,
+                                 int C_out, int KT, int KH, int KW,
+                                 int pad_t_front, int pad_t_back, int pad_h, int pad_w,
+                                 int stride_t, int stride_h, int stride_w,
+                                 int dtype, int act, int algo, int flags);
 
 /*
  * 3-D convolution with an explicit kernel family (libconv_algo).  With
@@ -172,7 +245,7 @@ libconv_status libconv_pack_weights(const void* w, void* packed, long long packe
 
 /*
  * conv3d_forward with packed weights (from libconv_pack_weights) in place of
- * w; always an implicit GEMM on the matrix cores, never allocates.  Returns
+ * w; always an implicit GEMM on the matrix cores; no workspace (no split).  Returns
  * LIBCONV_ERR_UNSUPPORTED when no packed kernel fits the shape.  A 2-D
  * convolution is the case T = KT = 1, pad_t = 0, stride_t = 1.
  */
@@ -211,8 +284,9 @@ libconv_status conv2d_forward_pool(const void* x, const void* w, const void* bia
  * floor((T + pad_t_front + pad_t_back - KT) / stride_t) + 1.
  * Weights: exactly one of w (OIDHW, as conv3d_forward; the dispatcher picks
  * the kernel) and packed_w (from libconv_pack_weights, as
- * libconv_forward_packed: MFMA kernels only, never allocates); the other is
- * NULL, else LIBCONV_ERR_NULL_POINTER.  Pads must be >= 0.
+ * libconv_forward_packed: MFMA kernels only); the other is NULL, else
+ * LIBCONV_ERR_NULL_POINTER.  No workspace (libconv_forward_ex takes one).
+ * Pads must be >= 0.
  */
 libconv_status conv3d_forward_tpad(const void* x, const void* w, const void* packed_w,
                                    const void* bias, void* y,
@@ -255,10 +329,13 @@ libconv_status libconv_unpack_activations(const void* x_packed, void* x, int N, 
  * zeros past C_out.  The channels past C_in in x must be finite (they meet
  * zero weights; pack_activations and this call write zeros there).  Both
  * must be 16-byte aligned.  Weights and bias as conv3d_forward_tpad (exactly
- * one of w and packed_w; with packed_w only the MFMA kernels run and nothing
- * is allocated).  2-D: T = KT = 1, time pads 0.  The MFMA kernels for this
- * layout cover 3x3x3 and 3x3 (stride 1), 3x3 stride 2 and 1x1; other shapes
- * run on the vector-ALU kernel (not with packed_w: LIBCONV_ERR_UNSUPPORTED).
+ * one of w and packed_w; with packed_w only the MFMA kernels run).  2-D:
+ * T = KT = 1, time pads 0.  The MFMA kernels for this layout read packed
+ * weights and cover 3x3x3 and 3x3 (stride 1), 3x3 stride 2 and 1x1; with
+ * OIDHW weights they run only when libconv_forward_ex (flag
+ * LIBCONV_PLAN_CPACK) is given a workspace to pack them into, else the
+ * vector-ALU kernel runs.  Without an MFMA kernel for the shape, packed_w is
+ * LIBCONV_ERR_UNSUPPORTED.
  */
 libconv_status conv3d_forward_cpack(const void* x, const void* w, const void* packed_w,
                                     const void* bias, void* y,
@@ -311,7 +388,8 @@ libconv_status conv3d_forward_frames(const void* x, const void* w, const void* p
 
 /*
  * Device workspace conv3d_forward_chunked needs: two input-window and two
- * output-chunk buffers.  -1 if the arguments are invalid for it.
+ * output-chunk buffers, and room for the weights packed once.  -1 if the
+ * arguments are invalid for it.
  */
 long long libconv_chunked_workspace_bytes(int N, int C_in, int T, int H, int W,
                                           int C_out, int KT, int KH, int KW,
@@ -337,8 +415,9 @@ long long libconv_chunked_workspace_bytes(int N, int C_in, int T, int H, int W,
  * work already on `stream`, and `stream` waits for the last of them.
  * copy_out_stream NULL: outputs are copied on copy_in_stream; both NULL:
  * everything runs in order on `stream`.  Weights and bias are on the device;
- * exactly one of w and packed_w (with OIDHW weights a packed kernel packs
- * them per chunk: pass packed weights for long videos).  Requires
+ * exactly one of w and packed_w (OIDHW weights of a kernel size the packed
+ * kernels take are packed once, into the workspace, before the first
+ * chunk).  Requires
  * pad_t_front < KT and pad_t_back < KT (every output frame reads an input
  * frame).  LIBCONV_ERR_UNSUPPORTED while either stream is being captured
  * into a graph; a too-small workspace is LIBCONV_ERR_BAD_SHAPE.  The call
@@ -357,7 +436,9 @@ libconv_status conv3d_forward_chunked(const void* x, const void* w, const void* 
                                       void* copy_out_stream);
 
 /*
- * Which kernel the dispatcher would launch for this shape, without launching.
+ * Which kernel the dispatcher would launch for this shape, without launching
+ * (the per-layer "generic implementation or not?" check of "OpenCL-101
+ * issue 52").
  * Arguments as for libconv_forward_algo (algo may force a family).  On
  * LIBCONV_OK: *algo_out is LIBCONV_ALGO_DIRECT or LIBCONV_ALGO_IGEMM,
  * *tile_out the tile configuration id (see libconv_tile_name) and
@@ -371,33 +452,23 @@ libconv_status libconv_query_algo(int N, int C_in, int T, int H, int W,
                                   int dtype, int act, int algo,
                                   int* algo_out, int* tile_out, long long* grid_out);
 
-/* Flags of libconv_query_plan. */
-enum {
-  LIBCONV_PLAN_CAPTURING = 1,  /* the call is made while its stream is captured into a graph */
-  LIBCONV_PLAN_POOL2 = 2,      /* the call is conv2d_forward_pool */
-  LIBCONV_PLAN_CPACK = 4,      /* the call is conv3d_forward_cpack (channel-packed activations) */
-  LIBCONV_PLAN_PACKED_W = 8    /* the call passes packed weights (libconv_forward_packed, or
-                                  packed_w of the _tpad / _cpack / _frames calls) */
-};
-
 /*
- * libconv_query_algo with two more facts about the plan: *ksplit_out, the
+ * libconv_query_algo with more facts about the plan: *ksplit_out, the
  * number of workgroups that share one output tile's reduction (split-K; 1 =
- * none), and, with LIBCONV_PLAN_CAPTURING in `capturing`, the plan for a call
- * made while its stream is being captured into a HIP graph (such a call takes
- * no stream-ordered temporaries: no split-K and no per-call weight packing,
- * so it can run another kernel than the same call made eagerly); with
- * LIBCONV_PLAN_POOL2, the plan of conv2d_forward_pool; with
- * LIBCONV_PLAN_CPACK, the plan of conv3d_forward_cpack; with
- * LIBCONV_PLAN_PACKED_W, the plan of a call given packed weights (MFMA
- * tiles that read them, no temporaries).  Pure host
- * arithmetic: works without a GPU.  Output pointers may not be NULL.
+ * none), for a call given a workspace of workspace_bytes (0: none);
+ * `flags` as libconv_forward_ex (LIBCONV_PLAN_POOL2: conv2d_forward_pool;
+ * LIBCONV_PLAN_CPACK: channel-packed activations), plus
+ * LIBCONV_PLAN_PACKED_W for a call given packed weights (MFMA tiles that
+ * read them).  LIBCONV_PLAN_CAPTURING changes nothing: a call plans the same
+ * way whether or not its stream is being captured.  Pure host arithmetic:
+ * works without a GPU.  Output pointers may not be NULL.
  */
 libconv_status libconv_query_plan(int N, int C_in, int T, int H, int W,
                                   int C_out, int KT, int KH, int KW,
                                   int pad_t, int pad_h, int pad_w,
                                   int stride_t, int stride_h, int stride_w,
-                                  int dtype, int act, int algo, int capturing,
+                                  int dtype, int act, int algo, int flags,
+                                  long long workspace_bytes,
                                   int* algo_out, int* tile_out, long long* grid_out,
                                   int* ksplit_out);
 
@@ -421,11 +492,16 @@ libconv_status libconv_fold_batchnorm(const float* w, const float* b, const floa
                                       float eps, int C_out, int k_per_out,
                                       float* w_out, float* b_out);
 
-/* Human-readable name of a tile configuration id; "?" if unknown. */
+/* Human-readable name of a tile configuration id; "?" if unknown.  With
+ * libconv_query_algo this answers the question the per-operator profiler of
+ * "OpenCL-101 issue 52" asks of every layer: which implementation (a tuned
+ * kernel or a generic one) a Conv actually runs. */
 const char* libconv_tile_name(int tile_id);
 
 /* Workgroups one compute unit holds at once for an MFMA tile configuration
- * and dtype: with measured = 0, the figure the dispatcher's cost model uses
+ * and dtype (the per-operator, per-device workgroup sizing that "PP-OCR on
+ * Vulkan compute shaders", section 4.4, tunes by hand; here a property of
+ * each built tile): with measured = 0, the figure the dispatcher's cost model uses
  * (pure host, works without a GPU); with measured != 0, the HIP runtime's
  * occupancy query for the built kernel on the current device.  -1 for an
  * unknown tile id, a dtype the tile does not run, or (measured) no gfx950
@@ -433,21 +509,32 @@ const char* libconv_tile_name(int tile_id);
 int libconv_tile_occupancy(int tile_id, int dtype, int measured);
 
 /* floor((in + 2*pad - k) / stride) + 1, or -1 if an argument is out of range
- * (in < 1, k < 1, pad < 0, stride < 1) or the window does not fit. */
+ * (in < 1, k < 1, pad < 0, stride < 1) or the window does not fit.  The
+ * conv shader of "PP-OCR on Vulkan compute shaders", section 2.2, takes the
+ * output extents as inputs without a formula; this is the only rule that
+ * gives that page's detector's 640 -> 320 -> 160 at kernel 3, pad 1,
+ * stride 2. */
 int libconv_out_size(int in, int k, int pad, int stride);
 
 /* The same with pad_lo before and pad_hi after the input (the frame axis of
  * conv3d_forward_tpad): floor((in + pad_lo + pad_hi - k) / stride) + 1, or -1. */
 int libconv_out_size2(int in, int k, int pad_lo, int pad_hi, int stride);
 
-/* Static description of a status code; never NULL. */
+/* Static description of a status code; never NULL.  Failures are reported,
+ * never turned into an abort (the fault-tolerant backend bring-up of
+ * "OpenCL-101 issue 52"). */
 const char* libconv_status_string(int status);
 
 /* LIBCONV_OK if `device` exists and is a gfx950 GPU, else LIBCONV_ERR_NO_DEVICE.
- * Never aborts; safe on a host without any GPU. */
+ * Never aborts; safe on a host without any GPU: the "is this backend
+ * usable" query that "OpenCL-101 issue 52" adds so that a caller can pick
+ * another path instead of crashing during initialisation. */
 libconv_status libconv_device_supported(int device);
 
-/* Library version as 10000*major + 100*minor + patch. */
+/* Library version as 10000*major + 100*minor + patch, so that a caller can
+ * check that the library it loaded is the one it was built against (the
+ * build and output-contract checks "SeedVR2 NCNN Vulkan", section 3.6,
+ * adds after a layer silently ran elsewhere). */
 int libconv_version(void);
 
 #ifdef __cplusplus

@@ -193,21 +193,6 @@ def conv_points(x: np.ndarray, w: np.ndarray, b: Optional[np.ndarray],
     return y, s
 
 
-def output_shape(x_shape, w_shape, stride=1, pad=0):
-    """Shape of y for the given operand shapes (the oracle's own extents)."""
-    nd = len(x_shape) - 2
-    s3 = _norm3(stride, nd)
-    p3 = _norm3(pad, nd)
-    if nd == 2:
-        o = (out_extent(x_shape[2], w_shape[2], p3[1], s3[1]),
-             out_extent(x_shape[3], w_shape[3], p3[2], s3[2]))
-    else:
-        o = (out_extent(x_shape[2], w_shape[2], p3[0], s3[0]),
-             out_extent(x_shape[3], w_shape[3], p3[1], s3[1]),
-             out_extent(x_shape[4], w_shape[4], p3[2], s3[2]))
-    return (x_shape[0], w_shape[0]) + o
-
-
 def fold_batchnorm(w: np.ndarray, b: Optional[np.ndarray], gamma: np.ndarray, beta: np.ndarray,
                    mean: np.ndarray, var: np.ndarray, eps: float) -> Tuple[np.ndarray, np.ndarray]:
     """Batch normalisation folded into the convolution before it, in fp64 (the

@@ -160,13 +160,32 @@ def test_forward_packed_validation():
                                     4, 0, None) == 3
 
 
-def test_3d_layers_dispatch_to_packed_tiles():
-    for name in ("c5_A", "c5_B"):
-        l = W.ALL_LAYERS[name]
-        st, algo, tile, grid = L.libconv_query_algo(
-            l.N, l.C_in, l.T, l.H, l.W, l.C_out, l.KT, l.KH, l.KW, *l.pad, *l.stride,
+def _layer_args(name):
+    l = W.ALL_LAYERS[name]
+    return (l.N, l.C_in, l.T, l.H, l.W, l.C_out, l.KT, l.KH, l.KW, *l.pad, *l.stride,
             W.DTYPE_CODE[l.dtype], W.ACT_CODE[l.act], L.ALGO_AUTO)
-        assert st == 0 and L.libconv_tile_name(tile).startswith("igemm16p_")
+
+
+def _ws_size(name, flags=0):
+    l = W.ALL_LAYERS[name]
+    return L.libconv_workspace_size(l.N, l.C_in, l.T, l.H, l.W, l.C_out, l.KT, l.KH, l.KW,
+                                    l.pad[0], l.pad[0], l.pad[1], l.pad[2], *l.stride,
+                                    W.DTYPE_CODE[l.dtype], W.ACT_CODE[l.act], L.ALGO_AUTO, flags)
+
+
+def test_3d_layers_dispatch_to_mfma_tiles_with_and_without_workspace():
+    """conv3d_forward (no workspace) runs the video-VAE layers on the MFMA
+    tiles that read OIDHW weights; given the workspace libconv_workspace_size
+    names, on the tiles that read weights packed into it."""
+    for name in ("c5_A", "c5_B"):
+        args = _layer_args(name)
+        st, algo, tile, grid = L.libconv_query_algo(*args)
+        assert st == 0 and algo == L.ALGO_IGEMM
+        assert L.libconv_tile_name(tile).startswith("igemm16_k333"), L.libconv_tile_name(tile)
+        ws = _ws_size(name)
+        assert ws > 0
+        st, algo, tile, grid, ks = L.libconv_query_plan(*args, 0, ws)
+        assert st == 0 and L.libconv_tile_name(tile).startswith("igemm16p_k333")
 
 
 def test_tile_occupancy_query_without_gpu():
@@ -186,28 +205,78 @@ def test_tile_occupancy_query_without_gpu():
                 assert occ == -1, (name, dt, occ)
 
 
-def test_query_plan_capture_excludes_temporaries():
-    """Under graph capture the plan takes no stream-ordered temporaries: no
-    split-K and no packed tile fed from OIHW weights; eagerly the same calls
-    may use both.  The eager plan agrees with libconv_query_algo."""
-    for name in ("c4_B", "c5_A", "c2_L2", "c3_B"):
-        l = W.ALL_LAYERS[name]
-        args = (l.N, l.C_in, l.T, l.H, l.W, l.C_out, l.KT, l.KH, l.KW, *l.pad, *l.stride,
-                W.DTYPE_CODE[l.dtype], W.ACT_CODE[l.act], L.ALGO_AUTO)
-        st, algo, tile, grid, ks = L.libconv_query_plan(*args, 0)
-        assert st == 0 and ks >= 1
-        assert L.libconv_query_algo(*args)[1:] == (algo, tile, grid)
-        st, calgo, ctile, cgrid, cks = L.libconv_query_plan(*args, 1)
-        assert st == 0 and cks == 1, (name, cks)
-        name_c = L.libconv_tile_name(ctile)
-        assert "16p" not in name_c and "32p" not in name_c, (name, name_c)
-    # the UNet 1280-channel layer splits eagerly (few tiles for the CUs)
+CONFIG_LAYERS = ("c1", "c2_L1", "c2_L2", "c2_L3", "c2_L4", "c3_A", "c3_B", "c4_A", "c4_B",
+                 "c5_A", "c5_B")
+
+
+@pytest.mark.parametrize("name", CONFIG_LAYERS)
+def test_query_plan_does_not_depend_on_capture(name):
+    """A call plans the same kernel, grid and split whether or not its stream
+    is being captured into a graph, with no workspace and with the one
+    libconv_workspace_size names; the no-workspace plan agrees with
+    libconv_query_algo and neither packs weights nor splits."""
+    args = _layer_args(name)
+    ws = _ws_size(name)
+    assert ws >= 0
+    for wsb in (0, ws):
+        eager = L.libconv_query_plan(*args, 0, wsb)
+        captured = L.libconv_query_plan(*args, L.PLAN_CAPTURING, wsb)
+        assert eager[0] == 0 and eager == captured, (name, wsb, eager, captured)
+    st, algo, tile, grid, ks = L.libconv_query_plan(*args, 0, 0)
+    assert L.libconv_query_algo(*args)[1:] == (algo, tile, grid)
+    assert ks == 1
+    nm = L.libconv_tile_name(tile)
+    assert "16p" not in nm and "32p" not in nm, (name, nm)
+    # the best plan fits exactly the workspace it asked for, and more changes nothing
+    assert L.libconv_query_plan(*args, 0, ws) == L.libconv_query_plan(*args, 0, ws + (1 << 30))
+
+
+def test_workspace_enables_split_and_packing():
+    """The UNet 1280-channel layer (few tiles for the CUs) splits its reduction
+    when given a workspace; the partial sums and the packed weights are what
+    the workspace holds."""
+    args = _layer_args("c4_B")
+    ws = _ws_size("c4_B")
+    st, algo, tile, grid, ks = L.libconv_query_plan(*args, 0, ws)
+    assert st == 0 and ks > 1
     l = W.ALL_LAYERS["c4_B"]
-    args = (l.N, l.C_in, l.T, l.H, l.W, l.C_out, l.KT, l.KH, l.KW, *l.pad, *l.stride,
-            W.DTYPE_CODE[l.dtype], W.ACT_CODE[l.act], L.ALGO_AUTO)
-    assert L.libconv_query_plan(*args, 0)[4] > 1
-    out = L.libconv_query_plan(1, 4, 1, 8, 8, 8, 1, 3, 3, 0, 1, 1, 1, 1, 1, 5, 0, 0, 0)
+    partials = ks * l.N * l.C_out * l.H * l.W * 4
+    packed = L.libconv_packed_weight_bytes(l.C_in, l.C_out, 1, 3, 3, L.BF16)
+    want = (-(-packed // 256) * 256 if "16p" in L.libconv_tile_name(tile) else 0) \
+        + -(-partials // 256) * 256
+    assert ws == want
+    # a workspace too small for the split: the best plan that fits
+    st2, _, tile2, _, ks2 = L.libconv_query_plan(*args, 0, ws - 256)
+    assert st2 == 0 and (ks2, tile2) != (ks, tile)
+    out = L.libconv_query_plan(1, 4, 1, 8, 8, 8, 1, 3, 3, 0, 1, 1, 1, 1, 1, 5, 0, 0, 0, 0)
     assert out[0] == 3  # bad dtype
+    assert L.libconv_query_plan(*args, 0, -1)[0] == 2
+    assert L.libconv_workspace_size(1, 4, 1, 8, 8, 8, 1, 3, 3, 0, 0, 1, 1, 1, 1, 1, 5, 0, 0,
+                                    0) == -1
+    # layers that need nothing (the vector-ALU stem) ask for nothing
+    assert _ws_size("c2_L1") == 0
+
+
+def test_workspace_argument_errors_without_gpu():
+    """Workspace checks come before any device access: a workspace that is not
+    256-byte aligned, that overlaps an operand, or a negative size."""
+    fake = 1 << 40
+    y = fake + (1 << 32)
+    ws = fake + (1 << 34)
+    geo = (1, 16, 5, 8, 32, 24, 3, 3, 3, 1, 1, 1, 1, 1, 1, 1)
+    ex = lambda x, w, pw, yy, wsp, wsb, flags=0: L.libconv_forward_ex(
+        x, w, pw, None, yy, 1, 16, 5, 8, 32, 24, 3, 3, 3, 1, 1, 1, 1, 1, 1, 1, L.F16, 0,
+        L.ALGO_AUTO, flags, wsp, wsb, None)
+    assert ex(fake, fake + 64, None, y, ws + 16, 1 << 20) == 12
+    assert ex(fake, fake + 64, None, y, y, 1 << 20) == 5
+    assert ex(fake, fake + 64, None, y, ws, -5) == 2
+    assert ex(fake, fake + 64, fake + 64, y, ws, 1 << 20) == 1
+    assert ex(fake, fake + 64, None, y, ws, 1 << 20) == 7  # valid: reaches the device check
+    assert ex(fake, fake + 64, None, y, None, 0) == 7
+    assert L.conv3d_forward_ws(fake, fake + 64, None, y, *geo[:6], 3, 3, 3, 1, 1, 1, 1, 1, 1,
+                               L.F16, 0, ws + 8, 1 << 20, None) == 12
+    assert L.conv2d_forward_ws(fake, fake + 64, None, y, 1, 16, 8, 32, 24, 3, 3, 1, 1, 1, 1,
+                               L.F16, 0, ws, 1 << 20, None) == 7
 
 
 def test_out_size2_matches_oracle():
@@ -315,12 +384,21 @@ def test_cpack_argument_errors_without_gpu():
 
 def test_query_plan_packed_weights_and_cpack_flags():
     """PLAN_PACKED_W plans as a call given packed weights (packed MFMA tiles,
-    no split); PLAN_CPACK plans the channel-packed layout's own tiles."""
+    no split without a workspace); PLAN_CPACK plans the channel-packed
+    layout's own tiles, which read packed weights: with OIDHW weights only
+    when a workspace can hold them packed, else the vector-ALU kernel."""
     vae = (1, 512, 5, 64, 120, 512, 3, 3, 3, 1, 1, 1, 1, 1, 1, L.F16, 1, L.ALGO_AUTO)
     st, algo, tile, grid, ks = L.libconv_query_plan(*vae, L.PLAN_PACKED_W)
     assert st == 0 and algo == L.ALGO_IGEMM and ks == 1
     assert L.libconv_tile_name(tile).startswith("igemm16p_")
     st, algo, tile, grid, ks = L.libconv_query_plan(*vae, L.PLAN_CPACK)
+    assert st == 0 and algo == L.ALGO_DIRECT
+    ws = L.libconv_workspace_size(1, 512, 5, 64, 120, 512, 3, 3, 3, 1, 1, 1, 1, 1, 1, 1,
+                                  L.F16, 1, L.ALGO_AUTO, L.PLAN_CPACK)
+    assert ws >= L.libconv_packed_weight_bytes(512, 512, 3, 3, 3, L.F16)
+    st, algo, tile, grid, ks = L.libconv_query_plan(*vae, L.PLAN_CPACK, ws)
+    assert st == 0 and L.libconv_tile_name(tile).startswith("igemm16x_")
+    st, algo, tile, grid, ks = L.libconv_query_plan(*vae, L.PLAN_CPACK | L.PLAN_PACKED_W)
     assert st == 0 and L.libconv_tile_name(tile).startswith("igemm16x_")
     # a 5x5 layer: no packed kernels at all
     k5 = (1, 16, 1, 32, 32, 16, 1, 5, 5, 0, 2, 2, 1, 1, 1, L.F16, 0, L.ALGO_AUTO)

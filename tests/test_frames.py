@@ -79,7 +79,12 @@ def _ws_expected(N, C, T, H, W, K, KT, KH, KW, pf, pb, ph, pw, st, sh, sw, chunk
         hi = min(T, (o0 + on - 1) * st - pf + KT)
         tw_max = max(tw_max, hi - lo)
     r = lambda v: -(-v // 256) * 256
-    return 2 * (r(N * C * tw_max * H * W * eb) + r(N * K * chunk * oh * ow * eb))
+    # room for the weights packed once (the packed layout of libconv.h: groups
+    # of 16 bytes of input channels, output channels padded to 128), for the
+    # kernel sizes the packed kernels take
+    taps = KT * KH * KW
+    packed = (-(-C // (16 // eb)) * taps * (-(-K // 128) * 128) * 16) if taps in (1, 9, 27) else 0
+    return 2 * (r(N * C * tw_max * H * W * eb) + r(N * K * chunk * oh * ow * eb)) + r(packed)
 
 
 @pytest.mark.parametrize("case", [

@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 import workloads as W
-from convcheck import assert_gates, metrics, to_f64
+from convcheck import BIG_WS, assert_gates, metrics, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -222,7 +222,7 @@ def test_cpack_split_k(tid, dt, ks, monkeypatch):
                         (0, 1, 1), (1, 1, 1), "relu", 2, "N01", "N01", "U0.05")
     dims = (layer.N, layer.C_in, layer.T, layer.H, layer.W, layer.C_out, layer.KT, layer.KH,
             layer.KW, *layer.pad, *layer.stride)
-    q = L.libconv_query_plan(*dims, W.DTYPE_CODE[dt], 1, 0, L.PLAN_CPACK)
+    q = L.libconv_query_plan(*dims, W.DTYPE_CODE[dt], 1, 0, L.PLAN_CPACK, BIG_WS)
     assert q[0] == 0 and q[2] == tid and q[4] == ks, q
     note(f"cpack split-K tile {tid} ks={ks}: x={layer.x_shape} w={layer.w_shape} {dt}")
     x, w, b = W.make_inputs(layer, 1300 + tid + ks)

@@ -2,9 +2,9 @@
 whose capture stream is the stream libconv enqueues on) and replayed: every
 replay, with the program's own eager work and synchronisations between
 replays, must give exactly the eager result (the kernels are deterministic,
-so bit for bit).  Covers a chained fp32 stack without temporaries and layers
-that take a stream-ordered temporary (split-K partial sums, weights packed
-per call)."""
+so bit for bit).  Covers a chained fp32 stack, layers given a workspace
+(split-K partial sums, weights packed per call) and the two north-star
+exports called directly."""
 import sys
 
 import pytest
@@ -87,13 +87,13 @@ def test_graph_chained_fp32_stack():
     _check_graph([l1, l2, l3], True, 500)
 
 
-def test_graph_layers_that_take_temporaries_eagerly(monkeypatch):
-    """Eagerly these calls take a stream-ordered temporary (split-K partial
-    sums, forced here; weights packed per call on a 3-D layer).  Under
-    capture the dispatcher plans without temporaries, so the replays run
-    other kernels: each replay must equal the first bit for bit, and both the
-    eager and the replayed results must pass the oracle gates.  A forward on
-    weights packed beforehand keeps the packed kernels inside the graph."""
+def test_graph_layers_with_a_workspace(monkeypatch):
+    """Calls given a workspace: split-K partial sums (forced here) and weights
+    packed per call on a 3-D layer, both in the workspace.  The plan does not
+    depend on capture, so the replays run the eager kernels: every replay
+    must equal the eager result bit for bit, and the eager result must pass
+    the oracle gates.  A forward on weights packed beforehand is recorded
+    alongside."""
     import direct_implicit_gemm_amd as L
     import oracle
     from convcheck import assert_gates, metrics, oracle_args, to_f64
@@ -110,12 +110,21 @@ def test_graph_layers_that_take_temporaries_eagerly(monkeypatch):
     ws = [w.torch(dev) for _, w, _ in ins]
     bs = [b.torch(dev) for _, _, b in ins]
     packed = L.pack_weights(ws[1])          # before any capture
+    # one workspace per call, allocated before capture (a model keeps its own)
+    need = []
+    for l in specs:
+        pt_ = l.pad[0]
+        need.append(L.libconv_workspace_size(l.N, l.C_in, l.T, l.H, l.W, l.C_out, l.KT, l.KH,
+                                             l.KW, pt_, pt_, l.pad[1], l.pad[2], *l.stride,
+                                             W.DTYPE_CODE[l.dtype], W.ACT_CODE[l.act], 0, 0))
+    assert need[0] > 0 and need[1] > 0, need
+    wsp = [torch.empty(n, dtype=torch.uint8, device=dev) for n in need]
     torch.cuda.synchronize()
 
     def run(outs):
         for i, l in enumerate(specs):
             st, pd = oracle_args(l)
-            L.conv_nd(xs[i], ws[i], bs[i], st, pd, l.act, out=outs[i])
+            L.conv_nd(xs[i], ws[i], bs[i], st, pd, l.act, out=outs[i], workspace=wsp[i])
         st, pd = oracle_args(specs[1])
         L.conv_nd_packed(xs[1], packed, bs[1], st, pd, specs[1].act, out=outs[2])
 
@@ -142,21 +151,75 @@ def test_graph_layers_that_take_temporaries_eagerly(monkeypatch):
     with torch.cuda.graph(g):
         run(outs)
     torch.cuda.synchronize()
-    first = None
     for r in range(4):
         for o in outs:
             o.zero_()
         g.replay()
         torch.cuda.synchronize()
-        if first is None:
-            first = [o.clone() for o in outs]
-            gates(outs, "replay 0")
-        else:
-            for i, o in enumerate(outs):
-                assert torch.equal(o, first[i]), f"replay {r}, output {i} differs from replay 0"
-        run(fresh())  # the program's own eager work between replays (with temporaries)
+        for i, o in enumerate(outs):
+            assert torch.equal(o, eager[i]), f"replay {r}, output {i} differs from eager"
+        run(fresh())  # the program's own eager work between replays (same workspaces)
         torch.cuda.synchronize()
         note(f"replay {r} ok")
+
+
+def test_graph_north_star_entry_points():
+    """conv3d_forward and conv2d_forward themselves (no workspace), with data,
+    recorded into a graph: every replay equals the eager call bit for bit and
+    both pass the oracle gates; the captured calls run the MFMA kernels the
+    eager ones run (a 3x3x3 f16 layer and a 3x3 bf16 layer)."""
+    import direct_implicit_gemm_amd as L
+    import oracle
+    from convcheck import assert_gates, metrics, oracle_args, to_f64
+    dev = "cuda:0"
+    l3 = W.Layer("ns3", "f16", 1, 64, 4, 9, 40, 72, 3, 3, 3, (1, 1, 1), (1, 1, 1), "relu", 3,
+                 "N01", "N01", "U0.05")
+    l2 = W.Layer("ns2", "bf16", 2, 96, 1, 11, 40, 80, 1, 3, 3, (0, 1, 1), (1, 1, 1), "none", 2,
+                 "N01", "N01", "U0.05")
+    for l in (l3, l2):
+        q = L.libconv_query_plan(l.N, l.C_in, l.T, l.H, l.W, l.C_out, l.KT, l.KH, l.KW,
+                                 *l.pad, *l.stride, W.DTYPE_CODE[l.dtype], W.ACT_CODE[l.act],
+                                 0, 0, 0)
+        assert q[0] == 0 and q[1] == L.ALGO_IGEMM, (l.name, q)
+        note(f"{l.name}: {L.libconv_tile_name(q[2])}")
+    i3, i2 = W.make_inputs(l3, 620), W.make_inputs(l2, 621)
+    t3 = [t.torch(dev) for t in i3]
+    t2 = [t.torch(dev) for t in i2]
+    y3 = torch.empty((1, 72, 4, 9, 40), dtype=torch.float16, device=dev)
+    y2 = torch.empty((2, 80, 11, 40), dtype=torch.bfloat16, device=dev)
+
+    def run():
+        s = torch.cuda.current_stream().cuda_stream
+        st = L.conv3d_forward(t3[0].data_ptr(), t3[1].data_ptr(), t3[2].data_ptr(),
+                              y3.data_ptr(), 1, 64, 4, 9, 40, 72, 3, 3, 3, 1, 1, 1, 1, 1, 1,
+                              L.F16, L.ACT_RELU, s)
+        assert st == 0, st
+        st = L.conv2d_forward(t2[0].data_ptr(), t2[1].data_ptr(), t2[2].data_ptr(),
+                              y2.data_ptr(), 2, 96, 11, 40, 80, 3, 3, 1, 1, 1, 1, L.BF16,
+                              L.ACT_NONE, s)
+        assert st == 0, st
+
+    run()
+    torch.cuda.synchronize()
+    eager = [y3.clone(), y2.clone()]
+    for l, (x, w, b), y in ((l3, i3, eager[0]), (l2, i2, eager[1])):
+        ref, sm = oracle.conv(x.f64(), w.f64(), b.f64(), *oracle_args(l), relu=l.act == "relu")
+        m = metrics(to_f64(y), ref, sm, l.dtype)
+        note(f"{l.name} eager: {m}")
+        assert_gates(m, l.dtype, l.name)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    torch.cuda.synchronize()
+    for r in range(3):
+        y3.fill_(float("nan"))
+        y2.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y3, eager[0]) and torch.equal(y2, eager[1]), f"replay {r}"
+        run()  # eager work between replays
+        torch.cuda.synchronize()
+        note(f"replay {r}: conv3d_forward and conv2d_forward equal the eager calls")
 
 
 def test_graph_packed_layout_frames_and_causal():

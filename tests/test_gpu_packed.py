@@ -5,7 +5,7 @@ import pytest
 
 import oracle
 import workloads as W
-from convcheck import assert_gates, metrics, oracle_args, to_f64
+from convcheck import BIG_WS, assert_gates, metrics, oracle_args, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -83,8 +83,9 @@ def test_forward_packed_forced_tile(case, monkeypatch):
     monkeypatch.setenv("LIBCONV_FORCE_TILE", str(tile))
     note(f"packed tile {tile}: {PACKED_CASES[case]}")
     st, pd = (layer.stride[1:], layer.pad[1:]) if dims == 2 else (layer.stride, layer.pad)
-    q = L.libconv_query_algo(layer.N, C, layer.T, layer.H, layer.W, K, layer.KT, 3, 3,
-                             *layer.pad, *layer.stride, W.DTYPE_CODE[dt], W.ACT_CODE[layer.act], 0)
+    q = L.libconv_query_plan(layer.N, C, layer.T, layer.H, layer.W, K, layer.KT, 3, 3,
+                             *layer.pad, *layer.stride, W.DTYPE_CODE[dt], W.ACT_CODE[layer.act], 0,
+                             0, BIG_WS)
     assert q[0] == 0 and q[2] == tile, q
     xt, wt, bt = x.torch("cuda"), w.torch("cuda"), b.torch("cuda")
     pw = L.pack_weights(wt)

@@ -18,7 +18,7 @@ import pytest
 
 import oracle
 import workloads as W
-from convcheck import assert_gates, gpu_forward, metrics, oracle_args, to_f64
+from convcheck import BIG_WS, assert_gates, gpu_forward, metrics, oracle_args, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -55,10 +55,11 @@ SMALL = {
 SMALL_SEED = {name: 100 + i for i, name in enumerate(sorted(SMALL))}
 
 
-def check_full(layer, seed, algo="auto"):
+def check_full(layer, seed, algo="auto", workspace=True):
     x, w, b = W.make_inputs(layer, seed)
-    note(f"{layer.name} seed={seed} algo={algo} x={layer.x_shape} w={layer.w_shape}")
-    y = to_f64(gpu_forward(layer, x, w, b, algo))
+    note(f"{layer.name} seed={seed} algo={algo} workspace={workspace} x={layer.x_shape} "
+         f"w={layer.w_shape}")
+    y = to_f64(gpu_forward(layer, x, w, b, algo, workspace=workspace))
     st, pd = oracle_args(layer)
     ref, s = oracle.conv(x.f64(), w.f64(), b.f64(), st, pd, relu=layer.act == "relu")
     assert y.shape == ref.shape
@@ -68,17 +69,20 @@ def check_full(layer, seed, algo="auto"):
     return m
 
 
+@pytest.mark.parametrize("workspace", [True, False], ids=["workspace", "export"])
 @pytest.mark.parametrize("name", sorted(SMALL))
-def test_small_layer(name):
-    check_full(SMALL[name], SMALL_SEED[name])
+def test_small_layer(name, workspace):
+    """Every output of each reduced workload layer; `export`: through
+    conv2d_forward / conv3d_forward themselves (no workspace)."""
+    check_full(SMALL[name], SMALL_SEED[name], workspace=workspace)
 
 
 def _supports(layer, algo):
     import direct_implicit_gemm_amd as L
-    st, *_ = L.libconv_query_algo(layer.N, layer.C_in, layer.T, layer.H, layer.W, layer.C_out,
+    st, *_ = L.libconv_query_plan(layer.N, layer.C_in, layer.T, layer.H, layer.W, layer.C_out,
                                   layer.KT, layer.KH, layer.KW, *layer.pad, *layer.stride,
                                   W.DTYPE_CODE[layer.dtype], W.ACT_CODE[layer.act],
-                                  {"direct": 1, "igemm": 2}[algo])
+                                  {"direct": 1, "igemm": 2}[algo], 0, BIG_WS)
     return st == 0
 
 
@@ -110,12 +114,14 @@ def _sample_indices(shape, rng, n_random=3000):
     return np.unique(np.concatenate(idx))
 
 
+@pytest.mark.parametrize("workspace", [True, False], ids=["workspace", "export"])
 @pytest.mark.parametrize("name", sorted(W.ALL_LAYERS))
-def test_full_size_sampled(name):
+def test_full_size_sampled(name, workspace):
     layer = W.ALL_LAYERS[name]
     x, w, b = W.make_inputs(layer)
-    note(f"{name} full size x={layer.x_shape} w={layer.w_shape} (workload inputs)")
-    y = to_f64(gpu_forward(layer, x, w, b))
+    note(f"{name} full size x={layer.x_shape} w={layer.w_shape} (workload inputs) "
+         f"workspace={workspace}")
+    y = to_f64(gpu_forward(layer, x, w, b, workspace=workspace))
     rng = np.random.default_rng(7)
     idx = _sample_indices(y.shape, rng)
     st, pd = oracle_args(layer)

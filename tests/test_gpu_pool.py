@@ -11,7 +11,7 @@ import pytest
 
 import oracle
 import workloads as W
-from convcheck import assert_gates, metrics, to_f64
+from convcheck import BIG_WS, assert_gates, metrics, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -55,7 +55,7 @@ def test_conv_pool(case):
                     "N01", "N01", "U0.05")
     x, w, b = W.make_inputs(layer, 500 + H + K)
     q = L.libconv_query_plan(N, C, 1, H, Wd, K, 1, 3, 3, 0, 1, 1, 1, s, s,
-                             W.DTYPE_CODE[dt], W.ACT_CODE[act], 0, L.PLAN_POOL2)
+                             W.DTYPE_CODE[dt], W.ACT_CODE[act], 0, L.PLAN_POOL2, BIG_WS)
     note(f"pool {case}: tile {L.libconv_tile_name(q[2])}")
     y = to_f64(L.conv2d_pool(x.torch("cuda"), w.torch("cuda"), b.torch("cuda"), s, 1, act))
     ref, sp = _pool_ref(layer, x, w, b)
@@ -90,7 +90,7 @@ def test_every_pool_tile_matches_unfused(monkeypatch):
                         "N01", "N01", "U0.05")
         monkeypatch.setenv("LIBCONV_FORCE_TILE", str(tid))
         q = L.libconv_query_plan(1, C, 1, H, Wd, 72, 1, 3, 3, 0, 1, 1, 1, s, s,
-                                 W.DTYPE_CODE[dt], 1, 0, L.PLAN_POOL2)
+                                 W.DTYPE_CODE[dt], 1, 0, L.PLAN_POOL2, BIG_WS)
         if q[0] != 0 or q[2] != tid:
             continue  # this tile does not pool
         x, w, b = W.make_inputs(layer, 600 + i)

@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 import workloads as W
-from convcheck import assert_gates, metrics, oracle_args, to_f64
+from convcheck import BIG_WS, assert_gates, metrics, oracle_args, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -58,13 +58,15 @@ def test_forced_split(case, ksplit, monkeypatch):
     monkeypatch.setenv("LIBCONV_FORCE_KSPLIT", str(ksplit))
     if tile:
         monkeypatch.setenv("LIBCONV_FORCE_TILE", str(tile))
-    q1 = L.libconv_query_algo(layer.N, layer.C_in, layer.T, layer.H, layer.W, layer.C_out,
+    q1 = L.libconv_query_plan(layer.N, layer.C_in, layer.T, layer.H, layer.W, layer.C_out,
                               layer.KT, layer.KH, layer.KW, *layer.pad, *layer.stride,
-                              W.DTYPE_CODE[layer.dtype], W.ACT_CODE[layer.act], L.ALGO_IGEMM)
+                              W.DTYPE_CODE[layer.dtype], W.ACT_CODE[layer.act], L.ALGO_IGEMM,
+                              0, BIG_WS)
     monkeypatch.setenv("LIBCONV_FORCE_KSPLIT", "1")
-    q0 = L.libconv_query_algo(layer.N, layer.C_in, layer.T, layer.H, layer.W, layer.C_out,
+    q0 = L.libconv_query_plan(layer.N, layer.C_in, layer.T, layer.H, layer.W, layer.C_out,
                               layer.KT, layer.KH, layer.KW, *layer.pad, *layer.stride,
-                              W.DTYPE_CODE[layer.dtype], W.ACT_CODE[layer.act], L.ALGO_IGEMM)
+                              W.DTYPE_CODE[layer.dtype], W.ACT_CODE[layer.act], L.ALGO_IGEMM,
+                              0, BIG_WS)
     monkeypatch.setenv("LIBCONV_FORCE_KSPLIT", str(ksplit))
     assert q1[0] == 0 and q0[0] == 0
     assert q1[2] == q0[2] and q1[3] == ksplit * q0[3], (q0, q1)  # same tile, S x workgroups

@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 import workloads as W
-from convcheck import assert_gates, metrics, oracle_args, to_f64
+from convcheck import BIG_WS, assert_gates, metrics, oracle_args, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -51,7 +51,7 @@ def _one_stage_width(tid: int, kdig: str, wide: bool) -> int:
     k = 1 if kdig == "1" else 3
     for c in ((128, 64, 32) if wide else (32, 16)):
         q = L.libconv_query_plan(1, c, 1, 12, 64, 16, 1, k, k, 0, k // 2, k // 2, 1, 1, 1,
-                                 1 if wide else 0, 0, 0, 0)
+                                 1 if wide else 0, 0, 0, 0, BIG_WS)
         if q[0] == 0 and q[2] == tid:
             return c
     raise AssertionError(f"no channel count fits tile {tid}")
@@ -94,9 +94,10 @@ def test_every_tile(ragged, monkeypatch):
     for i, (tid, name) in enumerate(tiles):
         monkeypatch.setenv("LIBCONV_FORCE_TILE", str(tid))
         layer = _layer_for(tid, name, ragged)
-        q = L.libconv_query_algo(layer.N, layer.C_in, layer.T, layer.H, layer.W, layer.C_out,
+        q = L.libconv_query_plan(layer.N, layer.C_in, layer.T, layer.H, layer.W, layer.C_out,
                                  layer.KT, layer.KH, layer.KW, *layer.pad, *layer.stride,
-                                 W.DTYPE_CODE[layer.dtype], W.ACT_CODE[layer.act], 0)
+                                 W.DTYPE_CODE[layer.dtype], W.ACT_CODE[layer.act], 0, 0,
+                                 BIG_WS)
         assert q[0] == 0 and q[2] == tid, (name, layer, q)
         note(f"tile {tid} {name} ragged={ragged}: x={layer.x_shape} w={layer.w_shape} "
              f"{layer.dtype} {layer.act}")
