@@ -29,7 +29,7 @@ STATUS = {
     0: "OK", 1: "ERR_NULL_POINTER", 2: "ERR_BAD_SHAPE", 3: "ERR_BAD_DTYPE",
     4: "ERR_BAD_ACTIVATION", 5: "ERR_ALIAS", 6: "ERR_UNSUPPORTED", 7: "ERR_NO_DEVICE",
     8: "ERR_LAUNCH", 9: "ERR_BAD_ALGO", 10: "ERR_TOO_LARGE", 11: "ERR_OUT_OF_MEMORY",
-    12: "ERR_MISALIGNED",
+    12: "ERR_MISALIGNED", 13: "ERR_SCRATCH_TOO_SMALL",
 }
 _ALGOS = {"auto": ALGO_AUTO, "direct": ALGO_DIRECT, "igemm": ALGO_IGEMM}
 _ACTS = {"none": ACT_NONE, "relu": ACT_RELU}
@@ -74,6 +74,8 @@ def load() -> ctypes.CDLL:
     lib.libconv_forward_ex.restype = I
     lib.libconv_workspace_size.argtypes = [I] * 20
     lib.libconv_workspace_size.restype = LL
+    lib.conv3d_forward_noalloc.argtypes = [P, P, P, P] + [I] * 17 + [P]
+    lib.conv3d_forward_noalloc.restype = I
     lib.libconv_tile_name.argtypes = [I]
     lib.libconv_tile_name.restype = ctypes.c_char_p
     lib.libconv_tile_occupancy.argtypes = [I, I, I]
@@ -177,6 +179,16 @@ def libconv_forward_ex(x, w, packed_w, bias, y, N, C_in, T, H, W, C_out, KT, KH,
                                      KW, pad_t_front, pad_t_back, pad_h, pad_w, stride_t,
                                      stride_h, stride_w, dtype, act, algo, flags, workspace,
                                      workspace_bytes, stream)
+
+
+SCRATCH_BYTES = 64 << 20
+
+
+def conv3d_forward_noalloc(x, w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW, pad_t, pad_h,
+                           pad_w, stride_t, stride_h, stride_w, dtype, act, stream) -> int:
+    return load().conv3d_forward_noalloc(x, w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW,
+                                         pad_t, pad_h, pad_w, stride_t, stride_h, stride_w,
+                                         dtype, act, stream)
 
 
 def libconv_workspace_size(N, C_in, T, H, W, C_out, KT, KH, KW, pad_t_front, pad_t_back,

@@ -139,6 +139,29 @@ bool device_ok(int d) {
   return d >= 0 && d < g_dev_count && g_dev_ok[d];
 }
 
+// The library's own workspace for conv3d_forward_noalloc: a device array of a
+// fixed size, one copy on every GPU the library runs on, held until the
+// process ends.  Host code never uses the array's name as an address: its
+// device address on each device is looked up once (hipGetSymbolAddress, with
+// that device current) and only that pointer is passed to kernels.
+constexpr long long kScratchBytes = 64LL << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+
+// The address of this device's scratch array, or null if the lookup failed.
+void* device_scratch(int d) {
+  std::call_once(g_scratch_once[d], [d] {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) {
+      (void)hipGetLastError();
+      ptr = nullptr;
+    }
+    g_scratch_ptr[d] = ptr;
+  });
+  return g_scratch_ptr[d];
+}
+
 // The dispatcher.  The vector-ALU direct kernel takes layers whose
 // reduction per output (C_in * taps) is too short to fill an MFMA k-step
 // pipeline -- stems with 3 input channels, pointwise layers with fewer than
@@ -482,6 +505,31 @@ libconv_status libconv_forward_ex(const void* x, const void* w, const void* pack
   return forward_ex(x, w, packed_w, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW, pad_t_front,
                     pad_t_back, pad_h, pad_w, stride_t, stride_h, stride_w, dtype, act, algo,
                     flags, workspace, workspace_bytes, stream);
+}
+
+libconv_status conv3d_forward_noalloc(const void* x, const void* w, const void* bias, void* y,
+                                     int N, int C_in, int T, int H, int W, int C_out, int KT,
+                                     int KH, int KW, int pad_t, int pad_h, int pad_w,
+                                     int stride_t, int stride_h, int stride_w, int dtype, int act,
+                                     void* stream) {
+  const long long need = libconv_workspace_size(N, C_in, T, H, W, C_out, KT, KH, KW, pad_t,
+                                                pad_t, pad_h, pad_w, stride_t, stride_h,
+                                                stride_w, dtype, act, LIBCONV_ALGO_AUTO, 0);
+  if (need > kScratchBytes) return LIBCONV_ERR_SCRATCH_TOO_SMALL;
+  if (need < 0 || N == 0)  // argument errors and empty batches: as conv3d_forward_ws
+    return forward_ex(x, w, nullptr, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW, pad_t, pad_t,
+                      pad_h, pad_w, stride_t, stride_h, stride_w, dtype, act, LIBCONV_ALGO_AUTO,
+                      0, nullptr, 0, stream);
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || !device_ok(dev)) {
+    (void)hipGetLastError();
+    return LIBCONV_ERR_NO_DEVICE;
+  }
+  void* ws = device_scratch(dev);
+  if (!ws) return LIBCONV_ERR_LAUNCH;
+  return forward_ex(x, w, nullptr, bias, y, N, C_in, T, H, W, C_out, KT, KH, KW, pad_t, pad_t,
+                    pad_h, pad_w, stride_t, stride_h, stride_w, dtype, act, LIBCONV_ALGO_AUTO, 0,
+                    ws, kScratchBytes, stream);
 }
 
 long long libconv_workspace_size(int N, int C_in, int T, int H, int W, int C_out, int KT, int KH,
@@ -905,6 +953,8 @@ const char* libconv_status_string(int status) {
     case LIBCONV_ERR_TOO_LARGE: return "tensor too large";
     case LIBCONV_ERR_OUT_OF_MEMORY: return "out of device memory";
     case LIBCONV_ERR_MISALIGNED: return "a pointer is not aligned as the call requires";
+    case LIBCONV_ERR_SCRATCH_TOO_SMALL:
+      return "the call needs more workspace than the library's 64 MiB scratch array";
     default: return "unknown status";
   }
 }

@@ -98,7 +98,9 @@ typedef enum {
   LIBCONV_ERR_BAD_ALGO = 9,       /* algo is not a libconv_algo */
   LIBCONV_ERR_TOO_LARGE = 10,     /* a tensor (or the packed weights) spans 2^31 bytes or more */
   LIBCONV_ERR_OUT_OF_MEMORY = 11, /* not returned by this version (no call allocates) */
-  LIBCONV_ERR_MISALIGNED = 12     /* a workspace is not 256-byte aligned */
+  LIBCONV_ERR_MISALIGNED = 12,    /* a workspace is not 256-byte aligned */
+  LIBCONV_ERR_SCRATCH_TOO_SMALL = 13 /* conv3d_forward_noalloc: the plan needs more than the
+                                        library's scratch array holds */
 } libconv_status;
 
 /*
@@ -161,6 +163,28 @@ libconv_status conv3d_forward_ws(const void* x, const void* w, const void* bias,
                                  int stride_t, int stride_h, int stride_w,
                                  int dtype, int act, void* workspace, long long workspace_bytes,
                                  void* stream);
+
+/*
+ * conv3d_forward_ws without a caller workspace and without any allocation:
+ * for callers that cannot allocate device memory at all (code recorded under
+ * HIP graph capture that must not take memory, tight serving loops,
+ * harnesses that forbid hipMalloc).  The workspace is the library's own
+ * device array of 64 MiB (LIBCONV_SCRATCH_BYTES), one per GPU, held until the
+ * process ends; a plan needing more (libconv_workspace_size above it) returns
+ * LIBCONV_ERR_SCRATCH_TOO_SMALL before anything is enqueued.  Same result as
+ * conv3d_forward_ws given the workspace libconv_workspace_size names (the
+ * same plan).  Every call on one GPU shares that array, so calls that may
+ * overlap on one GPU (other streams, other host threads) race: order them.
+ * The array's contents carry over between calls; no plan reads any of it
+ * before writing it.  2-D: T = KT = 1, pad_t = 0, stride_t = 1.
+ */
+#define LIBCONV_SCRATCH_BYTES (64LL << 20)
+libconv_status conv3d_forward_noalloc(const void* x, const void* w, const void* bias, void* y,
+                                      int N, int C_in, int T, int H, int W,
+                                      int C_out, int KT, int KH, int KW,
+                                      int pad_t, int pad_h, int pad_w,
+                                      int stride_t, int stride_h, int stride_w,
+                                      int dtype, int act, void* stream);
 
 /* Flags of libconv_forward_ex, libconv_workspace_size and libconv_query_plan. */
 enum {

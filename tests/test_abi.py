@@ -422,3 +422,23 @@ def test_new_calls_with_an_empty_batch_do_nothing():
                                     max(need, 1), L.F16, 0, None, None, None) == 0
     assert L.libconv_pack_activations(fake, y, 0, 16, 5, 8, 32, L.F16, None) == 0
     assert L.libconv_unpack_activations(fake, y, 0, 16, 5, 8, 32, L.F16, None) == 0
+
+
+def test_noalloc_rejects_plans_beyond_its_scratch():
+    """conv3d_forward_noalloc refuses, before any device access, a call whose
+    best plan needs more than the library's 64 MiB scratch array (here the
+    UNet 1280-channel layer at 64x64: 113 MB of packed weights and partial
+    sums); within the limit a valid call reaches the device check."""
+    fake = 1 << 40
+    args = (2, 1280, 1, 64, 64, 1280, 1, 3, 3, 0, 1, 1, 1, 1, 1, L.BF16, 0)
+    need = L.libconv_workspace_size(2, 1280, 1, 64, 64, 1280, 1, 3, 3, 0, 0, 1, 1, 1, 1, 1,
+                                    L.BF16, 0, L.ALGO_AUTO, 0)
+    assert need > L.SCRATCH_BYTES
+    assert L.conv3d_forward_noalloc(fake, fake + (1 << 30), None, fake + (1 << 33), *args,
+                                    None) == 13
+    assert L.libconv_status_string(13).startswith("the call needs more workspace")
+    small = (1, 64, 5, 8, 40, 64, 3, 3, 3, 1, 1, 1, 1, 1, 1, L.F16, 0)
+    assert L.conv3d_forward_noalloc(fake, fake + (1 << 30), None, fake + (1 << 33), *small,
+                                    None) == 7
+    assert L.conv3d_forward_noalloc(fake, fake + (1 << 30), None, fake + (1 << 33), *small[:15],
+                                    9, 0, None) == 3
