@@ -18,7 +18,9 @@ import re
 from typing import Optional, Sequence, Tuple, Union
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libconv.so")
+# LIBCONV_LIBRARY selects another build of the same library (the sanitizer
+# build, libconv_san.so); the default is the in-tree libconv.so.
+LIB_PATH = os.environ.get("LIBCONV_LIBRARY") or os.path.join(_HERE, "libconv.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "libconv.h")
 
 F32, F16, BF16 = 0, 1, 2

@@ -21,16 +21,29 @@ from typing import Optional, Sequence, Tuple
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "liboracle.so")
 SRC_PATH = os.path.join(_HERE, "conv_oracle.c")
+# ORACLE_LIBRARY selects another build (the sanitizer build, liboracle_san.so)
+LIB_PATH = os.environ.get("ORACLE_LIBRARY") or os.path.join(_HERE, "liboracle.so")
+SAN_LIB_PATH = os.path.join(_HERE, "liboracle_san.so")
 
 
-def build() -> str:
-    """Compile liboracle.so with gcc (fp64, OpenMP, no fast-math)."""
+def build(sanitize: bool = False) -> str:
+    """Compile liboracle.so with gcc (fp64, OpenMP, no fast-math).  With
+    sanitize: liboracle_san.so with AddressSanitizer and
+    UndefinedBehaviorSanitizer, by the clang that ships with the HIP compiler
+    (so that it shares one ASan runtime with the library's sanitizer build)."""
+    if sanitize:
+        cmd = ["/opt/rocm/llvm/bin/clang", "-O1", "-g", "-fno-omit-frame-pointer",
+               "-fsanitize=address,undefined", "-fno-fast-math", "-ffp-contract=off",
+               "-fopenmp", "-shared", "-fPIC", "-Wall", "-Werror", "-o", SAN_LIB_PATH, SRC_PATH,
+               "-lm"]
+        subprocess.run(cmd, check=True)
+        return SAN_LIB_PATH
+    out = os.path.join(_HERE, "liboracle.so")
     cmd = ["gcc", "-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp",
-           "-shared", "-fPIC", "-Wall", "-Werror", "-o", LIB_PATH, SRC_PATH, "-lm"]
+           "-shared", "-fPIC", "-Wall", "-Werror", "-o", out, SRC_PATH, "-lm"]
     subprocess.run(cmd, check=True)
-    return LIB_PATH
+    return out
 
 
 _lib = None
