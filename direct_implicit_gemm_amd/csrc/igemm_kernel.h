@@ -191,13 +191,27 @@ struct Cfg {
   static constexpr int WPASS = PK ? 0 : (WUNITS + kThreads - 1) / kThreads;
   static constexpr int NWREG = PK ? 0 : W3 ? WPASS * SE * 2 : WPASS * TS;
   // weight staging from packed weights: NSLOT runs of BM 16-byte vectors,
-  // moved as 1 KB chunks (one wave, one instruction each), NDMA per wave; when
-  // the chunks do not divide evenly, the spare copies read nothing (zeros)
-  // into a 1 KB scratch area at the end of LDS
+  // moved as 1 KB chunks (one wave, one instruction each), NDMA per weight
+  // wave (below); when the chunks do not divide evenly, the spare copies read
+  // nothing (zeros) into a 1 KB scratch area at the end of LDS
   static constexpr int WCHUNKS = NSLOT * BM / 64;
-  static constexpr int NDMA = (WCHUNKS + 3) / 4;
+  // input staging: one unit = one run (VX) or one halo pixel of one channel
+  // group; VX units come in blocks of 8 rows x NRUN runs
+  static constexpr int XUNITS = VX ? (NROWS + 7) / 8 * 8 * NRUN : CG * HR * HC;
+  static constexpr int XPASS = XP ? 0 : (XUNITS + kThreads - 1) / kThreads;
+  static constexpr int XPASS1 = XPASS > 0 ? XPASS : 1;  // array extent
+  // Which waves stage what.  When a stage's input units fit in fewer than
+  // four waves, only those (the first XW) read the input, and the weights go
+  // to the others (the last WW), so that no wave issues reads that would all
+  // fall outside the tensor (such reads still cost the address unit a full
+  // wave instruction) and the staging is spread over the four waves.  A wave
+  // may have both roles.
+  static constexpr int XW = (VX && XPASS == 1) ? (XUNITS + 63) / 64 : 4;
+  static constexpr int WW = PK ? (XW < 4 ? 4 - XW : 4) : (WPASS == 1 ? (WUNITS + 63) / 64 : 4);
+  static constexpr int W0 = 4 - WW;                // first weight wave
+  static constexpr int NDMA = PK ? (WCHUNKS + WW - 1) / WW : 0;
   static constexpr int DMA_PAD =
-      ((PK && WCHUNKS % 4 != 0) || (XP && XDMA % 4 != 0)) ? 1024 : 0;
+      ((PK && WCHUNKS % WW != 0) || (XP && XDMA % 4 != 0)) ? 1024 : 0;
   // LDS: two weight and two input buffers (one of each for single-stage tiles)
   static constexpr int NBUF = ONE ? 1 : 2;
   // the vectorised epilogue reuses LDS as four wave-private 32x32 tiles
@@ -210,11 +224,6 @@ struct Cfg {
   static constexpr int STAGES_LDS = NBUF * (WBYTES + XBYTES) + DMA_PAD;
   static constexpr int LDS0 = STAGES_LDS > EPI_LDS ? STAGES_LDS : EPI_LDS;
   static constexpr int LDS = LDS0 > EPI_POOL_LDS ? LDS0 : EPI_POOL_LDS;
-  // input staging: one unit = one run (VX) or one halo pixel of one channel
-  // group; VX units come in blocks of 8 rows x NRUN runs
-  static constexpr int XUNITS = VX ? (NROWS + 7) / 8 * 8 * NRUN : CG * HR * HC;
-  static constexpr int XPASS = XP ? 0 : (XUNITS + kThreads - 1) / kThreads;
-  static constexpr int XPASS1 = XPASS > 0 ? XPASS : 1;  // array extent
   // global reads into registers each wave issues per stage
   static constexpr int REG_LOADS = XPASS * SE + NWREG;
   // slot pair before whose MFMAs the next stage's registers are written to
@@ -346,6 +355,8 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int il = lane & 31;   // row (A) / column (B) inside a 32x32 block
   const int hf = lane >> 5;   // which slot of the pair this lane carries
+  const bool xwave = wave < G::XW;     // stages input (wave-uniform)
+  const bool wwave = wave >= G::W0;    // stages weights (wave-uniform)
 
   // ---- tile coordinates; XCD-aware order: the hardware deals workgroups to
   // the 8 XCDs round-robin, so consecutive logical tiles are gathered onto one
@@ -479,10 +490,10 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
   int wgrp[G::WPASS > 0 ? G::WPASS : 1];
 #pragma unroll
   for (int i = 0; i < G::WPASS; ++i) {
-    const int u = tid + i * kThreads;
+    const int u = tid - 64 * G::W0 + i * kThreads;  // weight units start at the first weight wave
     const int g = u / G::BM, col = u % G::BM;
     const int co = co0 + col;
-    const bool ok = u < G::WUNITS && co < a.K;
+    const bool ok = u >= 0 && u < G::WUNITS && co < a.K;
     woff[i] = guard_offset(true, ok ? (co * a.C * G::TS + g * SE * G::TS) * EB : kFar);
     wgrp[i] = g;
   }
@@ -524,12 +535,16 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
     q.wrun = 0;
     return q;
   };
-  auto read_w = [&](auto ragged, auto kc, const Src& q, StageRegs<G>& r, unsigned char* wdst)
-      __attribute__((always_inline)) {
+  // `role` (compile time): bit 0 the wave stages input, bit 1 weights; a
+  // read of the other kind is not issued at all.
+  auto read_w = [&](auto role, auto ragged, auto kc, const Src& q, StageRegs<G>& r,
+                    unsigned char* wdst) __attribute__((always_inline)) {
     constexpr int k = decltype(kc)::value;
-    if constexpr (G::PK) {
+    if constexpr ((decltype(role)::value & 2) == 0) {
+      return;
+    } else if constexpr (G::PK) {
       // chunk c = 64 channels of one slot; lane l lands at chunk base + 16 l
-      const int c = wave + k * (kThreads / 64);
+      const int c = (wave - G::W0) + k * G::WW;
       const int slot = c / (G::BM / 64), part = c % (G::BM / 64);
       const int t2 = slot / G::CG, g = slot % G::CG;
       const int run = q.wrun + (g * G::TS + t2) * 64 + part * a.wblk;
@@ -557,12 +572,14 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
           u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(q.rs, v + t * 16, 0, 0));
     }
   };
-  auto read_x = [&](auto ragged, auto kc, const Src& q, StageRegs<G>& r)
+  auto read_x = [&](auto role, auto ragged, auto kc, const Src& q, StageRegs<G>& r)
       __attribute__((always_inline)) {
     constexpr int k = decltype(kc)::value;
     constexpr int i = k / SE, j = k % SE;
     constexpr bool rg = decltype(ragged)::value;
-    if constexpr (G::VX) {
+    if constexpr ((decltype(role)::value & 1) == 0) {
+      return;
+    } else if constexpr (G::VX) {
       int v = xv[i];
       if constexpr (rg) v = guard_offset(true, q.ci0 + xgrp[i] * SE + j < a.C ? v : kFar);
       r.xr[i][j] = __builtin_bit_cast(
@@ -616,7 +633,7 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
     // conflict-free
 #pragma unroll
     for (int i = 0; i < G::WPASS; ++i) {
-      const int u = tid + i * kThreads;
+      const int u = tid - 64 * G::W0 + i * kThreads;
       unsigned char* base = wdst + ((u / G::BM) * G::BM + u % G::BM) * 16;
       if constexpr (G::W3) {
         // slot of spatial tap t: word m = channels 2m, 2m+1 at tap t
@@ -633,11 +650,12 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
               v[m] = (r.wt[i][2 * m] & 0xffffu) | (r.wt[i][2 * m + 1] << 16);
             }
           }
-          if (u < G::WUNITS)
+          if (u >= 0 && u < G::WUNITS)
             *reinterpret_cast<u32x4_t*>(base + t * G::CG * G::BM * 16) = v;
         }
       } else {
-        if (u < G::WUNITS) store_slots<SE, G::TS, 0>(base, G::CG * G::BM * 16, r.wv[i]);
+        if (u >= 0 && u < G::WUNITS)
+          store_slots<SE, G::TS, 0>(base, G::CG * G::BM * 16, r.wv[i]);
       }
     }
     // input halo: gather the SE channels of each pixel into one 16-byte word
@@ -776,12 +794,21 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
       }
     }
   };
-  auto main_loop = [&](auto ragged) __attribute__((always_inline)) {
+  // Reads a wave of role `role` has issued among a step's first lo pieces
+  // (weight pieces come first), and the register reads it issues per stage.
+  auto issued = [](int role, int lo) constexpr -> int {
+    return ((role & 2) ? (lo < NWP ? lo : NWP) : 0) + ((role & 1) ? (lo > NWP ? lo - NWP : 0) : 0);
+  };
+  auto reg_loads = [](int role) constexpr -> int {
+    return ((role & 1) ? G::XPASS * SE : 0) + ((role & 2) ? G::NWREG : 0);
+  };
+  auto main_loop = [&](auto ragged, auto rolec) __attribute__((always_inline)) {
+    constexpr int role = decltype(rolec)::value;
     if constexpr (G::ONE) {  // the one stage: read, write to LDS, multiply
       StageRegs<G> r1;
       const Src qw = w_src(chunk0, kt_lo), qx = x_src(chunk0, kt_lo);
-      static_for<0, NWP>([&](auto kc) { read_w(ragged, kc, qw, r1, wbuf(0)); });
-      static_for<0, NXP>([&](auto kc) { read_x(ragged, kc, qx, r1); });
+      static_for<0, NWP>([&](auto kc) { read_w(rolec, ragged, kc, qw, r1, wbuf(0)); });
+      static_for<0, NXP>([&](auto kc) { read_x(rolec, ragged, kc, qx, r1); });
       wait_vmcnt<0>();
       store_stage(r1, wbuf(0), xbuf(0));
       lds_barrier();
@@ -795,21 +822,21 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
     auto read_all = [&](StageRegs<G>& r, unsigned char* wdst) __attribute__((always_inline)) {
       const Src qw = G::PK ? w_src(cw.chunk, cw.kt) : w_src(cx.chunk, cx.kt);
       const Src qx = x_src(cx.chunk, cx.kt);
-      static_for<0, NWP>([&](auto kc) { read_w(ragged, kc, qw, r, wdst); });
-      static_for<0, NXP>([&](auto kc) { read_x(ragged, kc, qx, r); });
+      static_for<0, NWP>([&](auto kc) { read_w(rolec, ragged, kc, qw, r, wdst); });
+      static_for<0, NXP>([&](auto kc) { read_x(rolec, ragged, kc, qx, r); });
       if constexpr (G::PK) advance(cw);
       advance(cx);
     };
     if constexpr (G::PK) {
       read_all(ra, wbuf(0));              // weights of stage 0, input of stage 0
       const Src qx = x_src(cx.chunk, cx.kt);
-      static_for<0, NXP>([&](auto kc) { read_x(ragged, kc, qx, rb); });  // input of stage 1
+      static_for<0, NXP>([&](auto kc) { read_x(rolec, ragged, kc, qx, rb); });  // input of stage 1
       advance(cx);
     } else {
       read_all(ra, nullptr);
       read_all(rb, nullptr);
     }
-    wait_vmcnt<G::REG_LOADS>();
+    wait_vmcnt<reg_loads(role)>();
     store_stage(ra, wbuf(0), xbuf(0));
     lds_barrier();
     // Stage s: `mine` is free and receives the input (and OIHW weights) of
@@ -830,24 +857,24 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
         constexpr int p = decltype(pc)::value;
         constexpr int lo = p * (NWP + NXP) / G::NPAIR, hi = (p + 1) * (NWP + NXP) / G::NPAIR;
         if constexpr (p == G::SPAIR) {
-          // `other`'s reads precede the lo reads this step has issued so far
-          wait_vmcnt<lo>();
+          // `other`'s reads precede the reads this step has issued so far
+          wait_vmcnt<issued(role, lo)>();
           store_stage(other, wbuf((s + 1) & 1), xbuf((s + 1) & 1));
         }
         static_for<lo, hi>([&](auto kc) {
           constexpr int k = decltype(kc)::value;
           if constexpr (k < NWP)
-            read_w(ragged, kc, qw, mine, wdst);
+            read_w(rolec, ragged, kc, qw, mine, wdst);
           else
-            read_x(ragged, std::integral_constant<int, k - NWP>{}, qx, mine);
+            read_x(rolec, ragged, std::integral_constant<int, k - NWP>{}, qx, mine);
         });
       });
       if constexpr (G::PK) advance(cw);
       advance(cx);
       // packed weights of stage s+1 (copied straight to LDS, the first reads
-      // of this step) have landed; the REG_LOADS register reads of stage s+2
-      // issued after them may still be in flight
-      wait_vmcnt<G::REG_LOADS>();
+      // of this step) have landed; the register reads of stage s+2 issued
+      // after them may still be in flight
+      wait_vmcnt<reg_loads(role)>();
       if constexpr (G::SPAIR < 0) store_stage(other, wbuf((s + 1) & 1), xbuf((s + 1) & 1));
       lds_barrier();
     };
@@ -859,6 +886,25 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
     if (s < nstages) step(s, ra, rb);
     wait_vmcnt<0>();  // no copy into LDS may outlive the workgroup
   };
+  // Each wave runs the loop of its role (a wave-uniform branch), in which
+  // every step issues a fixed sequence of reads, so that the waits on the
+  // reads in flight are exact; every role runs the same barriers.
+  auto run_roles = [&](auto ragged) __attribute__((always_inline)) {
+    using R1 = std::integral_constant<int, 1>;
+    using R2 = std::integral_constant<int, 2>;
+    using R3 = std::integral_constant<int, 3>;
+    if constexpr (G::XW == 4 && G::W0 == 0) {
+      main_loop(ragged, R3{});
+    } else {
+      if (xwave && wwave) {
+        if constexpr (G::XW > G::W0) main_loop(ragged, R3{});
+      } else if (xwave) {
+        if constexpr (G::W0 > 0) main_loop(ragged, R1{});
+      } else {
+        if constexpr (G::XW < 4) main_loop(ragged, R2{});
+      }
+    }
+  };
   // Channel-packed input: weights and input of stage s+1 are both copied
   // straight into the free LDS buffers while stage s is multiplied (spread
   // over its slot pairs); a step ends when the copies have landed and every
@@ -869,7 +915,9 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
     Cursor c{chunk0, kt_lo, 0};
     {
       const Src qw = w_src(c.chunk, c.kt), qx = x_src(c.chunk, c.kt);
-      static_for<0, NWP>([&](auto kc) { read_w(ragged, kc, qw, unused, wbuf(0)); });
+      static_for<0, NWP>([&](auto kc) {
+        read_w(std::integral_constant<int, 3>{}, ragged, kc, qw, unused, wbuf(0));
+      });
       static_for<0, G::NXDMA>([&](auto kc) { read_xd(ragged, kc, qx, xbuf(0)); });
       advance(c);
     }
@@ -888,7 +936,7 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
           static_for<lo, hi>([&](auto kc) {
             constexpr int k = decltype(kc)::value;
             if constexpr (k < NWP)
-              read_w(ragged, kc, qw, unused, wdst);
+              read_w(std::integral_constant<int, 3>{}, ragged, kc, qw, unused, wdst);
             else
               read_xd(ragged, std::integral_constant<int, k - NWP>{}, qx, xdst);
           });
@@ -907,9 +955,9 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
         main_loop_dma(std::true_type{});
     } else {
       if (a.C % G::CK == 0)
-        main_loop(std::false_type{});
+        run_roles(std::false_type{});
       else
-        main_loop(std::true_type{});
+        run_roles(std::true_type{});
     }
   }
 
