@@ -201,13 +201,16 @@ struct Cfg {
   static constexpr int XPASS = XP ? 0 : (XUNITS + kThreads - 1) / kThreads;
   static constexpr int XPASS1 = XPASS > 0 ? XPASS : 1;  // array extent
   // Which waves stage what.  When a stage's input units fit in fewer than
-  // four waves, only those (the first XW) read the input, and the weights go
-  // to the others (the last WW), so that no wave issues reads that would all
-  // fall outside the tensor (such reads still cost the address unit a full
-  // wave instruction) and the staging is spread over the four waves.  A wave
-  // may have both roles.
+  // four waves, only those (the first XW) read the input, so that no wave
+  // issues reads that would all fall outside the tensor (such reads still
+  // cost the address unit a full wave instruction).  Packed weights are
+  // copied by all four waves: a wave that copied them alone (as many
+  // one-instruction copies as the input waves' reads, repacking and LDS
+  // writes together) finished each stage last and held the others at the
+  // barrier (measured per wave on the 3x3x3 video-VAE layers).  OIHW weight
+  // units go to the last WW waves.  A wave may have both roles.
   static constexpr int XW = (VX && XPASS == 1) ? (XUNITS + 63) / 64 : 4;
-  static constexpr int WW = PK ? (XW < 4 ? 4 - XW : 4) : (WPASS == 1 ? (WUNITS + 63) / 64 : 4);
+  static constexpr int WW = PK ? 4 : (WPASS == 1 ? (WUNITS + 63) / 64 : 4);
   static constexpr int W0 = 4 - WW;                // first weight wave
   static constexpr int NDMA = PK ? (WCHUNKS + WW - 1) / WW : 0;
   static constexpr int DMA_PAD =
