@@ -240,7 +240,7 @@ struct Cfg {
   static_assert(BM % 64 == 0 || !PK, "packed tiles move whole 64-channel chunks");
   static_assert(BM <= kPackAlign, "packed channel padding covers one tile");
   static_assert(!W3 || (TS2 == 9 && EB == 2), "OIDHW weights: 3x3 spatial taps, 16-bit types");
-  static_assert(!XP || (PK && !ONE), "channel-packed tiles read packed weights, two stages");
+  static_assert(!XP || !ONE, "channel-packed tiles run two stages");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -892,19 +892,19 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
   // Each wave runs the loop of its role (a wave-uniform branch), in which
   // every step issues a fixed sequence of reads, so that the waits on the
   // reads in flight are exact; every role runs the same barriers.
-  auto run_roles = [&](auto ragged) __attribute__((always_inline)) {
+  auto run_roles = [&](auto ragged, auto&& loop) __attribute__((always_inline)) {
     using R1 = std::integral_constant<int, 1>;
     using R2 = std::integral_constant<int, 2>;
     using R3 = std::integral_constant<int, 3>;
     if constexpr (G::XW == 4 && G::W0 == 0) {
-      main_loop(ragged, R3{});
+      loop(ragged, R3{});
     } else {
       if (xwave && wwave) {
-        if constexpr (G::XW > G::W0) main_loop(ragged, R3{});
+        if constexpr (G::XW > G::W0) loop(ragged, R3{});
       } else if (xwave) {
-        if constexpr (G::W0 > 0) main_loop(ragged, R1{});
+        if constexpr (G::W0 > 0) loop(ragged, R1{});
       } else {
-        if constexpr (G::XW < 4) main_loop(ragged, R2{});
+        if constexpr (G::XW < 4) loop(ragged, R2{});
       }
     }
   };
@@ -950,17 +950,95 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
       lds_barrier();
     }
   };
+  // Channel-packed input with OI(D)HW weights: the input of stage s+1 is
+  // copied straight into the free LDS buffer while stage s is multiplied (as
+  // packed weights are in the loop above), and the weights go through
+  // registers two stages ahead, transposed into LDS before slot pair SPAIR
+  // (as the input is there).  A step's copies come before its register
+  // reads, so that waiting for all but the register reads waits for the
+  // copies.
+  auto main_loop_xo = [&](auto ragged, auto rolec) __attribute__((always_inline)) {
+    constexpr int role = decltype(rolec)::value;
+    constexpr int NXD = G::NXDMA;                 // copy pieces of a step
+    constexpr int NWR = (role & 2) ? G::NWREG : 0;  // this wave's register reads per stage
+    StageRegs<G> ra, rb;
+    Cursor cd{chunk0, kt_lo, 0}, cr{chunk0, kt_lo, 0};  // next stage to copy / to read weights of
+    auto copy_x = [&](auto kc, const Src& q, unsigned char* xdst) __attribute__((always_inline)) {
+      if constexpr ((role & 1) != 0) read_xd(ragged, kc, q, xdst);
+    };
+    auto read_ws = [&](StageRegs<G>& r) __attribute__((always_inline)) {
+      const Src qw = w_src(cr.chunk, cr.kt);
+      static_for<0, G::NWREG>([&](auto kc) { read_w(rolec, ragged, kc, qw, r, nullptr); });
+      advance(cr);
+    };
+    {
+      const Src qx = x_src(cd.chunk, cd.kt);
+      static_for<0, NXD>([&](auto kc) { copy_x(kc, qx, xbuf(0)); });
+      advance(cd);
+    }
+    read_ws(ra);
+    read_ws(rb);
+    wait_vmcnt<NWR>();  // stage 0's copies and weights are in; stage 1's weights may be in flight
+    store_stage(ra, wbuf(0), xbuf(0));
+    lds_barrier();
+    // reads of role `role` among a step's first lo pieces (copies first)
+    auto issued_xo = [](int lo) constexpr -> int {
+      return ((role & 1) ? (lo < NXD ? lo : NXD) : 0) + ((role & 2) ? (lo > NXD ? lo - NXD : 0) : 0);
+    };
+    auto step = [&](int s, StageRegs<G>& mine, StageRegs<G>& other)
+        __attribute__((always_inline)) {
+      const Src qx = x_src(cd.chunk, cd.kt);  // stage s+1
+      const Src qw = w_src(cr.chunk, cr.kt);  // stage s+2
+      unsigned char* xdst = xbuf((s + 1) & 1);
+      compute(wbuf(s & 1), xbuf(s & 1), [&](auto pc) {
+        constexpr int p = decltype(pc)::value;
+        constexpr int NP = NXD + G::NWREG;
+        constexpr int lo = p * NP / G::NPAIR, hi = (p + 1) * NP / G::NPAIR;
+        if constexpr (p == G::SPAIR) {
+          // `other`'s weight reads precede every read this step has issued
+          wait_vmcnt<issued_xo(lo)>();
+          store_stage(other, wbuf((s + 1) & 1), xbuf((s + 1) & 1));
+        }
+        static_for<lo, hi>([&](auto kc) {
+          constexpr int k = decltype(kc)::value;
+          if constexpr (k < NXD)
+            copy_x(kc, qx, xdst);
+          else
+            read_w(rolec, ragged, std::integral_constant<int, k - NXD>{}, qw, mine, nullptr);
+        });
+      });
+      advance(cd);
+      advance(cr);
+      wait_vmcnt<NWR>();  // this step's copies have landed
+      if constexpr (G::SPAIR < 0) store_stage(other, wbuf((s + 1) & 1), xbuf((s + 1) & 1));
+      lds_barrier();
+    };
+    int s = 0;
+    for (; s + 1 < nstages; s += 2) {
+      step(s, ra, rb);
+      step(s + 1, rb, ra);
+    }
+    if (s < nstages) step(s, ra, rb);
+    wait_vmcnt<0>();  // no copy into LDS may outlive the workgroup
+  };
   if (nstages > 0) {
-    if constexpr (G::XP) {
+    if constexpr (G::XP && G::PK) {
       if (cgs % G::CG == 0)
         main_loop_dma(std::false_type{});
       else
         main_loop_dma(std::true_type{});
+    } else if constexpr (G::XP) {
+      // OI(D)HW weights need C a multiple of the group (the planner's rule),
+      // so a ragged last chunk is the same test on channels or groups
+      if (a.C % G::CK == 0)
+        run_roles(std::false_type{}, main_loop_xo);
+      else
+        run_roles(std::true_type{}, main_loop_xo);
     } else {
       if (a.C % G::CK == 0)
-        run_roles(std::false_type{});
+        run_roles(std::false_type{}, main_loop);
       else
-        run_roles(std::true_type{});
+        run_roles(std::true_type{}, main_loop);
     }
   }
 

@@ -385,14 +385,16 @@ def test_cpack_argument_errors_without_gpu():
 def test_query_plan_packed_weights_and_cpack_flags():
     """PLAN_PACKED_W plans as a call given packed weights (packed MFMA tiles,
     no split without a workspace); PLAN_CPACK plans the channel-packed
-    layout's own tiles, which read packed weights: with OIDHW weights only
-    when a workspace can hold them packed, else the vector-ALU kernel."""
+    layout's own tiles: those that read packed weights when the weights are
+    packed or a workspace can hold them packed, else those that transpose
+    OIDHW weights in registers."""
     vae = (1, 512, 5, 64, 120, 512, 3, 3, 3, 1, 1, 1, 1, 1, 1, L.F16, 1, L.ALGO_AUTO)
     st, algo, tile, grid, ks = L.libconv_query_plan(*vae, L.PLAN_PACKED_W)
     assert st == 0 and algo == L.ALGO_IGEMM and ks == 1
     assert L.libconv_tile_name(tile).startswith("igemm16p_")
     st, algo, tile, grid, ks = L.libconv_query_plan(*vae, L.PLAN_CPACK)
-    assert st == 0 and algo == L.ALGO_DIRECT
+    assert st == 0 and algo == L.ALGO_IGEMM
+    assert L.libconv_tile_name(tile).startswith("igemm16xo_")
     ws = L.libconv_workspace_size(1, 512, 5, 64, 120, 512, 3, 3, 3, 1, 1, 1, 1, 1, 1, 1,
                                   L.F16, 1, L.ALGO_AUTO, L.PLAN_CPACK)
     assert ws >= L.libconv_packed_weight_bytes(512, 512, 3, 3, 3, L.F16)

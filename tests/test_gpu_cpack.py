@@ -140,6 +140,37 @@ def test_cpack_tiles(case, monkeypatch):
     _check(layer, x, w, b, yp, f"tile {tid}")
 
 
+# The tiles that read OI(D)HW weights (transposed in registers; no workspace
+# to pack them into): C a multiple of the channel group, ragged stages
+# (C not a multiple of the stage's 16 / 8 channels), ragged K, odd widths,
+# one-sided time padding.
+XO_CASES = [
+    (286, "f16", 24, 72, 4, 9, 40, (3, 3, 3), (1, 1, 1), (1, 1, 1), None, True),
+    (286, "bf16", 16, 64, 5, 7, 33, (3, 3, 3), (1, 1, 1), (2, 1, 1), 0, False),  # causal, odd W
+    (287, "f16", 40, 70, 1, 19, 72, (1, 3, 3), (1, 1, 1), (0, 1, 1), None, True),  # K % 8 != 0
+    (287, "bf16", 32, 136, 1, 11, 35, (1, 3, 3), (1, 1, 1), (0, 1, 1), None, False),
+    (288, "f16", 24, 72, 1, 21, 75, (1, 3, 3), (1, 2, 2), (0, 1, 1), None, True),
+    (289, "f16", 64, 200, 1, 7, 33, (1, 1, 1), (1, 1, 1), (0, 0, 0), None, True),
+    (289, "bf16", 72, 96, 3, 5, 16, (1, 1, 1), (1, 1, 1), (0, 0, 0), None, False),  # frames
+    (293, "f32", 12, 40, 1, 17, 40, (1, 3, 3), (1, 1, 1), (0, 1, 1), None, True),
+    (294, "f32", 8, 70, 1, 19, 67, (1, 3, 3), (1, 2, 2), (0, 1, 1), None, True),
+    (295, "f32", 36, 70, 1, 9, 31, (1, 1, 1), (1, 1, 1), (0, 0, 0), None, False),
+]
+
+
+@pytest.mark.parametrize("case", XO_CASES, ids=lambda c: f"t{c[0]}_{c[1]}_C{c[2]}_K{c[3]}")
+def test_cpack_tiles_unpacked_weights(case, monkeypatch):
+    import direct_implicit_gemm_amd as L
+    layer, tid = _case_layer(case)
+    monkeypatch.setenv("LIBCONV_FORCE_TILE", str(tid))
+    note(f"cpack tile {tid} {L.libconv_tile_name(tid)} (OI(D)HW weights): x={layer.x_shape} "
+         f"w={layer.w_shape} {layer.dtype} pad={layer.pad} back={layer.pad_t_back} "
+         f"stride={layer.stride} {layer.act}")
+    x, w, b = W.make_inputs(layer, 1200 + case[2] + case[3])
+    yp = _run_cpack(layer, x, w, b, packed_w=False)
+    _check(layer, x, w, b, yp, f"tile {tid}")
+
+
 AUTO_CASES = [
     # shapes no MFMA tile of the layout covers (5x5, 3x3 stride 2 in 3-D):
     # the vector-ALU kernel, with OIHW weights
