@@ -289,27 +289,32 @@ class LayerCalls:
         assert self.ws_n >= 0, l.name
         self.ws = torch.empty(max(self.ws_n, 1), dtype=torch.uint8, device=dev)
         self.plan_step = self.plan(self.ws_n, packed=False)
-        # weights packed once, for the kernel-only call (when a packed kernel runs)
+        # The kernel-only call: weights packed once beforehand (as a runtime
+        # with fixed weights does), when the layer has a tile that reads
+        # packed weights; else the step's own call.
         self.packed = None
-        if L.libconv_tile_name(self.plan_step[1]).startswith(("igemm16p", "igemm32p", "igemm16x",
-                                                               "igemm32x")):
-            self.packed = L.pack_weights(self.w)
-            kw_n = lib.libconv_workspace_size(*self.dims, *self.pads, *self.strides, self.dt,
-                                              self.act, L.ALGO_AUTO,
-                                              self.flags | L.PLAN_PACKED_W)
-            self.kws_n = max(kw_n, 0)
-            self.kws = torch.empty(max(self.kws_n, 1), dtype=torch.uint8, device=dev)
-            self.plan_kernel = self.plan(self.kws_n, packed=True)
-        else:
-            self.plan_kernel = self.plan_step
+        self.plan_kernel = self.plan_step
+        kw_n = lib.libconv_workspace_size(*self.dims, *self.pads, *self.strides, self.dt,
+                                          self.act, L.ALGO_AUTO, self.flags | L.PLAN_PACKED_W)
+        if kw_n >= 0:
+            kws_n = max(kw_n, 0)
+            plan_k = self.plan(kws_n, packed=True, must=False)
+            if plan_k is not None and L.libconv_tile_name(plan_k[1]).startswith(
+                    ("igemm16p", "igemm32p", "igemm16x_", "igemm32x_")):
+                self.packed = L.pack_weights(self.w)
+                self.kws_n = kws_n
+                self.kws = torch.empty(max(self.kws_n, 1), dtype=torch.uint8, device=dev)
+                self.plan_kernel = plan_k
         self.plan_export = self.plan(0, packed=False)
 
-    def plan(self, ws_bytes, packed):
+    def plan(self, ws_bytes, packed, must=True):
         l = self.layer
         pad = (sum(self.pads[:2]) // 2,) + self.pads[2:]   # the query takes one time pad
         st, algo, tile, grid, ks = self.L.libconv_query_plan(
             *self.dims, *pad, *self.strides, self.dt, self.act, self.L.ALGO_AUTO,
             self.flags | (self.L.PLAN_PACKED_W if packed else 0), ws_bytes)
+        if st != 0 and not must:
+            return None
         assert st == 0, (l.name, st)
         return algo, tile, grid, ks
 

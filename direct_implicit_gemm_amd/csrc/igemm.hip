@@ -226,6 +226,7 @@ struct TileDesc {
                   // built kernel; checked against the runtime by a GPU test)
   int one;        // 1: single-stage tile (the layer's input channels fit one stage)
   int pool;       // 1: can fuse the 2x2 max pooling into its epilogue
+  int w1;         // 1: OIHW weights through one register set (read one stage ahead)
   int lds;
   const char* name;
   LaunchFn fn[3];  // by libconv_dtype
@@ -253,9 +254,10 @@ constexpr OccFn occupier() {
 
 #define LIBCONV_TILE(ID, WIDE, KT, KH, KW, SH, SW, FLAT, BM, TH, TW, WM, WN, CG, PK, VX, EFF,   \
                      OCC, NAME)                                                                 \
-  {ID, WIDE, KT, KH, KW, SH, SW, FLAT, BM, TH, TW, CG, (PK) & 1, VX, EFF, OCC, (PK) >> 1,        \
+  {ID, WIDE, KT, KH, KW, SH, SW, FLAT, BM, TH, TW, CG, (PK) & 1, VX, EFF, OCC, ((PK) >> 1) & 1, \
    !(FLAT) && Cfg<WIDE ? DT_F16 : DT_F32, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK,       \
                   VX>::POOLABLE,                                                                \
+   ((PK) >> 2) & 1,                                                                             \
    Cfg<WIDE ? DT_F16 : DT_F32, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK, VX>::LDS, NAME, \
    {launcher<DT_F32, WIDE, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK, VX>(),               \
     launcher<DT_F16, WIDE, KT, KH, KW, SH, SW, BM, TH, TW, WM, WN, CG, PK, VX>(),               \
@@ -433,6 +435,10 @@ static bool split_ok(const TileDesc& t, const Problem& p, int ksplit) {
 // writing and reading the fp32 partial sums once and writing the output.
 constexpr double kFirstUs = 4.5;
 constexpr double kStageUs = 1.6;
+// A one-weight-set tile reads the next stage's weights within the stage, so
+// a stage's chain is longer when no other workgroup hides it (fitted to the
+// 1280-channel UNet layer, 160 tiles: 140 vs 100 us for the two-set tile).
+constexpr double kStageUsW1 = 2.2;
 static double estimate_us(const TileDesc& t, const Problem& p, const TileCounts& c, int ksplit) {
   const double ck = t.CG * (t.wide ? 8 : 4);
   const int chunks = chunks_of(t, p);
@@ -440,7 +446,7 @@ static double estimate_us(const TileDesc& t, const Problem& p, const TileCounts&
   const double unit_flop = 2.0 * t.BM * t.TH * t.TW * cps * ck * p.KT * p.KH * p.KW;
   const double cu_flop_per_us = (t.wide ? 4096.0 : 256.0) * 2400.0 * (t.eff / 100.0);
   const double unit_us = unit_flop / cu_flop_per_us;
-  const double latency_us = kFirstUs + kStageUs * cps * p.KT;
+  const double latency_us = kFirstUs + (t.w1 ? kStageUsW1 : kStageUs) * cps * p.KT;
   const double cus = p.cus > 0 ? p.cus : 256.0;
   const double per_cu = std::ceil(c.total * ksplit / cus);
   const double full_rounds = std::floor(per_cu / t.occ);

@@ -132,6 +132,11 @@ struct IgemmArgs {
   uint32_t x_bytes, w_bytes, b_bytes, y_bytes, part_bytes;
 };
 
+// Slot pairs of a stage over which a one-weight-set tile (Cfg::W1) reads the
+// next stage's weights: the rest of the stage, up to SPAIR, covers their
+// latency.
+constexpr int kW1Pairs = 2;
+
 template <int DT_, int KT_, int KH_, int KW_, int SH_, int SW_, int BM_, int TH_, int TW_,
           int WM_, int WN_, int CG_, int PK_, int VX_>
 struct Cfg {
@@ -141,6 +146,11 @@ struct Cfg {
   // of the layer in one stage; one LDS buffer, no overlap machinery)
   static constexpr bool PK = (PK_ & 1) != 0;
   static constexpr bool ONE = (PK_ & 2) != 0;
+  // PK_ bit 2 (OIHW / OIDHW weights): the weights go through one register
+  // set, read at the start of a stage for the next one and transposed into
+  // LDS before slot pair SPAIR (the input keeps two sets, two stages ahead),
+  // which frees a set of weight registers for a second workgroup per CU
+  static constexpr bool W1 = (PK_ & 4) != 0;
   static constexpr bool VX = VX_ == 1;
   // VX_ == 2: channel-packed activations, x [N][C/SE][T][H][W][SE] and y
   // likewise over C_out.  A halo row of one channel group is then a run of
@@ -241,6 +251,7 @@ struct Cfg {
   static_assert(BM <= kPackAlign, "packed channel padding covers one tile");
   static_assert(!W3 || (TS2 == 9 && EB == 2), "OIDHW weights: 3x3 spatial taps, 16-bit types");
   static_assert(!XP || !ONE, "channel-packed tiles run two stages");
+  static_assert(!W1 || (!PK && !XP && !ONE && NPAIR >= 5), "one weight set: OIHW tiles of 5+ pairs");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -346,8 +357,10 @@ __device__ __forceinline__ void store_slots(unsigned char* base, int slot_stride
   }
 }
 
+// One-weight-set tiles are built for two workgroups per CU (the second
+// launch bound holds the register allocation to half the file).
 template <class G>
-__global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
+__global__ __launch_bounds__(kThreads, G::W1 ? 2 : 1) void igemm_kernel(IgemmArgs a) {
   using E = Elem<G::DT>;
   constexpr int EB = G::EB;
   constexpr int SE = G::SE;
@@ -610,10 +623,14 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
 
   // Registers of a stage -> LDS (weights into `wdst` unless they were copied
   // there directly, the input halo into `xdst`).
-  auto store_stage = [&](StageRegs<G>& r, unsigned char* wdst, unsigned char* xdst)
+  // `part` (compile time): bit 0 the input, bit 1 the weights
+  auto store_part = [&](auto partc, StageRegs<G>& r, unsigned char* wdst, unsigned char* xdst)
       __attribute__((always_inline)) {
+    constexpr bool SW_ = (decltype(partc)::value & 2) != 0;  // weights
+    constexpr bool SX_ = (decltype(partc)::value & 1) != 0;  // input
+    constexpr int WP = SW_ ? G::WPASS : 0, XPS = SX_ ? G::XPASS : 0;
 #pragma unroll
-    for (int i = 0; i < G::WPASS; ++i) {
+    for (int i = 0; i < WP; ++i) {
 #pragma unroll
       for (int k = 0; k < (G::W3 ? SE : G::TS); ++k) pin(r.wv[i][k]);
       if constexpr (G::W3) {
@@ -622,7 +639,7 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
       }
     }
 #pragma unroll
-    for (int i = 0; i < G::XPASS; ++i)
+    for (int i = 0; i < XPS; ++i)
 #pragma unroll
       for (int j = 0; j < SE; ++j) {
         if constexpr (G::VX) {
@@ -635,7 +652,7 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
     // lanes of a wave hold consecutive channels, so each 16-byte store is
     // conflict-free
 #pragma unroll
-    for (int i = 0; i < G::WPASS; ++i) {
+    for (int i = 0; i < WP; ++i) {
       const int u = tid - 64 * G::W0 + i * kThreads;
       unsigned char* base = wdst + ((u / G::BM) * G::BM + u % G::BM) * 16;
       if constexpr (G::W3) {
@@ -663,7 +680,7 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
     }
     // input halo: gather the SE channels of each pixel into one 16-byte word
 #pragma unroll
-    for (int i = 0; i < G::XPASS; ++i) {
+    for (int i = 0; i < XPS; ++i) {
       const int u = tid + i * kThreads;
       if constexpr (G::VX) {
         // unit u covers the RUN words of its run in its row
@@ -695,6 +712,11 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
         if (u < G::XUNITS) *reinterpret_cast<u32x4_t*>(xdst + u * 16) = v;
       }
     }
+  };
+
+  auto store_stage = [&](StageRegs<G>& r, unsigned char* wdst, unsigned char* xdst)
+      __attribute__((always_inline)) {
+    store_part(std::integral_constant<int, 3>{}, r, wdst, xdst);
   };
 
   // ---- MFMA operand addressing
@@ -816,6 +838,66 @@ __global__ __launch_bounds__(kThreads) void igemm_kernel(IgemmArgs a) {
       store_stage(r1, wbuf(0), xbuf(0));
       lds_barrier();
       compute(wbuf(0), xbuf(0), [](auto) {});
+      return;
+    }
+    if constexpr (G::W1) {
+      // One weight register set: stage s+1's weights are read in the first
+      // kW1Pairs slot pairs of stage s and go to LDS at SPAIR with the input
+      // of stage s+1 (read during stage s-1); the input of stage s+2 is read
+      // over the remaining pairs.  Weight reads precede the step's input
+      // reads, so waiting for all but the input reads issued so far waits
+      // for the weights.
+      constexpr int PW = kW1Pairs;
+      constexpr int NXR = (role & 1) ? NXP : 0;  // this wave's input reads per stage
+      StageRegs<G> ra, rb, wr;
+      Cursor cw{chunk0, kt_lo, 0}, cx{chunk0, kt_lo, 0};
+      {
+        const Src qw = w_src(cw.chunk, cw.kt);
+        static_for<0, NWP>([&](auto kc) { read_w(rolec, ragged, kc, qw, wr, nullptr); });
+        advance(cw);
+        const Src qx0 = x_src(cx.chunk, cx.kt);
+        static_for<0, NXP>([&](auto kc) { read_x(rolec, ragged, kc, qx0, ra); });
+        advance(cx);
+        const Src qx1 = x_src(cx.chunk, cx.kt);
+        static_for<0, NXP>([&](auto kc) { read_x(rolec, ragged, kc, qx1, rb); });
+        advance(cx);
+      }
+      wait_vmcnt<NXR>();  // stage 0 is in; stage 1's input may be in flight
+      store_part(std::integral_constant<int, 2>{}, wr, wbuf(0), nullptr);
+      store_part(std::integral_constant<int, 1>{}, ra, nullptr, xbuf(0));
+      lds_barrier();
+      auto step1 = [&](int s, StageRegs<G>& mine, StageRegs<G>& other)
+          __attribute__((always_inline)) {
+        const Src qw = w_src(cw.chunk, cw.kt);  // stage s+1
+        const Src qx = x_src(cx.chunk, cx.kt);  // stage s+2
+        compute(wbuf(s & 1), xbuf(s & 1), [&](auto pc) {
+          constexpr int p = decltype(pc)::value;
+          if constexpr (p == G::SPAIR) {
+            // the input reads issued so far in this step: pairs PW .. SPAIR-1
+            constexpr int xin = (role & 1) ? (G::SPAIR - PW) * NXP / (G::NPAIR - PW) : 0;
+            wait_vmcnt<xin>();
+            store_part(std::integral_constant<int, 2>{}, wr, wbuf((s + 1) & 1), nullptr);
+            store_part(std::integral_constant<int, 1>{}, other, nullptr, xbuf((s + 1) & 1));
+          }
+          if constexpr (p < PW) {
+            static_for<p * NWP / PW, (p + 1) * NWP / PW>(
+                [&](auto kc) { read_w(rolec, ragged, kc, qw, wr, nullptr); });
+          } else {
+            static_for<(p - PW) * NXP / (G::NPAIR - PW), (p - PW + 1) * NXP / (G::NPAIR - PW)>(
+                [&](auto kc) { read_x(rolec, ragged, kc, qx, mine); });
+          }
+        });
+        advance(cw);
+        advance(cx);
+        lds_barrier();
+      };
+      int s = 0;
+      for (; s + 1 < nstages; s += 2) {
+        step1(s, ra, rb);
+        step1(s + 1, rb, ra);
+      }
+      if (s < nstages) step1(s, ra, rb);
+      wait_vmcnt<0>();
       return;
     }
     StageRegs<G> ra, rb;
