@@ -55,6 +55,7 @@ PEAK_HBM_GBS = 8000.0
 PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6, "bf16": 2516.6}   # dense MFMA
 METRIC = "conv fwd effective TFLOP/s + HBM GB/s per layer, % of binding MI355X roofline"
 FLUSH_MB = 512
+SPIN_CYCLES = 300_000   # GPU spin after the scratch write (cycles of torch.cuda._sleep)
 
 WORKLOAD_TEXT = {
     "conv1": "single conv2d fp32 N=1 3x32x32 -> 8, 3x3 s1 p1, bias",
@@ -433,12 +434,22 @@ def main():
 
     Ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
+    def evict():
+        """The cold protocol's scratch write, then a GPU spin of about 150 us:
+        both outside the event pair.  The spin keeps the GPU busy while the host
+        enqueues the first event and the call, so that the event pair times the
+        GPU's work and not the host's enqueue latency (a workspace call's pack
+        and convolution kernels otherwise showed 7-20 us of idle GPU between
+        them and the first event)."""
+        scratch.zero_()
+        torch.cuda._sleep(SPIN_CYCLES)
+
     def cold(fn, reps):
         """reps timed calls of fn, each after the scratch write, events on the
         launch stream; returns the per-call times in microseconds."""
         pairs = []
         for _ in range(reps):
-            scratch.zero_()                       # outside the event pair
+            evict()                               # outside the event pair
             e0, e1 = Ev(), Ev()
             e0.record()
             fn()
@@ -455,7 +466,7 @@ def main():
     for _ in range(K):
         lp = []
         for i, c in enumerate(calls):
-            scratch.zero_()
+            evict()
             e0, e1 = Ev(), Ev()
             e0.record()
             c.step(stream, x_of(i))
@@ -588,9 +599,9 @@ def main():
         "data": "synthetic (seeded; shapes and value distributions of the workload)",
         "config": {"workload": args.workload, "description": WORKLOAD_TEXT[args.workload],
                    "chained": chained,
-                   "timing": f"cold: {FLUSH_MB} MB scratch write before each call, outside "
-                             "the event pair; ms_per_step = median over steps of the summed "
-                             "layer times",
+                   "timing": f"cold: {FLUSH_MB} MB scratch write and a GPU spin (the host "
+                             "enqueues the call meanwhile) before each call, outside the event "
+                             "pair; ms_per_step = median over steps of the summed layer times",
                    "ms_per_step_min": round(min(step_us) / 1000.0, 5),
                    "warm_ms_per_step_eager": round(warm_eager, 5),
                    "warm_ms_per_step_graph": None if warm_graph is None else round(warm_graph, 5),
