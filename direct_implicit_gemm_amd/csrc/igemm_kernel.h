@@ -142,6 +142,9 @@ template <int DT_, int KT_, int KH_, int KW_, int SH_, int SW_, int BM_, int TH_
 struct Cfg {
   static constexpr int DT = DT_, KT = KT_, KH = KH_, KW = KW_, SH = SH_, SW = SW_;
   static constexpr int BM = BM_, TH = TH_, TW = TW_, WM = WM_, WN = WN_, CG = CG_;
+  // waves of a workgroup (a WM x WN grid) and its threads
+  static constexpr int NWV = WM * WN;
+  static constexpr int NT = 64 * NWV;
   // PK_ bit 0: packed weights; bit 1: single-stage tile (all input channels
   // of the layer in one stage; one LDS buffer, no overlap machinery)
   static constexpr bool PK = (PK_ & 1) != 0;
@@ -185,7 +188,7 @@ struct Cfg {
   // channel-packed input: CG x HR x HC words per stage, 64 per wave-wide
   // direct-to-LDS copy (the buffer is rounded up to whole copies)
   static constexpr int XDMA = XP ? (CG * HR * HC + 63) / 64 : 0;
-  static constexpr int NXDMA = (XDMA + 3) / 4;     // copies per wave
+  static constexpr int NXDMA = (XDMA + NWV - 1) / NWV;  // copies per wave
   static constexpr int XBYTES = XP ? XDMA * 1024 : CG * XPLANE * 16;
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int FA = WTM / 32, FB = WTN / 32;
@@ -198,7 +201,7 @@ struct Cfg {
   // load of its first 8 taps and one 2-byte load of the ninth.
   static constexpr bool W3 = !PK && KT > 1;
   static constexpr int WUNITS = PK ? 0 : BM * CG;
-  static constexpr int WPASS = PK ? 0 : (WUNITS + kThreads - 1) / kThreads;
+  static constexpr int WPASS = PK ? 0 : (WUNITS + NT - 1) / NT;
   static constexpr int NWREG = PK ? 0 : W3 ? WPASS * SE * 2 : WPASS * TS;
   // weight staging from packed weights: NSLOT runs of BM 16-byte vectors,
   // moved as 1 KB chunks (one wave, one instruction each), NDMA per weight
@@ -208,7 +211,7 @@ struct Cfg {
   // input staging: one unit = one run (VX) or one halo pixel of one channel
   // group; VX units come in blocks of 8 rows x NRUN runs
   static constexpr int XUNITS = VX ? (NROWS + 7) / 8 * 8 * NRUN : CG * HR * HC;
-  static constexpr int XPASS = XP ? 0 : (XUNITS + kThreads - 1) / kThreads;
+  static constexpr int XPASS = XP ? 0 : (XUNITS + NT - 1) / NT;
   static constexpr int XPASS1 = XPASS > 0 ? XPASS : 1;  // array extent
   // Which waves stage what.  When a stage's input units fit in fewer than
   // four waves, only those (the first XW) read the input, so that no wave
@@ -219,21 +222,21 @@ struct Cfg {
   // writes together) finished each stage last and held the others at the
   // barrier (measured per wave on the 3x3x3 video-VAE layers).  OIHW weight
   // units go to the last WW waves.  A wave may have both roles.
-  static constexpr int XW = (VX && XPASS == 1) ? (XUNITS + 63) / 64 : 4;
-  static constexpr int WW = PK ? 4 : (WPASS == 1 ? (WUNITS + 63) / 64 : 4);
-  static constexpr int W0 = 4 - WW;                // first weight wave
+  static constexpr int XW = (VX && XPASS == 1) ? (XUNITS + 63) / 64 : NWV;
+  static constexpr int WW = PK ? NWV : (WPASS == 1 ? (WUNITS + 63) / 64 : NWV);
+  static constexpr int W0 = NWV - WW;              // first weight wave
   static constexpr int NDMA = PK ? (WCHUNKS + WW - 1) / WW : 0;
   static constexpr int DMA_PAD =
-      ((PK && WCHUNKS % WW != 0) || (XP && XDMA % 4 != 0)) ? 1024 : 0;
+      ((PK && WCHUNKS % WW != 0) || (XP && XDMA % NWV != 0)) ? 1024 : 0;
   // LDS: two weight and two input buffers (one of each for single-stage tiles)
   static constexpr int NBUF = ONE ? 1 : 2;
-  // the vectorised epilogue reuses LDS as four wave-private 32x32 tiles
-  static constexpr int EPI_LDS = 4 * 32 * (32 + 16 / EB) * EB;
+  // the vectorised epilogue reuses LDS as wave-private 32x32 tiles
+  static constexpr int EPI_LDS = NWV * 32 * (32 + 16 / EB) * EB;
   // 2x2 max pooling in the epilogue: a wave's consecutive blocks are
   // consecutive output rows (one 32-pixel block per tile row) in even-odd
   // pairs; two fp32 32x36 LDS tiles per wave
-  static constexpr bool POOLABLE = BPR == 1 && FB % 2 == 0 && TH % 2 == 0 && KT == 1;
-  static constexpr int EPI_POOL_LDS = POOLABLE ? 4 * 2 * 32 * 36 * 4 : 0;
+  static constexpr bool POOLABLE = NWV == 4 && BPR == 1 && FB % 2 == 0 && TH % 2 == 0 && KT == 1;
+  static constexpr int EPI_POOL_LDS = POOLABLE ? NWV * 2 * 32 * 36 * 4 : 0;
   static constexpr int STAGES_LDS = NBUF * (WBYTES + XBYTES) + DMA_PAD;
   static constexpr int LDS0 = STAGES_LDS > EPI_LDS ? STAGES_LDS : EPI_LDS;
   static constexpr int LDS = LDS0 > EPI_POOL_LDS ? LDS0 : EPI_POOL_LDS;
@@ -244,7 +247,7 @@ struct Cfg {
   // latency before the end-of-stage barrier; -1: after the last pair
   static constexpr int SPAIR = NPAIR >= 3 ? NPAIR - 2 : -1;
 
-  static_assert(WM * WN == 4, "four waves");
+  static_assert(NWV == 4 || (NWV == 8 && !XP && !ONE), "four waves, or eight");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
   static_assert(TW % 32 == 0, "tile rows are whole 32-pixel blocks");
   static_assert(BM % 64 == 0 || !PK, "packed tiles move whole 64-channel chunks");
@@ -360,7 +363,7 @@ __device__ __forceinline__ void store_slots(unsigned char* base, int slot_stride
 // One-weight-set tiles are built for two workgroups per CU (the second
 // launch bound holds the register allocation to half the file).
 template <class G>
-__global__ __launch_bounds__(kThreads, G::W1 ? 2 : 1) void igemm_kernel(IgemmArgs a) {
+__global__ __launch_bounds__(G::NT, G::W1 ? 2 : 1) void igemm_kernel(IgemmArgs a) {
   using E = Elem<G::DT>;
   constexpr int EB = G::EB;
   constexpr int SE = G::SE;
@@ -457,7 +460,7 @@ __global__ __launch_bounds__(kThreads, G::W1 ? 2 : 1) void igemm_kernel(IgemmArg
   int xgrp[G::XPASS1];
 #pragma unroll
   for (int i = 0; i < G::XPASS; ++i) {
-    const int u = tid + i * kThreads;
+    const int u = tid + i * G::NT;
     if constexpr (G::VX) {
       const int run = (u >> 3) % G::NRUN;
       const int row = (u >> 3) / G::NRUN * 8 + (u & 7);
@@ -482,7 +485,7 @@ __global__ __launch_bounds__(kThreads, G::W1 ? 2 : 1) void igemm_kernel(IgemmArg
     }
   }
   const int ch_bytes = plane * EB;       // scalar offset between channels
-  // Channel-packed input: copy k of this wave is words (wave + 4k) * 64 +
+  // Channel-packed input: copy k of this wave is words (wave + NWV k) * 64 +
   // lane of the stage's halo, word f = (g * HR + hr) * HC + hc, i.e. the
   // 16-byte channel group g of halo pixel (hr, hc); one offset per copy,
   // relative to the stage's first channel group at the stage's frame.
@@ -492,7 +495,7 @@ __global__ __launch_bounds__(kThreads, G::W1 ? 2 : 1) void igemm_kernel(IgemmArg
   if constexpr (G::XP) {
 #pragma unroll
     for (int k = 0; k < G::NXDMA; ++k) {
-      const int f = (wave + 4 * k) * 64 + lane;
+      const int f = (wave + G::NWV * k) * 64 + lane;
       const int g = f / (G::HR * G::HC);
       const int hr = (f / G::HC) % G::HR, hc = f % G::HC;
       const int ih = ih0 + hr, iw = iw0 + hc;
@@ -506,7 +509,7 @@ __global__ __launch_bounds__(kThreads, G::W1 ? 2 : 1) void igemm_kernel(IgemmArg
   int wgrp[G::WPASS > 0 ? G::WPASS : 1];
 #pragma unroll
   for (int i = 0; i < G::WPASS; ++i) {
-    const int u = tid - 64 * G::W0 + i * kThreads;  // weight units start at the first weight wave
+    const int u = tid - 64 * G::W0 + i * G::NT;  // weight units start at the first weight wave
     const int g = u / G::BM, col = u % G::BM;
     const int co = co0 + col;
     const bool ok = u >= 0 && u < G::WUNITS && co < a.K;
@@ -613,7 +616,7 @@ __global__ __launch_bounds__(kThreads, G::W1 ? 2 : 1) void igemm_kernel(IgemmArg
   auto read_xd = [&](auto ragged, auto kc, const Src& q, unsigned char* xdst)
       __attribute__((always_inline)) {
     constexpr int k = decltype(kc)::value;
-    const int ins = wave + 4 * k;
+    const int ins = wave + G::NWV * k;
     int off = xdo[k];
     if constexpr (decltype(ragged)::value)
       off = guard_offset(true, q.ci0 / SE + xdg[k] < cgs ? off : kFar);
@@ -653,7 +656,7 @@ __global__ __launch_bounds__(kThreads, G::W1 ? 2 : 1) void igemm_kernel(IgemmArg
     // conflict-free
 #pragma unroll
     for (int i = 0; i < WP; ++i) {
-      const int u = tid - 64 * G::W0 + i * kThreads;
+      const int u = tid - 64 * G::W0 + i * G::NT;
       unsigned char* base = wdst + ((u / G::BM) * G::BM + u % G::BM) * 16;
       if constexpr (G::W3) {
         // slot of spatial tap t: word m = channels 2m, 2m+1 at tap t
@@ -681,7 +684,7 @@ __global__ __launch_bounds__(kThreads, G::W1 ? 2 : 1) void igemm_kernel(IgemmArg
     // input halo: gather the SE channels of each pixel into one 16-byte word
 #pragma unroll
     for (int i = 0; i < XPS; ++i) {
-      const int u = tid + i * kThreads;
+      const int u = tid + i * G::NT;
       if constexpr (G::VX) {
         // unit u covers the RUN words of its run in its row
         const int run = (u >> 3) % G::NRUN;
@@ -978,7 +981,7 @@ __global__ __launch_bounds__(kThreads, G::W1 ? 2 : 1) void igemm_kernel(IgemmArg
     using R1 = std::integral_constant<int, 1>;
     using R2 = std::integral_constant<int, 2>;
     using R3 = std::integral_constant<int, 3>;
-    if constexpr (G::XW == 4 && G::W0 == 0) {
+    if constexpr (G::XW == G::NWV && G::W0 == 0) {
       loop(ragged, R3{});
     } else {
       if (xwave && wwave) {
@@ -986,7 +989,7 @@ __global__ __launch_bounds__(kThreads, G::W1 ? 2 : 1) void igemm_kernel(IgemmArg
       } else if (xwave) {
         if constexpr (G::W0 > 0) loop(ragged, R1{});
       } else {
-        if constexpr (G::XW < 4) loop(ragged, R2{});
+        if constexpr (G::XW < G::NWV) loop(ragged, R2{});
       }
     }
   };

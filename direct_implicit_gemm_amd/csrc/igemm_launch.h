@@ -10,7 +10,7 @@ namespace igk {
 
 template <class G>
 hipError_t launch_cfg(const IgemmArgs& a, unsigned grid, hipStream_t s) {
-  hipLaunchKernelGGL(igemm_kernel<G>, dim3(grid), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(igemm_kernel<G>, dim3(grid), dim3(G::NT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -19,7 +19,7 @@ hipError_t launch_cfg(const IgemmArgs& a, unsigned grid, hipStream_t s) {
 template <class G>
 int occupancy_cfg() {
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, igemm_kernel<G>, kThreads, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, igemm_kernel<G>, G::NT, 0) !=
       hipSuccess) {
     (void)hipGetLastError();
     return -1;

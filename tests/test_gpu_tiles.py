@@ -59,7 +59,7 @@ def _one_stage_width(tid: int, kdig: str, wide: bool) -> int:
 
 def _layer_for(tid: int, name: str, ragged: bool) -> W.Layer:
     """A small layer that the tile `name` fits."""
-    m = re.match(r"igemm(16|32)(p?)_k(\d+)(s(\d))?_m(\d+)w?_n(\d+)x?(\d+)?(_c8)?(_e)?(_one)?(_w1)?$", name)
+    m = re.match(r"igemm(16|32)(p?)_k(\d+)(s(\d))?_m(\d+)w?_n(\d+)x?(\d+)?(_c8)?(_e)?(_one)?(_w1)?(_8w)?$", name)
     assert m, name
     wide, packed, kdig = m.group(1) == "16", m.group(2) == "p", m.group(3)
     stride, bm = m.group(5), int(m.group(6))
