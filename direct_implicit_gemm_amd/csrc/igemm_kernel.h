@@ -247,7 +247,7 @@ struct Cfg {
   // latency before the end-of-stage barrier; -1: after the last pair
   static constexpr int SPAIR = NPAIR >= 3 ? NPAIR - 2 : -1;
 
-  static_assert(NWV == 4 || (NWV == 8 && !XP && !ONE), "four waves, or eight");
+  static_assert(NWV == 4 || (NWV == 8 && !ONE), "four waves, or eight");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
   static_assert(TW % 32 == 0, "tile rows are whole 32-pixel blocks");
   static_assert(BM % 64 == 0 || !PK, "packed tiles move whole 64-channel chunks");
@@ -360,10 +360,11 @@ __device__ __forceinline__ void store_slots(unsigned char* base, int slot_stride
   }
 }
 
-// One-weight-set tiles are built for two workgroups per CU (the second
-// launch bound holds the register allocation to half the file).
+// Four-wave one-weight-set tiles are built for two workgroups per CU (the
+// second launch bound holds the register allocation to half the file; an
+// eight-wave workgroup already holds two waves per SIMD).
 template <class G>
-__global__ __launch_bounds__(G::NT, G::W1 ? 2 : 1) void igemm_kernel(IgemmArgs a) {
+__global__ __launch_bounds__(G::NT, (G::W1 && G::NWV == 4) ? 2 : 1) void igemm_kernel(IgemmArgs a) {
   using E = Elem<G::DT>;
   constexpr int EB = G::EB;
   constexpr int SE = G::SE;
