@@ -40,6 +40,14 @@ CASES = [  # channel counts give 10 chunks of a stage, so every split count 2..4
     ("f16_k1", "f16", 2, 600, 1, 7, 40, 130, 1, 1, (0, 0, 0), (1, 1, 1), "relu", 221, False),
     ("f16_k333_packed", "f16", 1, 152, 4, 7, 40, 64, 3, 3, (1, 1, 1), (1, 1, 1), "relu", 262,
      True),
+    # eight-wave packed tiles (128 channels x 256 pixels; K ragged over two channel tiles)
+    ("bf16_k3s1_packed_8w", "bf16", 1, 156, 1, 9, 48, 136, 1, 3, (0, 1, 1), (1, 1, 1), "relu",
+     277, True),
+    ("f16_k333_packed_8w", "f16", 1, 152, 4, 7, 40, 136, 3, 3, (1, 1, 1), (1, 1, 1), "none", 259,
+     True),
+    # OI(D)HW weights through one register set
+    ("f16_k3s1_w1", "f16", 2, 152, 1, 11, 40, 72, 1, 3, (0, 1, 1), (1, 1, 1), "none", 207, True),
+    ("bf16_k333_w1", "bf16", 1, 152, 4, 7, 40, 64, 3, 3, (1, 1, 1), (1, 1, 1), "relu", 266, True),
 ]
 
 
