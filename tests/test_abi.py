@@ -188,6 +188,23 @@ def test_3d_layers_dispatch_to_mfma_tiles_with_and_without_workspace():
         assert st == 0 and L.libconv_tile_name(tile).startswith("igemm16p_k333")
 
 
+WIDE_LAYERS = ("c3_A", "c4_A", "c4_B", "c5_A", "c5_B")
+
+
+@pytest.mark.parametrize("cpack", [False, True])
+@pytest.mark.parametrize("name", WIDE_LAYERS)
+def test_wide_layers_stay_on_the_matrix_cores_without_a_workspace(name, cpack):
+    """Without a workspace (so with OI(D)HW weights and no split) every
+    wide workload layer still plans an MFMA tile, in the plain layout and in
+    the channel-packed one: the tiles that transpose the weights in
+    registers, never the vector-ALU kernel."""
+    flags = L.PLAN_CPACK if cpack else 0
+    st, algo, tile, grid, ks = L.libconv_query_plan(*_layer_args(name), flags, 0)
+    nm = L.libconv_tile_name(tile)
+    assert st == 0 and algo == L.ALGO_IGEMM and ks == 1, (name, cpack, nm)
+    assert nm.startswith(("igemm16xo_",) if cpack else ("igemm16_",)), (name, cpack, nm)
+
+
 def test_tile_occupancy_query_without_gpu():
     """The cost model's occupancy column is a host query; unknown ids and
     dtypes a tile does not run give -1."""
