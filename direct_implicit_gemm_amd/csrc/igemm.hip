@@ -124,6 +124,61 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(PackArgs a) {
   store_packed<SE, TS, 0>(pr, (((co >> 6) * a.G + g) * TS * 64 + (co & 63)) * 16, 64 * 16, v);
 }
 
+// The same packing when C is a multiple of the channel group: one workgroup
+// per block of 64 output channels x one channel group.  The block's 64 rows
+// of SE * TS contiguous elements are read whole (consecutive lanes read
+// consecutive 16-byte pieces of a row) into LDS, rows one dword apart in
+// banks; then each thread takes one output channel and every fourth tap,
+// gathers the SE channels of each of its taps from the row and writes the
+// slot vector.  Lanes hold consecutive output channels, so each store of a
+// wave writes 1 KB contiguous, as above.
+template <int DT, int TS>
+__global__ __launch_bounds__(kThreads) void pack_rows_kernel(PackArgs a) {
+  using E = Elem<DT>;
+  constexpr int SE = Mma<DT>::SE;
+  constexpr int EB = E::bytes;
+  constexpr int ROWW = SE * TS * EB / 4 + 1;  // row pitch in dwords (odd: no bank conflicts)
+  __shared__ uint32_t rows[64 * ROWW];
+  const int g = blockIdx.x % a.G, cb = blockIdx.x / a.G;
+  const int tid = threadIdx.x;
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(a.w, a.w_bytes);
+  const __amdgpu_buffer_rsrc_t pr = make_rsrc(a.wp, a.wp_bytes);
+#pragma unroll
+  for (int v0 = 0; v0 < 64 * TS; v0 += kThreads) {
+    const int v = v0 + tid;
+    if (v < 64 * TS) {
+      const int row = v / TS, k = v % TS;
+      const int co = cb * 64 + row;
+      const u32x4_t x = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                       wr, guard_offset(co < a.K, (co * a.C + g * SE) * TS * EB + k * 16), 0, 0));
+#pragma unroll
+      for (int m = 0; m < 4; ++m) rows[row * ROWW + k * 4 + m] = x[m];
+    }
+  }
+  __syncthreads();
+  const int co_l = tid & 63;
+  const uint32_t* r = rows + co_l * ROWW;
+  auto elem = [&](int c, int t) -> uint32_t {  // element (channel c, tap t) of the row
+    const int e = c * TS + t;
+    if constexpr (EB == 4) {
+      return r[e];
+    } else {
+      const uint32_t d = r[e >> 1];
+      return (e & 1) ? (d >> 16) : (d & 0xffffu);
+    }
+  };
+#pragma unroll
+  for (int t = tid >> 6; t < TS; t += kThreads / 64) {
+    u32x4_t o;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      o[m] = EB == 4 ? elem(m, t) : (elem(2 * m, t) | (elem(2 * m + 1, t) << 16));
+    __builtin_amdgcn_raw_buffer_store_b128(o, pr, (((cb * a.G + g) * TS + t) * 64 + co_l) * 16, 0,
+                                           0);
+  }
+}
+
 // ------------------------------------------------------------ split-K sum
 // y[e] = act(b[co] + sum_{s < S} part[s][e]) rounded once to the storage
 // dtype, the slices added in order s = 0, 1, ... (so the result does not
@@ -335,7 +390,10 @@ using PackFn = hipError_t (*)(const PackArgs&, unsigned, hipStream_t);
 
 template <int DT, int TS>
 hipError_t launch_pack(const PackArgs& a, unsigned grid, hipStream_t s) {
-  hipLaunchKernelGGL((pack_kernel<DT, TS>), dim3(grid), dim3(kThreads), 0, s, a);
+  if (a.C % Mma<DT>::SE == 0)  // whole groups: block-wise, rows read whole
+    hipLaunchKernelGGL((pack_rows_kernel<DT, TS>), dim3(a.Kp / 64 * a.G), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((pack_kernel<DT, TS>), dim3(grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -430,8 +488,8 @@ static bool split_ok(const TileDesc& t, const Problem& p, int ksplit) {
 // (fitted to single-round launches on MI355X: a one-stage 1x1 tile takes 5-7
 // us, a four-stage 3x3 tile 10-12 us).  Packed tiles on OIHW weights add the
 // pack kernel into the caller's workspace (a launch, plus reading and
-// writing the weights once; fitted to the pack kernel's measured times, 10 us
-// for 14 MB and 19 us for 30 MB).  A split adds the sum kernel: a launch, plus
+// writing the weights once; fitted to the pack kernel's measured times, 6 us
+// for 0.9 MB and 9 us for 14 MB).  A split adds the sum kernel: a launch, plus
 // writing and reading the fp32 partial sums once and writing the output.
 constexpr double kFirstUs = 4.5;
 constexpr double kStageUs = 1.6;
@@ -455,7 +513,7 @@ static double estimate_us(const TileDesc& t, const Problem& p, const TileCounts&
   if (rest > 0) us += std::max(rest * unit_us, latency_us);
   if (t.packed && !p.wp) {
     const double wbytes = (double)packed_weight_bytes(p.C, p.K, p.KT, p.KH, p.KW, p.dtype);
-    us += 3.0 + 2.0 * wbytes / 3.8e6;
+    us += 5.0 + 2.0 * wbytes / 6.5e6;
   }
   if (ksplit > 1)
     us += 8.0 + (2.0 * part_bytes(p, ksplit) + out_elems(p) * dtype_bytes(p.dtype)) / 4.0e6;

@@ -39,6 +39,9 @@ def _expected_packed(w: np.ndarray, se: int, kp_align: int = 128) -> np.ndarray:
     ("f16", 16, 128, (3, 3)), ("bf16", 24, 40, (3, 3)), ("f16", 12, 8, (3, 3, 3)),
     ("f32", 8, 130, (3, 3)), ("f32", 6, 5, (1, 1)), ("bf16", 128, 128, (3, 3, 3)),
     ("f16", 3, 7, (1, 1)),
+    # several 64-channel blocks and groups (the block-wise packing of whole groups)
+    ("f16", 64, 200, (3, 3, 3)), ("f32", 32, 70, (3, 3)), ("bf16", 16, 130, (1, 1)),
+    ("bf16", 40, 64, (3, 3)),
 ])
 def test_pack_layout(dt, C, K, ks):
     import direct_implicit_gemm_amd as L
