@@ -45,6 +45,9 @@ CASES = [  # channel counts give 10 chunks of a stage, so every split count 2..4
      277, True),
     ("f16_k333_packed_8w", "f16", 1, 152, 4, 7, 40, 136, 3, 3, (1, 1, 1), (1, 1, 1), "none", 259,
      True),
+    # 12-row eight-wave tile (64 x 96 per wave); 13 rows leave a ragged second row tile
+    ("f16_k333_packed_8w_12r", "f16", 1, 152, 4, 13, 40, 136, 3, 3, (1, 1, 1), (1, 1, 1), "relu",
+     258, True),
     # OI(D)HW weights through one register set
     ("f16_k3s1_w1", "f16", 2, 152, 1, 11, 40, 72, 1, 3, (0, 1, 1), (1, 1, 1), "none", 207, True),
     ("bf16_k333_w1", "bf16", 1, 152, 4, 7, 40, 64, 3, 3, (1, 1, 1), (1, 1, 1), "relu", 266, True),
