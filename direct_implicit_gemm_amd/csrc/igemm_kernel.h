@@ -193,6 +193,11 @@ struct Cfg {
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int FA = WTM / 32, FB = WTN / 32;
   static constexpr int BPR = TW / 32;              // 32-pixel blocks per tile row
+  // one set of B fragments (the next pair's B reads wait for this pair's
+  // MFMAs, the other wave of the SIMD covers them): eight-wave tiles of four
+  // 32-pixel blocks per wave that stage through registers, whose fragments
+  // do not fit twice beside the accumulators and the staged stages
+  static constexpr bool SB = NWV == 8 && FB >= 4 && !(XP && PK);
   // weight staging from OIHW: one unit = one output channel x one group of
   // SE input channels = TS contiguous 16-byte vectors; unit u = g * BM + channel.
   // From OIDHW (W3: 3-D tiles that read unpacked weights) a stage is one
@@ -761,30 +766,41 @@ __global__ __launch_bounds__(G::NT, (G::W1 && G::NWV == 4) ? 2 : 1) void igemm_k
   // (it issues pieces of later stages' reads).
   auto compute = [&](const unsigned char* wl, const unsigned char* xl, auto&& hook)
       __attribute__((always_inline)) {
-    u32x4_t fa[2][G::FA], fb[2][G::FB];
-    auto load_frags = [&](auto pc, int k) {
+    constexpr int NBB = G::SB ? 1 : 2;  // B fragment sets
+    u32x4_t fa[2][G::FA], fb[NBB][G::FB];
+    auto load_a = [&](auto pc, int k) {
+      constexpr int p = decltype(pc)::value;
+      const int s0 = 2 * p;
+#pragma unroll
+      for (int i = 0; i < G::FA; ++i)
+        fa[k][i] = *reinterpret_cast<const u32x4_t*>(wl + a_lane + (s0 * G::BM + i * 32) * 16);
+      if (2 * p + 1 >= G::NSLOT && hf) {
+        // odd slot count: the second half of the last pair carries nothing
+#pragma unroll
+        for (int i = 0; i < G::FA; ++i) fa[k][i] = u32x4_t{0u, 0u, 0u, 0u};
+      }
+    };
+    auto load_b = [&](auto pc, int k) {
       constexpr int p = decltype(pc)::value;
       const int s0 = 2 * p;
       const int s1 = (2 * p + 1 < G::NSLOT) ? 2 * p + 1 : 2 * p;
       const int xo = hf ? xslot(s1) : xslot(s0);
 #pragma unroll
-      for (int i = 0; i < G::FA; ++i)
-        fa[k][i] = *reinterpret_cast<const u32x4_t*>(wl + a_lane + (s0 * G::BM + i * 32) * 16);
-#pragma unroll
       for (int j = 0; j < G::FB; ++j)
         fb[k][j] = *reinterpret_cast<const u32x4_t*>(xl + b_lane + xo + xblock(j));
       if (2 * p + 1 >= G::NSLOT && hf) {
-        // odd slot count: the second half of the last pair carries nothing
-#pragma unroll
-        for (int i = 0; i < G::FA; ++i) fa[k][i] = u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int j = 0; j < G::FB; ++j) fb[k][j] = u32x4_t{0u, 0u, 0u, 0u};
       }
     };
-    load_frags(std::integral_constant<int, 0>{}, 0);
+    load_a(std::integral_constant<int, 0>{}, 0);
+    load_b(std::integral_constant<int, 0>{}, 0);
     static_for<0, G::NPAIR>([&](auto pc) {
       constexpr int p = decltype(pc)::value;
-      if constexpr (p + 1 < G::NPAIR) load_frags(std::integral_constant<int, p + 1>{}, (p + 1) & 1);
+      if constexpr (p + 1 < G::NPAIR) {
+        load_a(std::integral_constant<int, p + 1>{}, (p + 1) & 1);
+        if constexpr (!G::SB) load_b(std::integral_constant<int, p + 1>{}, (p + 1) & 1);
+      }
       hook(pc);
       // keep the next pair's LDS reads (and the hook's global reads) ahead of
       // this pair's MFMAs: left alone, the scheduler sinks them below the
@@ -796,7 +812,13 @@ __global__ __launch_bounds__(G::NT, (G::W1 && G::NWV == 4) ? 2 : 1) void igemm_k
         for (int i = 0; i < G::FA; ++i)
 #pragma unroll
           for (int j = 0; j < G::FB; ++j)
-            Mma<G::DT>::step(fa[p & 1][i], fb[p & 1][j], acc[i][j], k);
+            Mma<G::DT>::step(fa[p & 1][i], fb[G::SB ? 0 : p & 1][j], acc[i][j], k);
+      if constexpr (G::SB && p + 1 < G::NPAIR) {
+        // one B set: the next pair's B reads follow this pair's MFMAs (the
+        // other wave of the SIMD covers their latency)
+        __builtin_amdgcn_sched_barrier(0);
+        load_b(std::integral_constant<int, p + 1>{}, 0);
+      }
     });
   };
 
