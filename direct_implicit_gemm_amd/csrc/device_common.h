@@ -47,6 +47,14 @@ __device__ __forceinline__ int guard_offset(bool ok, int off) {
   return v;
 }
 
+// Cache policy of the stores that write a call's output (the aux operand of
+// the buffer store builtins): non-temporal, so that output lines stream out
+// to memory while the kernel runs instead of sitting dirty in L2 until the
+// write-back at its end, and push fewer of the lines that later workgroups
+// read out of L2.  Split-K partial sums and packed weights, which the next
+// kernel reads back at once, keep the default policy.
+constexpr int kOutPolicy = 2;
+
 // --- storage element <-> fp32 -------------------------------------------
 template <int DT> struct Elem;
 
@@ -57,6 +65,10 @@ template <> struct Elem<DT_F32> {
   }
   __device__ static __forceinline__ void store(float v, __amdgpu_buffer_rsrc_t r, int byte_off) {
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, byte_off, 0, 0);
+  }
+  __device__ static __forceinline__ void store_out(float v, __amdgpu_buffer_rsrc_t r, int byte_off) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, byte_off, 0,
+                                          kOutPolicy);
   }
   __device__ static __forceinline__ uint32_t load_bits(__amdgpu_buffer_rsrc_t r, int byte_off) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0);
@@ -91,6 +103,9 @@ template <> struct Elem<DT_F16> {
   __device__ static __forceinline__ void store(float v, __amdgpu_buffer_rsrc_t r, int byte_off) {
     __builtin_amdgcn_raw_buffer_store_b16(from_f32(v), r, byte_off, 0, 0);
   }
+  __device__ static __forceinline__ void store_out(float v, __amdgpu_buffer_rsrc_t r, int byte_off) {
+    __builtin_amdgcn_raw_buffer_store_b16(from_f32(v), r, byte_off, 0, kOutPolicy);
+  }
 };
 
 template <> struct Elem<DT_BF16> {
@@ -114,6 +129,9 @@ template <> struct Elem<DT_BF16> {
   }
   __device__ static __forceinline__ void store(float v, __amdgpu_buffer_rsrc_t r, int byte_off) {
     __builtin_amdgcn_raw_buffer_store_b16(from_f32(v), r, byte_off, 0, 0);
+  }
+  __device__ static __forceinline__ void store_out(float v, __amdgpu_buffer_rsrc_t r, int byte_off) {
+    __builtin_amdgcn_raw_buffer_store_b16(from_f32(v), r, byte_off, 0, kOutPolicy);
   }
 };
 

@@ -215,7 +215,7 @@ __global__ __launch_bounds__(kThreads) void direct_kernel(DirectArgs a) {
     for (int p = 0; p < P; ++p) {
       const int ow = ow0 + p * 64 + lane;
       if (co < k_store && ow < a.OW)
-        E::store(epilogue(acc[j][p], bias[j], a.relu), yr,
+        E::store_out(epilogue(acc[j][p], bias[j], a.relu), yr,
                  act_offset<eb>(a.cpack, n, a.K, co, a.OT, ot, a.OH, oh, a.OW, ow));
     }
   }
@@ -459,7 +459,7 @@ __global__ __launch_bounds__(kThreads) void tap_kernel(TapArgs a) {
     for (int r = 0; r < R; ++r) {
       const int oh = oh0 + wave * R + r;
       if (co < a.K && oh < a.OH && ow < a.OW)
-        E::store(epilogue(acc[r][j], bias, a.relu), yr,
+        E::store_out(epilogue(acc[r][j], bias, a.relu), yr,
                  ((((n * a.K + co) * a.T + fr) * a.OH + oh) * a.OW + ow) * G::EB);
     }
   }

@@ -220,7 +220,8 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_kernel(ReduceArgs a) {
     }
   }
 #pragma unroll
-  for (int m = 0; m < V; ++m) E::store(epilogue(v[m], bias, a.relu), yr, (int)((e0 + m) * E::bytes));
+  for (int m = 0; m < V; ++m)
+    E::store_out(epilogue(v[m], bias, a.relu), yr, (int)((e0 + m) * E::bytes));
 }
 
 // The same sum for channel-packed y: one thread per output channel group of
@@ -262,7 +263,7 @@ __global__ __launch_bounds__(kThreads) void splitk_reduce_cpack_kernel(ReduceArg
     else
       w[m] = (uint32_t)E::from_f32(v[2 * m]) | ((uint32_t)E::from_f32(v[2 * m + 1]) << 16);
   }
-  __builtin_amdgcn_raw_buffer_store_b128(w, yr, (int)(u * 16), 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(w, yr, (int)(u * 16), 0, kOutPolicy);
 }
 
 // ------------------------------------------------------------------ tiles

@@ -1206,11 +1206,11 @@ __global__ __launch_bounds__(G::NT, (G::W1 && G::NWV == 4) ? 2 : 1) void igemm_k
           if constexpr (EB == 4) {
             const u32x4_t word{__builtin_bit_cast(uint32_t, v[0]), __builtin_bit_cast(uint32_t, v[1]),
                                __builtin_bit_cast(uint32_t, v[2]), __builtin_bit_cast(uint32_t, v[3])};
-            __builtin_amdgcn_raw_buffer_store_b128(word, yr, guard_offset(ok, off), 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(word, yr, guard_offset(ok, off), 0, kOutPolicy);
           } else {
             const u32x2_t word{(uint32_t)E::from_f32(v[0]) | ((uint32_t)E::from_f32(v[1]) << 16),
                                (uint32_t)E::from_f32(v[2]) | ((uint32_t)E::from_f32(v[3]) << 16)};
-            __builtin_amdgcn_raw_buffer_store_b64(word, yr, guard_offset(ok, off), 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(word, yr, guard_offset(ok, off), 0, kOutPolicy);
           }
         }
       }
@@ -1275,12 +1275,12 @@ __global__ __launch_bounds__(G::NT, (G::W1 && G::NWV == 4) ? 2 : 1) void igemm_k
                             ((uint32_t)E::from_f32(m[v * VP + 2 * e + 1]) << 16);
               }
               __builtin_amdgcn_raw_buffer_store_b128(
-                  word, yr, guard_offset(ok && owp + v * VP < owp_n, (off + v * VP) * EB), 0, 0);
+                  word, yr, guard_offset(ok && owp + v * VP < owp_n, (off + v * VP) * EB), 0, kOutPolicy);
             }
           } else {
 #pragma unroll
             for (int q = 0; q < 8; ++q)
-              if (ok && owp + q < owp_n) E::store(m[q], yr, (off + q) * EB);
+              if (ok && owp + q < owp_n) E::store_out(m[q], yr, (off + q) * EB);
           }
         }
       }
@@ -1334,7 +1334,7 @@ __global__ __launch_bounds__(G::NT, (G::W1 && G::NWV == 4) ? 2 : 1) void igemm_k
           // a.OW is a multiple of VEC, so a segment is wholly inside or
           // wholly outside the row; outside the output the store is dropped
           __builtin_amdgcn_raw_buffer_store_b128(
-              v, yr, guard_offset(co < a.K && oh < a.OH && ow < a.OW, off), 0, 0);
+              v, yr, guard_offset(co < a.K && oh < a.OH && ow < a.OW, off), 0, kOutPolicy);
         }
         lds_fence();
       }
@@ -1363,7 +1363,7 @@ __global__ __launch_bounds__(G::NT, (G::W1 && G::NWV == 4) ? 2 : 1) void igemm_k
         const int oh = oh0 + b / G::BPR;
         const int ow = ow0 + (b % G::BPR) * 32 + il;
         if (co < a.K && oh < a.OH && ow < a.OW)
-          E::store(epilogue(acc[i][j][r], bias[i][r], a.relu), yr,
+          E::store_out(epilogue(acc[i][j][r], bias[i][r], a.relu), yr,
                    (cbase + oh * a.OW + ow) * EB);
       }
     }
