@@ -214,8 +214,15 @@ struct Cfg {
   // nothing (zeros) into a 1 KB scratch area at the end of LDS
   static constexpr int WCHUNKS = NSLOT * BM / 64;
   // input staging: one unit = one run (VX) or one halo pixel of one channel
-  // group; VX units come in blocks of 8 rows x NRUN runs
-  static constexpr int XUNITS = VX ? (NROWS + 7) / 8 * 8 * NRUN : CG * HR * HC;
+  // group.  VX units come in blocks of 8 rows x NRUN runs (8 lanes side by
+  // side on 8 rows), or, when the halo's rows are not a multiple of 8 and
+  // that saves a wave-wide read per channel, densely as NRUN runs of all the
+  // rows (lanes side by side on consecutive rows, then the next run).  Every
+  // wave-wide read costs the address unit alike, however many of its lanes
+  // fall outside the halo.
+  static constexpr int XUNITS_BLK = (NROWS + 7) / 8 * 8 * NRUN;
+  static constexpr bool XDENSE = VX && (NROWS * NRUN + 63) / 64 < (XUNITS_BLK + 63) / 64;
+  static constexpr int XUNITS = VX ? (XDENSE ? NROWS * NRUN : XUNITS_BLK) : CG * HR * HC;
   static constexpr int XPASS = XP ? 0 : (XUNITS + NT - 1) / NT;
   static constexpr int XPASS1 = XPASS > 0 ? XPASS : 1;  // array extent
   // Which waves stage what.  When a stage's input units fit in fewer than
@@ -455,7 +462,8 @@ __global__ __launch_bounds__(G::NT, (G::W1 && G::NWV == 4) ? 2 : 1) void igemm_k
   // descriptor (scalar arithmetic), while the range check keeps covering
   // every access up to the end of the tensor.
   // VX: halo unit u holds run (u / 8) % NRUN of row 8 * (u / (8 * NRUN)) +
-  // u % 8, row = g * HR + hr; one offset per unit (the channel j of its group
+  // u % 8 (dense: run u / NROWS of row u % NROWS), row = g * HR + hr; one
+  // offset per unit (the channel j of its group
   // is added as the scalar offset j * plane).  The runs start at a multiple
   // of RUN columns, `shift` columns left of the first tap column; with W a
   // multiple of RUN a run lies wholly inside or wholly outside the row.
@@ -468,8 +476,8 @@ __global__ __launch_bounds__(G::NT, (G::W1 && G::NWV == 4) ? 2 : 1) void igemm_k
   for (int i = 0; i < G::XPASS; ++i) {
     const int u = tid + i * G::NT;
     if constexpr (G::VX) {
-      const int run = (u >> 3) % G::NRUN;
-      const int row = (u >> 3) / G::NRUN * 8 + (u & 7);
+      const int run = G::XDENSE ? u / G::NROWS : (u >> 3) % G::NRUN;
+      const int row = G::XDENSE ? u % G::NROWS : (u >> 3) / G::NRUN * 8 + (u & 7);
       const int hr = row % G::HR;
       const int g = row / G::HR;
       const int ih = ih0 + hr, iw = iw0 - shift + run * G::RUN;
@@ -693,8 +701,8 @@ __global__ __launch_bounds__(G::NT, (G::W1 && G::NWV == 4) ? 2 : 1) void igemm_k
       const int u = tid + i * G::NT;
       if constexpr (G::VX) {
         // unit u covers the RUN words of its run in its row
-        const int run = (u >> 3) % G::NRUN;
-        const int row = (u >> 3) / G::NRUN * 8 + (u & 7);
+        const int run = G::XDENSE ? u / G::NROWS : (u >> 3) % G::NRUN;
+        const int row = G::XDENSE ? u % G::NROWS : (u >> 3) / G::NRUN * 8 + (u & 7);
         unsigned char* dst = xdst + (row * G::PITCH + run * G::RUN) * 16;
 #pragma unroll
         for (int q = 0; q < G::RUN; ++q) {
