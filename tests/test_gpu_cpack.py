@@ -74,6 +74,9 @@ TILE_CASES = [
     (280, "f16", 16, 72, 4, 9, 40, (3, 3, 3), (1, 1, 1), (1, 1, 1), None, True),
     (280, "bf16", 20, 64, 5, 7, 33, (3, 3, 3), (1, 1, 1), (2, 1, 1), 0, False),  # causal, odd W
     (281, "bf16", 24, 136, 3, 10, 48, (3, 3, 3), (1, 1, 1), (1, 1, 1), None, True),
+    # eight waves, 64 x 128 per wave: 19 rows leave a ragged second 16-row tile
+    (279, "f16", 24, 136, 3, 19, 40, (3, 3, 3), (1, 1, 1), (1, 1, 1), None, True),
+    (279, "bf16", 16, 64, 4, 17, 72, (3, 3, 3), (1, 1, 1), (2, 1, 1), 0, False),  # causal
     (282, "f16", 20, 70, 1, 19, 72, (1, 3, 3), (1, 1, 1), (0, 1, 1), None, True),  # K % 8 != 0
     (283, "bf16", 32, 200, 1, 11, 40, (1, 3, 3), (1, 1, 1), (0, 1, 1), None, False),
     (284, "f16", 16, 72, 1, 21, 75, (1, 3, 3), (1, 2, 2), (0, 1, 1), None, True),
@@ -238,16 +241,16 @@ def test_cpack_full_size_sampled(name):
 
 
 @pytest.mark.parametrize("tid,dt,ks", [(282, "f16", 3), (283, "bf16", 2), (290, "f32", 2),
-                                       (280, "bf16", 2)])
+                                       (280, "bf16", 2), (279, "f16", 2)])
 def test_cpack_split_k(tid, dt, ks, monkeypatch):
     """Split-K on packed activations: fp32 partial sums, then the sum kernel
     writes the packed output (with zeros past C_out)."""
     import direct_implicit_gemm_amd as L
     monkeypatch.setenv("LIBCONV_FORCE_TILE", str(tid))
     monkeypatch.setenv("LIBCONV_FORCE_KSPLIT", str(ks))
-    if tid == 280:
-        layer = W.Layer("cpk", dt, 1, 64, 3, 9, 40, 70, 3, 3, 3, (1, 1, 1), (1, 1, 1), "relu", 3,
-                        "N01", "N01", "U0.05")
+    if tid in (279, 280):
+        layer = W.Layer("cpk", dt, 1, 64, 3, 9 if tid == 280 else 19, 40, 70, 3, 3, 3, (1, 1, 1),
+                        (1, 1, 1), "relu", 3, "N01", "N01", "U0.05")
     else:
         layer = W.Layer("cpk", dt, 2, 96 if dt != "f32" else 48, 1, 11, 40, 70, 1, 3, 3,
                         (0, 1, 1), (1, 1, 1), "relu", 2, "N01", "N01", "U0.05")

@@ -45,6 +45,9 @@ CASES = [  # channel counts give 10 chunks of a stage, so every split count 2..4
      277, True),
     ("f16_k333_packed_8w", "f16", 1, 152, 4, 7, 40, 136, 3, 3, (1, 1, 1), (1, 1, 1), "none", 259,
      True),
+    # 16-row eight-wave tile (64 x 128 per wave, one B fragment set); 19 rows: ragged
+    ("f16_k333_packed_8w_16r", "bf16", 1, 152, 4, 19, 40, 136, 3, 3, (1, 1, 1), (1, 1, 1), "none",
+     257, True),
     # 12-row eight-wave tile (64 x 96 per wave); 13 rows leave a ragged second row tile
     ("f16_k333_packed_8w_12r", "f16", 1, 152, 4, 13, 40, 136, 3, 3, (1, 1, 1), (1, 1, 1), "relu",
      258, True),
