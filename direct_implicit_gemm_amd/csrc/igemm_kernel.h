@@ -225,14 +225,15 @@ struct Cfg {
   static constexpr int XUNITS = VX ? (XDENSE ? NROWS * NRUN : XUNITS_BLK) : CG * HR * HC;
   static constexpr int XPASS = XP ? 0 : (XUNITS + NT - 1) / NT;
   static constexpr int XPASS1 = XPASS > 0 ? XPASS : 1;  // array extent
-  // Which waves stage what.  When a stage's input units fit in fewer than
-  // four waves, only those (the first XW) read the input, so that no wave
-  // issues reads that would all fall outside the tensor (such reads still
-  // cost the address unit a full wave instruction).  Packed weights are
-  // copied by all four waves: a wave that copied them alone (as many
+  // Which waves stage what.  When a stage's input units fit in fewer waves
+  // than the workgroup has, only those (the first XW) read the input, so that
+  // no wave issues reads that would all fall outside the tensor (such reads
+  // still cost the address unit a full wave instruction).  Packed weights are
+  // copied by all the waves: a wave that copied them alone (as many
   // one-instruction copies as the input waves' reads, repacking and LDS
   // writes together) finished each stage last and held the others at the
-  // barrier (measured per wave on the 3x3x3 video-VAE layers).  OIHW weight
+  // barrier (measured per wave on the 3x3x3 video-VAE layers), and leaving
+  // them to the waves without input units measured no faster.  OIHW weight
   // units go to the last WW waves.  A wave may have both roles.
   static constexpr int XW = (VX && XPASS == 1) ? (XUNITS + 63) / 64 : NWV;
   static constexpr int WW = PK ? NWV : (WPASS == 1 ? (WUNITS + 63) / 64 : NWV);
